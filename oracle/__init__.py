@@ -1,0 +1,153 @@
+"""CPU oracle for MoE expert-parallel route / dispatch / combine.
+
+TEST INFRASTRUCTURE ONLY.  Imported by tests/, by __graft_entry__.smoke() and by
+bench.py's cpu_baseline leg -- never by the product package, which has no CPU
+fallback.  The arithmetic lives in ep_oracle.c (plain C, double precision);
+this module only marshals numpy arrays into it.  Page citations for each
+function are in ep_oracle.h.
+
+parity pins: every function here is pinned by the CPU tests in
+tests/test_oracle_*.py against closed forms, brute force, library routines
+and hand-derived fixtures under tests/golden/.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+def lib():
+    """Load (building first if absent) the oracle shared library."""
+    global _lib
+    if _lib is None:
+        path = os.path.join(_HERE, "libep_oracle.so")
+        if not os.path.exists(path):
+            _build.build()
+        L = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        L.ep_oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.ep_oracle_bf16_to_double.restype = ctypes.c_double
+        L.ep_oracle_double_to_bf16.argtypes = [ctypes.c_double]
+        L.ep_oracle_double_to_bf16.restype = ctypes.c_uint16
+        L.ep_oracle_route_topk.argtypes = [P, i64, i32, i32, i32, P, P]
+        L.ep_oracle_dispatch_layout.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, P]
+        L.ep_oracle_dispatch.argtypes = [P, i64, i32, i32, P, P]
+        L.ep_oracle_combine.argtypes = [P, P, P, i64, i32, i32, P]
+        L.ep_oracle_combine_tokens.argtypes = [P, P, P, i64, i32, i32, P, i64, P]
+        L.ep_oracle_fused_trailer.argtypes = [ctypes.c_uint64, P, i64, P]
+        for f in ("ep_oracle_route_topk", "ep_oracle_dispatch_layout",
+                  "ep_oracle_dispatch", "ep_oracle_combine",
+                  "ep_oracle_combine_tokens", "ep_oracle_fused_trailer"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name} rejected its arguments (rc={rc})")
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def bf16_to_double(b: int) -> float:
+    return lib().ep_oracle_bf16_to_double(int(b))
+
+
+def double_to_bf16(v: float) -> int:
+    return int(lib().ep_oracle_double_to_bf16(float(v)))
+
+
+def route_topk(logits, k: int, normalize: int = 1):
+    """logits f32 [T][E] -> (topk_idx i32 [T][k], topk_w f32 [T][k])."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    _check(lib().ep_oracle_route_topk(_p(logits), T, E, k, int(normalize), _p(idx), _p(w)),
+           "route_topk")
+    return idx, w
+
+
+def dispatch_layout(topk_idx, E: int, R: int):
+    """topk_idx i32 [T][k] -> dict of the layout arrays."""
+    topk_idx = _c(topk_idx, np.int32)
+    T, k = topk_idx.shape
+    out = dict(
+        expert_counts=np.empty(E, np.int32),
+        expert_offsets=np.empty(E + 1, np.int32),
+        rank_counts=np.empty(R, np.int32),
+        rank_offsets=np.empty(R + 1, np.int32),
+        pos=np.empty((T, k), np.int32),
+        slot_src=np.empty(T * k, np.int32),
+    )
+    _check(lib().ep_oracle_dispatch_layout(
+        _p(topk_idx), T, k, E, R, _p(out["expert_counts"]), _p(out["expert_offsets"]),
+        _p(out["rank_counts"]), _p(out["rank_offsets"]), _p(out["pos"]), _p(out["slot_src"])),
+        "dispatch_layout")
+    return out
+
+
+def dispatch(x_bits, pos, out=None):
+    """x bf16 bits u16 [T][H], pos i32 [T][k] -> send u16 [T*k][H]."""
+    x_bits = _c(x_bits, np.uint16)
+    pos = _c(pos, np.int32)
+    T, H = x_bits.shape
+    k = pos.shape[1]
+    send = out if out is not None else np.empty((T * k, H), np.uint16)
+    _check(lib().ep_oracle_dispatch(_p(x_bits), T, H, k, _p(pos), _p(send)), "dispatch")
+    return send
+
+
+def combine(y_bits, pos, topk_w):
+    """y u16 [T*k][H] (send order), pos i32 [T][k], w f32 [T][k] -> out u16 [T][H]."""
+    y_bits = _c(y_bits, np.uint16)
+    pos = _c(pos, np.int32)
+    topk_w = _c(topk_w, np.float32)
+    T, k = pos.shape
+    H = y_bits.shape[1]
+    out = np.empty((T, H), np.uint16)
+    _check(lib().ep_oracle_combine(_p(y_bits), _p(pos), _p(topk_w), T, H, k, _p(out)),
+           "combine")
+    return out
+
+
+def combine_tokens(y_bits, pos, topk_w, tokens):
+    """Combine for the listed tokens only -> u16 [len(tokens)][H]."""
+    y_bits = _c(y_bits, np.uint16)
+    pos = _c(pos, np.int32)
+    topk_w = _c(topk_w, np.float32)
+    tokens = _c(tokens, np.int64)
+    T, k = pos.shape
+    H = y_bits.shape[1]
+    out = np.empty((len(tokens), H), np.uint16)
+    _check(lib().ep_oracle_combine_tokens(_p(y_bits), _p(pos), _p(topk_w), T, H, k,
+                                          _p(tokens), len(tokens), _p(out)),
+           "combine_tokens")
+    return out
+
+
+def fused_trailers(epoch: int, slot_src):
+    """Expected 16-byte trailers of every slot -> u8 [S][16]."""
+    slot_src = _c(slot_src, np.int32)
+    S = slot_src.shape[0]
+    tr = np.empty((S, 16), np.uint8)
+    L = lib()
+    for s in range(S):
+        _check(L.ep_oracle_fused_trailer(ctypes.c_uint64(epoch), _p(slot_src), s,
+                                         ctypes.c_void_p(tr.ctypes.data + 16 * s)),
+               "fused_trailer")
+    return tr

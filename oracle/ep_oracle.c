@@ -1,0 +1,280 @@
+/*
+ * ep_oracle.c -- CPU oracle for MoE expert-parallel route / dispatch / combine.
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the tests, the smoke check and the
+ * benchmark's CPU-baseline leg, never by the product library.  Plain C,
+ * single-threaded, no blocking, no fusion; floating point in double.
+ * Built with -ffp-contract=off so every expression rounds as written.
+ * The page citations are spelled out in ep_oracle.h.
+ */
+#include "ep_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* bf16 format: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.     */
+/* ------------------------------------------------------------------------ */
+
+double ep_oracle_bf16_to_double(uint16_t b)
+{
+    int sign = (b >> 15) & 1;
+    int expo = (b >> 7) & 0xFF;
+    int frac = b & 0x7F;
+    double mag;
+    if (expo == 0xFF) {
+        mag = frac ? NAN : INFINITY;
+    } else if (expo == 0) {
+        mag = ldexp((double)frac, -126 - 7);            /* subnormal: 0.frac * 2^-126 */
+    } else {
+        mag = ldexp(128.0 + (double)frac, expo - 127 - 7); /* 1.frac * 2^(expo-127) */
+    }
+    return sign ? -mag : mag;
+}
+
+/* Round a double to the nearest bf16, ties to even, in one step (no detour
+ * through float, which could round twice).  The quantum (spacing of bf16
+ * values) next to |v| is 2^(e-8) for |v| in [2^(e-1), 2^e), never below the
+ * subnormal spacing 2^-133.  Overflow goes to infinity; NaN stays NaN (quiet,
+ * sign kept). */
+uint16_t ep_oracle_double_to_bf16(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v)) return (uint16_t)(sign | 0x7FC0u);
+    double a = fabs(v);
+    if (isinf(a)) return (uint16_t)(sign | 0x7F80u);
+    if (a == 0.0) return sign;
+
+    int e;
+    (void)frexp(a, &e);                 /* a = m * 2^e, m in [0.5, 1) */
+    int qexp = e - 8;
+    if (qexp < -133) qexp = -133;
+    double q = nearbyint(ldexp(a, -qexp)); /* RNE under the default rounding mode */
+    double r = ldexp(q, qexp);             /* exact: q has at most 9 bits */
+
+    if (r >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80u);
+
+    /* r is now a bf16 value; encode it from the format's definition. */
+    if (r < ldexp(1.0, -126)) {                       /* subnormal (or zero) */
+        int frac = (int)ldexp(r, 133);
+        return (uint16_t)(sign | (uint16_t)frac);
+    }
+    int er;
+    double mr = frexp(r, &er);                        /* r = mr * 2^er, mr in [0.5,1) */
+    int expo = er - 1 + 127;                          /* r = 1.f * 2^(er-1) */
+    int frac = (int)ldexp(mr, 8) - 128;               /* 8 significant bits */
+    return (uint16_t)(sign | (uint16_t)(expo << 7) | (uint16_t)frac);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Route: top-k selection + softmax gating.                                  */
+/* HyperParallel-MoE sec. 2.2: the router picks a small subset of experts per */
+/* token by top-k routing and their outputs are weighted by routing scores.  */
+/* ------------------------------------------------------------------------ */
+
+/* "a ranks before b": larger logit first, equal logits -> lower index. */
+static int ranks_before(float la, int a, float lb, int b)
+{
+    if (la > lb) return 1;
+    if (la < lb) return 0;
+    return a < b;
+}
+
+int ep_oracle_route_topk(const float* logits, int64_t T, int32_t E, int32_t k,
+                         int32_t normalize, int32_t* topk_idx, float* topk_w)
+{
+    if (!logits || !topk_idx || !topk_w || T < 0 || E < 1 || k < 1 || k > E)
+        return -1;
+    char* taken = (char*)malloc((size_t)E);
+    double* ex = (double*)malloc(sizeof(double) * (size_t)k);
+    if (!taken || !ex) { free(taken); free(ex); return -2; }
+
+    for (int64_t t = 0; t < T; ++t) {
+        const float* l = logits + t * (int64_t)E;
+        int32_t* idx = topk_idx + t * (int64_t)k;
+        float* w = topk_w + t * (int64_t)k;
+        for (int32_t e = 0; e < E; ++e) {
+            if (!isfinite(l[e])) { free(taken); free(ex); return -3; }
+        }
+
+        /* Selection: k passes, each picks the best expert not yet taken. */
+        memset(taken, 0, (size_t)E);
+        for (int32_t j = 0; j < k; ++j) {
+            int best = -1;
+            for (int32_t e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || ranks_before(l[e], e, l[best], best)) best = e;
+            }
+            taken[best] = 1;
+            idx[j] = best;
+        }
+
+        /* Gating weights.  The first pick holds the largest logit m; shifting
+         * every exponent by m leaves each ratio unchanged. */
+        double m = (double)l[idx[0]];
+        if (normalize) {
+            double s = 0.0;
+            for (int32_t j = 0; j < k; ++j) {
+                ex[j] = exp((double)l[idx[j]] - m);
+                s += ex[j];
+            }
+            for (int32_t j = 0; j < k; ++j) w[j] = (float)(ex[j] / s);
+        } else {
+            double z = 0.0;
+            for (int32_t e = 0; e < E; ++e) z += exp((double)l[e] - m);
+            for (int32_t j = 0; j < k; ++j)
+                w[j] = (float)(exp((double)l[idx[j]] - m) / z);
+        }
+    }
+    free(taken);
+    free(ex);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dispatch layout.                                                          */
+/* UBEP sec. 2.3 / Fig. 2: per-expert token counts, then offset calculation  */
+/* and a contiguous reordering; sec. 3.2: prefix sums give each expert's     */
+/* offset.  StrataCL appendix (Hierarchical Workload Partitioning): the      */
+/* token-placement metadata is destination expert, per-expert counts,        */
+/* prefix-sum offsets and token-local offsets.  Written here as a stable     */
+/* counting sort of the flattened slots s = t*k + j by expert.               */
+/* ------------------------------------------------------------------------ */
+
+int ep_oracle_dispatch_layout(const int32_t* topk_idx, int64_t T, int32_t k,
+                              int32_t E, int32_t R, int32_t* expert_counts,
+                              int32_t* expert_offsets, int32_t* rank_counts,
+                              int32_t* rank_offsets, int32_t* pos,
+                              int32_t* slot_src)
+{
+    if (!topk_idx || !expert_counts || !expert_offsets || !rank_counts ||
+        !rank_offsets || !pos || T < 0 || k < 1 || E < 1 || R < 1 || E % R != 0)
+        return -1;
+    const int64_t S = T * (int64_t)k;
+    if (S >= ((int64_t)1 << 30)) return -1;
+    const int32_t L = E / R;                    /* experts per virtual rank */
+
+    /* 1. per-expert counts */
+    for (int32_t e = 0; e < E; ++e) expert_counts[e] = 0;
+    for (int64_t s = 0; s < S; ++s) {
+        int32_t e = topk_idx[s];
+        if (e < 0 || e >= E) return -4;
+        expert_counts[e] += 1;
+    }
+    /* 2. exclusive prefix sum -> per-expert offsets */
+    expert_offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e)
+        expert_offsets[e + 1] = expert_offsets[e] + expert_counts[e];
+    /* 3. rank r owns experts [r*L, r*L + L): its segment of the send buffer */
+    for (int32_t r = 0; r < R; ++r) {
+        rank_offsets[r] = expert_offsets[r * L];
+        rank_counts[r] = 0;
+        for (int32_t i = 0; i < L; ++i) rank_counts[r] += expert_counts[r * L + i];
+    }
+    rank_offsets[R] = expert_offsets[E];
+    /* 4. token-local offsets: walk the slots in order, each takes the next free
+     *    place of its expert (this is what makes the order stable) */
+    int32_t* cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+    if (!cursor) return -2;
+    for (int32_t e = 0; e < E; ++e) cursor[e] = expert_offsets[e];
+    for (int64_t s = 0; s < S; ++s) {
+        int32_t e = topk_idx[s];
+        pos[s] = cursor[e]++;
+        if (slot_src) slot_src[pos[s]] = (int32_t)s;
+    }
+    free(cursor);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dispatch: UBEP sec. 2.1 / 2.3 -- each token's activation goes to every    */
+/* expert it picked; a token may be sent to several experts.                 */
+/* ------------------------------------------------------------------------ */
+
+int ep_oracle_dispatch(const uint16_t* x, int64_t T, int32_t H, int32_t k,
+                       const int32_t* pos, uint16_t* send)
+{
+    if (!x || !pos || !send || T < 0 || H < 1 || k < 1) return -1;
+    const int64_t S = T * (int64_t)k;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < k; ++j) {
+            int64_t p = pos[t * k + j];
+            if (p < 0 || p >= S) return -4;
+            memcpy(send + p * (int64_t)H, x + t * (int64_t)H, sizeof(uint16_t) * (size_t)H);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Combine: HyperParallel-MoE sec. 4.1 -- the top-k expert contributions are */
+/* accumulated according to the routing scores; RailWave "System Design" --  */
+/* combine uses the dispatch metadata to put outputs back at their original  */
+/* token positions.  Sum in double (w*y is exact there), one rounding to bf16.*/
+/* ------------------------------------------------------------------------ */
+
+static void combine_one(const uint16_t* y, const int32_t* pos, const float* topk_w,
+                        int64_t t, int32_t H, int32_t k, uint16_t* out_row)
+{
+    const int32_t* p = pos + t * (int64_t)k;
+    const float* w = topk_w + t * (int64_t)k;
+    for (int32_t h = 0; h < H; ++h) {
+        double acc = (double)w[0] * ep_oracle_bf16_to_double(y[(int64_t)p[0] * H + h]);
+        for (int32_t j = 1; j < k; ++j)
+            acc = acc + (double)w[j] * ep_oracle_bf16_to_double(y[(int64_t)p[j] * H + h]);
+        out_row[h] = ep_oracle_double_to_bf16(acc);
+    }
+}
+
+static int check_pos(const int32_t* pos, int64_t T, int32_t k)
+{
+    const int64_t S = T * (int64_t)k;
+    for (int64_t s = 0; s < S; ++s)
+        if (pos[s] < 0 || pos[s] >= S) return -4;
+    return 0;
+}
+
+int ep_oracle_combine(const uint16_t* y, const int32_t* pos, const float* topk_w,
+                      int64_t T, int32_t H, int32_t k, uint16_t* out)
+{
+    if (!y || !pos || !topk_w || !out || T < 0 || H < 1 || k < 1) return -1;
+    if (check_pos(pos, T, k)) return -4;
+    for (int64_t t = 0; t < T; ++t)
+        combine_one(y, pos, topk_w, t, H, k, out + t * (int64_t)H);
+    return 0;
+}
+
+int ep_oracle_combine_tokens(const uint16_t* y, const int32_t* pos,
+                             const float* topk_w, int64_t T, int32_t H, int32_t k,
+                             const int64_t* tokens, int64_t n_tokens,
+                             uint16_t* out_rows)
+{
+    if (!y || !pos || !topk_w || !tokens || !out_rows || T < 0 || H < 1 || k < 1 ||
+        n_tokens < 0)
+        return -1;
+    if (check_pos(pos, T, k)) return -4;
+    for (int64_t i = 0; i < n_tokens; ++i) {
+        if (tokens[i] < 0 || tokens[i] >= T) return -1;
+        combine_one(y, pos, topk_w, tokens[i], H, k, out_rows + i * (int64_t)H);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Flag-in-payload trailer.  UBEP sec. 3.4 / Fig. 6 (Token-Flag Fusion): the */
+/* readiness flag travels inside the data block, so seeing the flag proves   */
+/* the block arrived.  Read here as one 16-byte trailer after each row:      */
+/* the call's 64-bit epoch, then the slot's source index, then zero.         */
+/* ------------------------------------------------------------------------ */
+
+int ep_oracle_fused_trailer(uint64_t epoch, const int32_t* slot_src, int64_t slot,
+                            uint8_t trailer[16])
+{
+    if (!slot_src || !trailer || slot < 0) return -1;
+    uint32_t src = (uint32_t)slot_src[slot];
+    for (int i = 0; i < 8; ++i) trailer[i] = (uint8_t)(epoch >> (8 * i));
+    for (int i = 0; i < 4; ++i) trailer[8 + i] = (uint8_t)(src >> (8 * i));
+    for (int i = 0; i < 4; ++i) trailer[12 + i] = 0;
+    return 0;
+}
