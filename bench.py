@@ -1,0 +1,255 @@
+"""Benchmark of the MoE expert-parallel hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input that
+is already resident in HBM: route (top-k gating) -> dispatch layout ->
+dispatch -> combine, on the DeepSeek-V3-like workload (T=4096 tokens,
+H=7168 bf16, E=256 experts over R=32 virtual ranks, top-8) -- one EP rank's
+share of the EP=32, 4096-token, H=7168, top-8 dispatch/combine benchmark.
+The fused flag-in-payload mode is timed beside it on the same inputs.
+
+Prints ONE JSON line.  `value` = algorithmic HBM bytes of a whole step /
+step time (GB/s); tokens/s and the fraction of the 8 TB/s HBM peak ride along.
+`roofline` is measured live with HIP events around the dominant kernel on
+the stream it runs on; `cpu_baseline` times the CPU oracle on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "dispatch+combine effective HBM GB/s (% of MI355X peak) and tokens/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def src_digest(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "combine_ep_route_topk_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str, src: str):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, or None
+    when absent or when the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for ln in f:
+            if ln.startswith("json:"):
+                rec = json.loads(ln[5:])
+    if rec.get("source_sha256_16") != src_digest(src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the multi-GPU "
+                                   "exchange is not part of it; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    from combine_ep_route_topk_amd import ep
+    from combine_ep_route_topk_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS[args.workload]
+    T, H, E, R, k = w.T, w.H, w.E, w.R, w.k
+    inp = wl.make_inputs(w)
+    logits = torch.from_numpy(inp["logits"]).to(dev)
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # pre-allocated outputs: the timed region allocates nothing
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wt = torch.empty((T, k), dtype=torch.float32, device=dev)
+    lay = ep.layout_outputs(T, k, E, R, dev, slot_src=True)
+    send = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ep.ep_route_topk(logits, k, True, idx, wt, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        ep.ep_dispatch_layout(idx, E, R, out=lay, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        ep.ep_dispatch(x, lay["pos"], send, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        ep.ep_combine(send, lay["pos"], wt, out, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    # correctness gate before timing: the identity-expert round trip is exact
+    step()
+    torch.cuda.synchronize()
+    if not torch.equal(out.view(torch.int16), x.view(torch.int16)):
+        print(json.dumps({"error": "parity gate failed: combine(dispatch(x)) != x"}))
+        sys.exit(1)
+    if ep.ep_get_device_error(lay["workspace"]) != ep.EP_OK:
+        print(json.dumps({"error": "layout reported a device error"}))
+        sys.exit(1)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = ["route", "layout", "dispatch", "combine"]
+    per_op = {n: [] for n in names}
+    for e in evs:
+        for j, n in enumerate(names):
+            per_op[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)     # us
+    mean_us = {n: float(np.mean(v)) for n, v in per_op.items()}
+    p10_us = {n: float(np.percentile(v, 10)) for n, v in per_op.items()}
+    p90_us = {n: float(np.percentile(v, 90)) for n, v in per_op.items()}
+
+    ab = wl.algorithmic_bytes(w)
+    step_bytes = sum(ab.values())
+    ms_per_step = wall / K * 1e3
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dc_us = mean_us["dispatch"] + mean_us["combine"]
+    dc_gbps = (ab["dispatch"] + ab["combine"]) / (dc_us * 1e-6) / 1e9
+
+    dom = "dispatch" if mean_us["dispatch"] >= mean_us["combine"] else "combine"
+    achieved = ab[dom] / (mean_us[dom] * 1e-6) / 1e9
+    roofline = {
+        "kernel": dom,
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": traffic_for(dom, w.name, f"{dom}.hip"),
+        "algorithmic_bytes_per_launch": ab[dom],
+        "avg_launch_us": round(mean_us[dom], 2),
+    }
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.describe(), "global_batch": T, "hidden": H,
+                   "experts": E, "virtual_ranks": R, "top_k": k,
+                   "step": "route -> layout -> dispatch -> combine"},
+        "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "dispatch_combine_gbps": round(dc_gbps, 1),
+        "dispatch_combine_pct_of_peak": round(100 * dc_gbps / HBM_PEAK_GBPS, 2),
+        "per_op_us": {n: round(v, 2) for n, v in mean_us.items()},
+        "per_op_p10_p90_us": {n: [round(p10_us[n], 2), round(p90_us[n], 2)] for n in names},
+        "algorithmic_bytes": ab,
+        "roofline": roofline,
+    }
+
+    if not args.no_fused:
+        result["fused"] = bench_fused(ep, torch, w, x, idx, wt, stream, K, args.warmup)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp, lay, args.cpu_seconds, step_bytes)
+
+    print(json.dumps(result), flush=True)
+
+
+def bench_fused(ep, torch, w, x, idx, wt, stream, K, W):
+    T, H, E, R, k = w.T, w.H, w.E, w.R, w.k
+    try:
+        fz = ep.fused_outputs(T, H, k, E, R, x.device)
+        ep.ep_fused_dispatch_combine(x, idx, wt, E, R, out=fz, stream=stream)
+    except ep.EpError as e:
+        return {"status": str(e)}
+    torch.cuda.synchronize()
+    if ep.ep_get_device_error(fz["workspace"]) != ep.EP_OK or \
+            not torch.equal(fz["out"].view(torch.int16), x.view(torch.int16)):
+        return {"status": "parity gate failed"}
+    for _ in range(W):
+        ep.ep_fused_dispatch_combine(x, idx, wt, E, R, out=fz, stream=stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(K):
+        ep.ep_fused_dispatch_combine(x, idx, wt, E, R, out=fz, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / K
+    from combine_ep_route_topk_amd import workloads as wl
+    ab = wl.algorithmic_bytes(w)
+    byts = ab["layout"] + ab["dispatch"] + ab["combine"] + 16 * w.S
+    return {"us_per_call": round(us, 2), "gbps": round(byts / (us * 1e-6) / 1e9, 1),
+            "algorithmic_bytes": byts,
+            "what": "layout + dispatch + combine (identity experts) in one launch"}
+
+
+def cpu_baseline(w, inp, gpu_lay, seconds, step_bytes):
+    """The CPU oracle (single-threaded C, double precision) on this host:
+    whole steps of the same workload, repeated for about `seconds`."""
+    import oracle
+
+    reps, t_total = 0, 0.0
+    idx = wt = lay = None
+    while reps < 1 or (t_total < seconds and reps < 20):
+        t0 = time.perf_counter()
+        idx, wt = oracle.route_topk(inp["logits"], w.k, 1)
+        lay = oracle.dispatch_layout(idx, w.E, w.R)
+        send = oracle.dispatch(inp["x"], lay["pos"])
+        oracle.combine(send, lay["pos"], wt)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    sec_per_step = t_total / reps
+    agree = bool(np.array_equal(gpu_lay["pos"].cpu().numpy(), lay["pos"]))
+    return {"value": round(step_bytes / sec_per_step / 1e9, 3), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{reps} whole steps of {w.name} (route, layout, dispatch, combine), "
+                      f"{sec_per_step:.3f} s per step, single thread; host has "
+                      f"{os.cpu_count()} cores",
+            "gpu_pos_matches_oracle": agree}
+
+
+if __name__ == "__main__":
+    main()

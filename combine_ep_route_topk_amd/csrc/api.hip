@@ -1,0 +1,261 @@
+// api.hip -- the extern "C" entry points of libep_route_topk (declared and
+// documented in include/ep_route_topk.h): synchronous argument validation,
+// workspace sizing, then kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <chrono>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <random>
+
+#include "../../include/ep_route_topk.h"
+#include "ep_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+ep_status fail(ep_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+ep_status ok() {
+    g_err[0] = '\0';
+    return EP_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+ep_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess)
+        return fail(EP_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+// Sizes shared by route / layout / fused.
+ep_status check_routing_sizes(const char* fn, int32_t T, int32_t k, int32_t E) {
+    if (T < 1) return fail(EP_ERR_INVALID_ARG, "%s: T=%d must be >= 1", fn, T);
+    if (E < 1) return fail(EP_ERR_INVALID_ARG, "%s: E=%d must be >= 1", fn, E);
+    if (E > ep::kMaxE) return fail(EP_ERR_UNSUPPORTED, "%s: E=%d exceeds %d", fn, E, ep::kMaxE);
+    if (k < 1 || k > E) return fail(EP_ERR_INVALID_ARG, "%s: k=%d must be in [1, E=%d]", fn, k, E);
+    if (k > ep::kMaxK) return fail(EP_ERR_UNSUPPORTED, "%s: k=%d exceeds %d", fn, k, ep::kMaxK);
+    if (int64_t(T) * k >= (int64_t(1) << 30))
+        return fail(EP_ERR_UNSUPPORTED, "%s: T*k=%lld must be < 2^30", fn, (long long)T * k);
+    return EP_OK;
+}
+
+ep_status check_rows(const char* fn, int32_t T, int32_t H, int32_t k) {
+    if (T < 1) return fail(EP_ERR_INVALID_ARG, "%s: T=%d must be >= 1", fn, T);
+    if (k < 1) return fail(EP_ERR_INVALID_ARG, "%s: k=%d must be >= 1", fn, k);
+    if (k > ep::kMaxK) return fail(EP_ERR_UNSUPPORTED, "%s: k=%d exceeds %d", fn, k, ep::kMaxK);
+    if (H < 8 || H % 8 != 0) return fail(EP_ERR_INVALID_ARG, "%s: H=%d must be a positive multiple of 8", fn, H);
+    if (H > (1 << 20)) return fail(EP_ERR_UNSUPPORTED, "%s: H=%d exceeds 2^20", fn, H);
+    if (int64_t(T) * k >= (int64_t(1) << 30))
+        return fail(EP_ERR_UNSUPPORTED, "%s: T*k=%lld must be < 2^30", fn, (long long)T * k);
+    return EP_OK;
+}
+
+#define EP_REQUIRE_PTR(fn, p, a)                                                     \
+    do {                                                                             \
+        if (!(p)) return fail(EP_ERR_INVALID_ARG, "%s: %s is NULL", fn, #p);         \
+        if (!aligned((p), (a)))                                                      \
+            return fail(EP_ERR_INVALID_ARG, "%s: %s is not %d-byte aligned", fn, #p, \
+                        int(a));                                                     \
+    } while (0)
+
+#define EP_TRY(expr)                  \
+    do {                              \
+        ep_status st_ = (expr);       \
+        if (st_ != EP_OK) return st_; \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int ep_abi_version(void) { return EP_ABI_VERSION; }
+
+const char* ep_status_string(int status) {
+    switch (status) {
+        case EP_OK: return "EP_OK";
+        case EP_ERR_INVALID_ARG: return "EP_ERR_INVALID_ARG";
+        case EP_ERR_UNSUPPORTED: return "EP_ERR_UNSUPPORTED";
+        case EP_ERR_WORKSPACE: return "EP_ERR_WORKSPACE";
+        case EP_ERR_LAUNCH: return "EP_ERR_LAUNCH";
+        case EP_ERR_DEVICE: return "EP_ERR_DEVICE";
+        case EP_ERR_TIMEOUT: return "EP_ERR_TIMEOUT";
+        default: return "EP_ERR_UNKNOWN";
+    }
+}
+
+const char* ep_last_error(void) { return g_err; }
+
+ep_status ep_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+                        int32_t normalize, int32_t* topk_idx, float* topk_w, void* stream)
+{
+    const char* fn = "ep_route_topk";
+    EP_TRY(check_routing_sizes(fn, T, k, E));
+    EP_REQUIRE_PTR(fn, logits, 4);
+    EP_REQUIRE_PTR(fn, topk_idx, 4);
+    EP_REQUIRE_PTR(fn, topk_w, 4);
+    return launched(ep::launch_route_topk(logits, T, E, k, normalize ? 1 : 0, topk_idx,
+                                          topk_w, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+size_t ep_dispatch_layout_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t R)
+{
+    if (T < 1 || k < 1 || E < 1 || R < 1) return 0;
+    return ep::layout_plan(T, k, E).bytes;
+}
+
+ep_status ep_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                             int32_t R, int32_t* expert_counts, int32_t* expert_offsets,
+                             int32_t* rank_counts, int32_t* rank_offsets, int32_t* pos,
+                             int32_t* slot_src, void* workspace, size_t workspace_bytes,
+                             void* stream)
+{
+    const char* fn = "ep_dispatch_layout";
+    EP_TRY(check_routing_sizes(fn, T, k, E));
+    if (R < 1 || E % R != 0)
+        return fail(EP_ERR_INVALID_ARG, "%s: R=%d must be >= 1 and divide E=%d", fn, R, E);
+    EP_REQUIRE_PTR(fn, topk_idx, 4);
+    EP_REQUIRE_PTR(fn, expert_counts, 4);
+    EP_REQUIRE_PTR(fn, expert_offsets, 4);
+    EP_REQUIRE_PTR(fn, rank_counts, 4);
+    EP_REQUIRE_PTR(fn, rank_offsets, 4);
+    EP_REQUIRE_PTR(fn, pos, 4);
+    if (slot_src && !aligned(slot_src, 4))
+        return fail(EP_ERR_INVALID_ARG, "%s: slot_src is not 4-byte aligned", fn);
+    EP_REQUIRE_PTR(fn, workspace, 256);
+    const size_t need = ep::layout_plan(T, k, E).bytes;
+    if (workspace_bytes < need)
+        return fail(EP_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn,
+                    workspace_bytes, need);
+    return launched(ep::launch_dispatch_layout(topk_idx, T, k, E, R, expert_counts,
+                                               expert_offsets, rank_counts, rank_offsets,
+                                               pos, slot_src, workspace,
+                                               static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+ep_status ep_dispatch(const uint16_t* x, int32_t T, int32_t H, int32_t k,
+                      const int32_t* pos, uint16_t* send, void* stream)
+{
+    const char* fn = "ep_dispatch";
+    EP_TRY(check_rows(fn, T, H, k));
+    EP_REQUIRE_PTR(fn, x, 16);
+    EP_REQUIRE_PTR(fn, pos, 4);
+    EP_REQUIRE_PTR(fn, send, 16);
+    return launched(ep::launch_dispatch(x, T, H, k, pos, send,
+                                        static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+ep_status ep_combine(const uint16_t* y, const int32_t* pos, const float* topk_w,
+                     int32_t T, int32_t H, int32_t k, uint16_t* out, void* stream)
+{
+    const char* fn = "ep_combine";
+    EP_TRY(check_rows(fn, T, H, k));
+    EP_REQUIRE_PTR(fn, y, 16);
+    EP_REQUIRE_PTR(fn, pos, 4);
+    EP_REQUIRE_PTR(fn, topk_w, 4);
+    EP_REQUIRE_PTR(fn, out, 16);
+    return launched(ep::launch_combine(y, pos, topk_w, T, H, k, out,
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+size_t ep_fused_row_stride_bytes(int32_t H)
+{
+    if (H < 8 || H % 8 != 0) return 0;
+    return ep::fused_row_stride(H);
+}
+
+size_t ep_fused_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t R)
+{
+    if (T < 1 || k < 1 || E < 1 || R < 1) return 0;
+    return ep::fused_plan(T, k, E).bytes;
+}
+
+ep_status ep_fused_workspace_init(void* workspace, size_t workspace_bytes, void* stream)
+{
+    const char* fn = "ep_fused_workspace_init";
+    EP_REQUIRE_PTR(fn, workspace, 256);
+    if (workspace_bytes < sizeof(ep::WsHeader))
+        return fail(EP_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs at least %zu", fn,
+                    workspace_bytes, sizeof(ep::WsHeader));
+    // The first epoch is unpredictable across workspaces and processes, so a
+    // trailer left in a reused send buffer by another workspace's call can
+    // never be mistaken for one of this workspace's.
+    static std::atomic<uint64_t> counter{0};
+    std::random_device rd;
+    uint64_t e = (uint64_t(rd()) << 32) ^ uint64_t(rd()) ^
+                 uint64_t(std::chrono::steady_clock::now().time_since_epoch().count()) ^
+                 (counter.fetch_add(1) * 0x9E3779B97F4A7C15ull);
+    if (e == 0) e = 1;
+    return launched(ep::launch_fused_init(workspace, e, static_cast<hipStream_t>(stream)), fn);
+}
+
+ep_status ep_fused_dispatch_combine(const uint16_t* x, const int32_t* topk_idx,
+                                    const float* topk_w, int32_t T, int32_t H, int32_t k,
+                                    int32_t E, int32_t R, int32_t* expert_counts,
+                                    int32_t* expert_offsets, int32_t* rank_counts,
+                                    int32_t* rank_offsets, int32_t* pos, uint8_t* send_rows,
+                                    uint16_t* out, void* workspace, size_t workspace_bytes,
+                                    uint64_t* epoch_out, uint32_t spin_limit, void* stream)
+{
+    const char* fn = "ep_fused_dispatch_combine";
+    EP_TRY(check_routing_sizes(fn, T, k, E));
+    EP_TRY(check_rows(fn, T, H, k));
+    if (R < 1 || E % R != 0)
+        return fail(EP_ERR_INVALID_ARG, "%s: R=%d must be >= 1 and divide E=%d", fn, R, E);
+    EP_REQUIRE_PTR(fn, x, 16);
+    EP_REQUIRE_PTR(fn, topk_idx, 4);
+    EP_REQUIRE_PTR(fn, topk_w, 4);
+    EP_REQUIRE_PTR(fn, expert_counts, 4);
+    EP_REQUIRE_PTR(fn, expert_offsets, 4);
+    EP_REQUIRE_PTR(fn, rank_counts, 4);
+    EP_REQUIRE_PTR(fn, rank_offsets, 4);
+    EP_REQUIRE_PTR(fn, pos, 4);
+    EP_REQUIRE_PTR(fn, send_rows, 128);
+    EP_REQUIRE_PTR(fn, out, 16);
+    EP_REQUIRE_PTR(fn, workspace, 256);
+    const size_t need = ep::fused_plan(T, k, E).bytes;
+    if (workspace_bytes < need)
+        return fail(EP_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn,
+                    workspace_bytes, need);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // Host view of the epoch: read back synchronously only when asked for.
+    (void)epoch_out;
+    (void)spin_limit;
+    (void)s;
+    return fail(EP_ERR_UNSUPPORTED, "%s: not available in this build", fn);
+}
+
+ep_status ep_get_device_error(const void* workspace, void* stream)
+{
+    const char* fn = "ep_get_device_error";
+    EP_REQUIRE_PTR(fn, workspace, 256);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t head[2] = {0, 0};
+    hipError_t e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipMemcpy(head, workspace, sizeof(head), hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return fail(EP_ERR_LAUNCH, "%s: reading the workspace failed: %s", fn,
+                    hipGetErrorString(e));
+    if (head[0] != ep::kLayoutMagic && head[0] != ep::kFusedMagic)
+        return fail(EP_ERR_WORKSPACE, "%s: workspace was never written by this library", fn);
+    if (head[1] == ep::kDevOk) return ok();
+    if (head[1] == ep::kDevTimeout)
+        return fail(EP_ERR_TIMEOUT, "%s: a bounded device-side wait expired", fn);
+    return fail(EP_ERR_DEVICE, "%s: an expert id outside [0, E) was seen", fn);
+}
+
+}  // extern "C"

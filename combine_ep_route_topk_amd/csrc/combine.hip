@@ -1,0 +1,175 @@
+// combine.hip -- top-k weighted gather-reduce back to token order.
+//
+// HyperParallel-MoE sec. 4.1: the top-k expert contributions of a token are
+// accumulated according to its routing scores; RailWave "System Design"
+// (Fig. 3): combine returns outputs to their original token positions with
+// the metadata dispatch saved.  Here:
+//   out[t] = bf16( sum_j w[t][j] * y[pos[t][j]] ),
+// fp32 accumulation in the fixed order j = 0..k-1 (a product, then fused
+// multiply-adds), one round-to-nearest-even to bf16 at the end.
+//
+// HBM-bound gather (k reads, 1 write per row).  A wave owns one (token, row
+// segment) item: per pick it issues U coalesced 16-byte loads per lane from
+// row pos[t][j]; the k row indices and weights are wave-uniform scalar loads.
+// For the common k = 8 the pick loop is unrolled so all 8*U loads of a lane
+// can be in flight before the first FMA.
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+template <int U>
+__device__ __forceinline__ void accumulate(float (&acc)[U][8], const u32x4 (&r)[U],
+                                           float wj, bool first)
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float lo = bf16_lo(r[u][q]);
+            const float hi = bf16_hi(r[u][q]);
+            if (first) {
+                acc[u][2 * q] = wj * lo;
+                acc[u][2 * q + 1] = wj * hi;
+            } else {
+                acc[u][2 * q] = __builtin_fmaf(wj, lo, acc[u][2 * q]);
+                acc[u][2 * q + 1] = __builtin_fmaf(wj, hi, acc[u][2 * q + 1]);
+            }
+        }
+    }
+}
+
+template <int U>
+__device__ __forceinline__ void load_pick(u32x4 (&r)[U], const char* __restrict__ y,
+                                          int32_t p, uint32_t S, int64_t row_bytes,
+                                          uint32_t lane_off)
+{
+    if (uint32_t(p) < S) {
+        const char* src = y + int64_t(p) * row_bytes + lane_off;
+#pragma unroll
+        for (int u = 0; u < U; ++u) r[u] = load16(src + u * kWave * 16);
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) r[u] = u32x4{0, 0, 0, 0};
+    }
+}
+
+template <int U>
+__device__ __forceinline__ void store_acc(char* __restrict__ dst, const float (&acc)[U][8])
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[u][2 * q], acc[u][2 * q + 1]);
+        store16(dst + u * kWave * 16, o);
+    }
+}
+
+// A (token, segment) item whose vectors all lie inside the row.  KC > 0: the
+// pick count is the compile-time KC, so all KC*U loads of a lane are issued
+// before the first FMA; KC == 0: runtime k, one pick at a time.
+template <int U, int KC>
+__device__ __forceinline__ void combine_whole(const char* __restrict__ y,
+                                              const int32_t* __restrict__ prow,
+                                              const float* __restrict__ wrow, int k,
+                                              uint32_t S, int64_t row_bytes,
+                                              uint32_t lane_off, char* __restrict__ dst)
+{
+    float acc[U][8];
+    if constexpr (KC > 0) {
+        u32x4 r[KC][U];
+#pragma unroll
+        for (int j = 0; j < KC; ++j) load_pick<U>(r[j], y, prow[j], S, row_bytes, lane_off);
+#pragma unroll
+        for (int j = 0; j < KC; ++j) accumulate<U>(acc, r[j], wrow[j], j == 0);
+    } else {
+        {
+            u32x4 r[U];
+            load_pick<U>(r, y, prow[0], S, row_bytes, lane_off);
+            accumulate<U>(acc, r, wrow[0], true);
+        }
+        for (int j = 1; j < k; ++j) {
+            u32x4 r[U];
+            load_pick<U>(r, y, prow[j], S, row_bytes, lane_off);
+            accumulate<U>(acc, r, wrow[j], false);
+        }
+    }
+    store_acc<U>(dst + lane_off, acc);
+}
+
+// The last, partial segment of a row: one vector at a time.
+__device__ __noinline__ void combine_tail(const char* __restrict__ y,
+                                          const int32_t* __restrict__ prow,
+                                          const float* __restrict__ wrow, int k, uint32_t S,
+                                          int64_t row_bytes, int v0, int U, int nvec,
+                                          char* __restrict__ dst)
+{
+    for (int u = 0; u < U; ++u) {
+        const int vi = v0 + u * kWave;
+        if (vi >= nvec) break;
+        const uint32_t off = uint32_t(vi) * 16u;
+        float acc[1][8];
+        for (int j = 0; j < k; ++j) {
+            u32x4 r[1];
+            load_pick<1>(r, y, prow[j], S, row_bytes, off);
+            accumulate<1>(acc, r, wrow[j], j == 0);
+        }
+        store_acc<1>(dst + off, acc);
+    }
+}
+
+// grid.x: groups of 4 tokens (one per wave); grid.y: row segments of
+// kWave*U vectors.
+template <int U, int KC>
+__global__ __launch_bounds__(kBlock) void combine_kernel(
+    const uint16_t* __restrict__ y, const int32_t* __restrict__ pos,
+    const float* __restrict__ w, int T, int nvec, int k,
+    uint16_t* __restrict__ out)
+{
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int t = int(blockIdx.x) * kWavesPerBlock + wave;
+    if (t >= T) return;
+    const int seg = int(blockIdx.y);
+    const uint32_t S = uint32_t(T) * uint32_t(k);
+    const int64_t row_bytes = int64_t(nvec) * 16;
+    const int32_t* prow = pos + int64_t(t) * k;
+    const float* wrow = w + int64_t(t) * k;
+    const char* yb = reinterpret_cast<const char*>(y);
+    char* dst = reinterpret_cast<char*>(out) + int64_t(t) * row_bytes;
+    const int v0 = seg * kWave * U + lane_id();
+    if ((seg + 1) * kWave * U <= nvec)
+        combine_whole<U, KC>(yb, prow, wrow, k, S, row_bytes, uint32_t(v0) * 16u, dst);
+    else
+        combine_tail(yb, prow, wrow, k, S, row_bytes, v0, U, nvec, dst);
+}
+
+template <int U>
+hipError_t launch_u(const uint16_t* y, const int32_t* pos, const float* w, int T,
+                    int nvec, int k, uint16_t* out, hipStream_t s)
+{
+    const int segs = (nvec + kWave * U - 1) / (kWave * U);
+    const dim3 grid((T + kWavesPerBlock - 1) / kWavesPerBlock, segs);
+    if (k == 8)
+        hipLaunchKernelGGL((combine_kernel<U, 8>), grid, dim3(kBlock), 0, s,
+                           y, pos, w, T, nvec, k, out);
+    else
+        hipLaunchKernelGGL((combine_kernel<U, 0>), grid, dim3(kBlock), 0, s,
+                           y, pos, w, T, nvec, k, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w,
+                          int T, int H, int k, uint16_t* out, hipStream_t s)
+{
+    const int nvec = H / 8;
+    if (nvec >= kWave * 2) return launch_u<2>(y, pos, w, T, nvec, k, out, s);
+    return launch_u<1>(y, pos, w, T, nvec, k, out, s);
+}
+
+}  // namespace ep

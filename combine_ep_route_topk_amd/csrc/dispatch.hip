@@ -1,0 +1,104 @@
+// dispatch.hip -- permute token rows into the expert-contiguous send buffer.
+//
+// UBEP sec. 2.1 / sec. 2.3: each token's activation goes to every expert it
+// picked, written straight into its final place in the receive region that
+// is partitioned by (rank, expert) -- no staging copy.  Here:
+// send[pos[t][j]] = x[t] for every pick (t, j).
+//
+// HBM-bound copy (1 read, k writes per row).  A wave owns one (token, row
+// segment) item: each lane loads U 16-byte vectors of the row (coalesced,
+// 1 KiB per wave instruction), then writes them to the k destination rows
+// with streaming (nontemporal) 16-byte stores, so each row is read from HBM
+// once.  The k row indices are wave-uniform scalar loads.
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// One (token, segment) item whose vectors all lie inside the row: U loads
+// per lane, then U stores per pick, no per-vector checks.
+template <int U>
+__device__ __forceinline__ void copy_whole(const char* __restrict__ src,
+                                           char* __restrict__ send, int64_t row_bytes,
+                                           const int32_t* __restrict__ prow, int k,
+                                           uint32_t S, int v0)
+{
+    const uint32_t lane_off = uint32_t(v0) * 16u;
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = load16(src + lane_off + u * kWave * 16);
+    for (int j = 0; j < k; ++j) {
+        const int32_t p = prow[j];
+        if (uint32_t(p) >= S) continue;
+        char* dst = send + int64_t(p) * row_bytes + lane_off;
+#pragma unroll
+        for (int u = 0; u < U; ++u) store16_nt(dst + u * kWave * 16, v[u]);
+    }
+}
+
+// The last, partial segment of a row: one vector at a time.
+__device__ __noinline__ void copy_tail(const char* __restrict__ src, char* __restrict__ send,
+                                       int64_t row_bytes, const int32_t* __restrict__ prow,
+                                       int k, uint32_t S, int v0, int U, int nvec)
+{
+    for (int u = 0; u < U; ++u) {
+        const int vi = v0 + u * kWave;
+        if (vi >= nvec) break;
+        const u32x4 v = load16(src + int64_t(vi) * 16);
+        for (int j = 0; j < k; ++j) {
+            const int32_t p = prow[j];
+            if (uint32_t(p) < S) store16_nt(send + int64_t(p) * row_bytes + int64_t(vi) * 16, v);
+        }
+    }
+}
+
+// grid.x: groups of 4 tokens (one per wave); grid.y: row segments of
+// kWave*U vectors.
+template <int U>
+__global__ __launch_bounds__(kBlock) void dispatch_kernel(
+    const uint16_t* __restrict__ x, int T, int nvec, int k,
+    const int32_t* __restrict__ pos, uint16_t* __restrict__ send)
+{
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int t = int(blockIdx.x) * kWavesPerBlock + wave;
+    if (t >= T) return;
+    const int seg = int(blockIdx.y);
+    const uint32_t S = uint32_t(T) * uint32_t(k);
+    const int64_t row_bytes = int64_t(nvec) * 16;
+    const char* src = reinterpret_cast<const char*>(x) + int64_t(t) * row_bytes;
+    char* dst = reinterpret_cast<char*>(send);
+    const int32_t* prow = pos + int64_t(t) * k;
+    const int v0 = seg * kWave * U + lane_id();
+    if ((seg + 1) * kWave * U <= nvec)
+        copy_whole<U>(src, dst, row_bytes, prow, k, S, v0);
+    else
+        copy_tail(src, dst, row_bytes, prow, k, S, v0, U, nvec);
+}
+
+template <int U>
+hipError_t launch_u(const uint16_t* x, int T, int nvec, int k, const int32_t* pos,
+                    uint16_t* send, hipStream_t s)
+{
+    const int segs = (nvec + kWave * U - 1) / (kWave * U);
+    const dim3 grid((T + kWavesPerBlock - 1) / kWavesPerBlock, segs);
+    hipLaunchKernelGGL((dispatch_kernel<U>), grid, dim3(kBlock), 0, s, x, T, nvec, k, pos,
+                       send);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const uint16_t* x, int T, int H, int k, const int32_t* pos,
+                           uint16_t* send, hipStream_t s)
+{
+    const int nvec = H / 8;                   // 16-byte vectors per row
+    if (nvec % (kWave * 7) == 0) return launch_u<7>(x, T, nvec, k, pos, send, s);
+    if (nvec >= kWave * 8) return launch_u<8>(x, T, nvec, k, pos, send, s);
+    if (nvec >= kWave * 4) return launch_u<4>(x, T, nvec, k, pos, send, s);
+    return launch_u<1>(x, T, nvec, k, pos, send, s);
+}
+
+}  // namespace ep

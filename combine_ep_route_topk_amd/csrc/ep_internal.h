@@ -1,0 +1,118 @@
+// ep_internal.h -- workspace layouts, tuning constants and kernel launchers
+// shared by the host API (api.hip) and the kernel files of libep_route_topk.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ep {
+
+// ----------------------------------------------------------------- tuning
+constexpr int kBlock = 256;          // threads per workgroup (4 waves of 64)
+constexpr int kTileSlots = 4096;     // slots per layout tile (histogram unit)
+constexpr int kScanItems = 1024;     // (expert, tile) counters per scan block
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 64;
+
+// Error codes stored in a workspace's error word (host maps them to ep_status).
+enum : uint32_t { kDevOk = 0, kDevBadExpert = 1, kDevTimeout = 2 };
+
+// Magic words marking initialised workspaces.
+constexpr uint32_t kLayoutMagic = 0x45504C57u;   // "EPLW"
+constexpr uint32_t kFusedMagic = 0x45504657u;    // "EPFW"
+
+// Common 256-byte header at the start of every workspace.
+struct WsHeader {
+    uint32_t magic;
+    uint32_t error;         // result of the last call (kDev*)
+    uint32_t scan_ticket;   // decoupled-lookback block ticket
+    uint32_t timeout;       // set by any expired bounded wait
+    // fused mode only
+    uint32_t work_ticket;   // next work item to claim
+    uint32_t hist_done;     // histogram tiles finished
+    uint32_t exit_count;    // workgroups that left the persistent loop
+    uint32_t pad0;
+    uint64_t epoch;         // epoch of the NEXT fused call
+    uint64_t last_epoch;    // epoch of the last fused call
+    uint32_t reserved[52];
+};
+static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
+
+__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Layout of the dispatch-layout workspace (also the first part of the fused
+// workspace).  All offsets are from the workspace base, 256-byte aligned.
+struct LayoutPlan {
+    int64_t S;          // slots = T*k
+    int nTiles;         // histogram tiles
+    int nCnt;           // E * nTiles (expert-major counters)
+    int nScan;          // scan blocks
+    size_t off_status;  // u32 [nScan]      lookback status words
+    size_t off_cnt;     // i32 [nCnt]       per-(expert, tile) counts
+    size_t off_base;    // i32 [nCnt]       per-(expert, tile) first row
+    size_t off_rank;    // i32 [S]          rank of a slot inside its (tile, expert)
+    size_t bytes;
+};
+
+inline LayoutPlan layout_plan(int T, int k, int E) {
+    LayoutPlan p{};
+    p.S = int64_t(T) * k;
+    p.nTiles = int((p.S + kTileSlots - 1) / kTileSlots);
+    p.nCnt = E * p.nTiles;
+    p.nScan = (p.nCnt + kScanItems - 1) / kScanItems;
+    size_t off = sizeof(WsHeader);
+    p.off_status = off; off += align256(sizeof(uint32_t) * p.nScan);
+    p.off_cnt = off;    off += align256(sizeof(int32_t) * p.nCnt);
+    p.off_base = off;   off += align256(sizeof(int32_t) * p.nCnt);
+    p.off_rank = off;   off += align256(sizeof(int32_t) * p.S);
+    p.bytes = off;
+    return p;
+}
+
+// Fused workspace: the layout part, then Data-as-Flag base words.
+struct FusedPlan {
+    LayoutPlan lay;
+    size_t off_fbase;   // u64 [nCnt]  (epoch32 << 32 | base) published bases
+    size_t bytes;
+};
+
+inline FusedPlan fused_plan(int T, int k, int E) {
+    FusedPlan f{};
+    f.lay = layout_plan(T, k, E);
+    size_t off = f.lay.bytes;
+    f.off_fbase = off; off += align256(sizeof(uint64_t) * f.lay.nCnt);
+    f.bytes = off;
+    return f;
+}
+
+inline size_t fused_row_stride(int H) {
+    return (size_t(2) * H + 16 + 127) / 128 * 128;
+}
+
+// ----------------------------------------------------------------- launchers
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int normalize,
+                             int32_t* topk_idx, float* topk_w, hipStream_t s);
+
+hipError_t launch_dispatch_layout(const int32_t* topk_idx, int T, int k, int E, int R,
+                                  int32_t* expert_counts, int32_t* expert_offsets,
+                                  int32_t* rank_counts, int32_t* rank_offsets,
+                                  int32_t* pos, int32_t* slot_src, void* ws,
+                                  hipStream_t s);
+
+hipError_t launch_dispatch(const uint16_t* x, int T, int H, int k, const int32_t* pos,
+                           uint16_t* send, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w,
+                          int T, int H, int k, uint16_t* out, hipStream_t s);
+
+hipError_t launch_fused_init(void* ws, uint64_t first_epoch, hipStream_t s);
+
+hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float* topk_w,
+                        int T, int H, int k, int E, int R, int32_t* expert_counts,
+                        int32_t* expert_offsets, int32_t* rank_counts,
+                        int32_t* rank_offsets, int32_t* pos, uint8_t* send_rows,
+                        uint16_t* out, void* ws, uint32_t spin_limit, int grid,
+                        hipStream_t s);
+
+}  // namespace ep

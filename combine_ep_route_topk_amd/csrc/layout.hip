@@ -1,0 +1,270 @@
+// layout.hip -- dispatch layout on gfx950: per-expert counts, prefix-sum
+// offsets and a stable position for every (token, pick) slot.
+//
+// UBEP sec. 2.3 / Fig. 2: per-expert token counts, then offset calculation,
+// then a contiguous per-expert reordering; UBEP sec. 3.2: prefix sums of the
+// counts give each expert's offset; StrataCL appendix "Hierarchical Workload
+// Partitioning for MoE Dispatch/Combine": the placement metadata is the
+// destination expert, per-expert counts, prefix-sum offsets and token-local
+// offsets.  The slots s = t*k + j are ordered expert-major and, inside one
+// expert, by ascending s, i.e. a stable counting sort.
+//
+// Three launches on one stream (the kernel boundaries are the barriers):
+//   1. hist  -- one workgroup per tile of kTileSlots slots.  Each wave walks
+//      its 64-slot chunks in order; lanes with the same expert find each other
+//      with ceil(log2 E) ballots (wave multisplit), the group's lowest lane
+//      adds the group size to the wave's private LDS counter with an LDS
+//      atomic and broadcasts the old value: that is the slots' rank.  Ranks
+//      are therefore deterministic and stable; no atomic order is observed.
+//      Per-wave counts are then turned into per-wave offsets, giving
+//      cnt[e][tile] (expert-major) and each slot's rank inside (tile, e).
+//   2. scan  -- exclusive prefix sum of cnt flattened expert-major, single
+//      pass with decoupled look-back: blocks take ids from an atomic ticket,
+//      publish their aggregate, then look back over predecessors 64 at a time.
+//      Each 32-bit status word packs a 2-bit flag with a 30-bit value, so one
+//      relaxed atomic load sees both and no fence is needed: the status word
+//      IS the data.  The result base[e][tile] is the first send row of
+//      expert e's slots from that tile; base[e][0] is expert e's offset.
+//   3. pos   -- pos[s] = base[e][tile(s)] + rank(s); slot_src[pos[s]] = s;
+//      block 0 derives the per-expert / per-rank counts and offsets.
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+constexpr int kWavesPerBlock = kBlock / kWave;                         // 4
+constexpr int kChunksPerWave = kTileSlots / (kWavesPerBlock * kWave);  // 16
+static_assert(kChunksPerWave * kWavesPerBlock * kWave == kTileSlots, "tile split");
+
+constexpr uint32_t kFlagAggregate = 1u << 30;
+constexpr uint32_t kFlagInclusive = 2u << 30;
+constexpr uint32_t kValueMask = (1u << 30) - 1;
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+__global__ __launch_bounds__(kBlock) void layout_hist_kernel(
+    const int32_t* __restrict__ topk_idx, int64_t S, int E, int nTiles, int nScan,
+    int32_t* __restrict__ cnt, int32_t* __restrict__ local_rank,
+    uint32_t* __restrict__ status, WsHeader* __restrict__ hdr)
+{
+    __shared__ int32_t hist[kWavesPerBlock][kMaxE];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = lane_id();
+    const int tile = blockIdx.x;
+
+    // Reset the scan state for this call; the scan kernel runs after this
+    // kernel completes (stream order).
+    if (tile == 0) {
+        for (int i = tid; i < nScan; i += kBlock) status[i] = 0;
+        if (tid == 0) {
+            hdr->scan_ticket = 0;
+            hdr->timeout = 0;
+        }
+    }
+    for (int i = tid; i < kWavesPerBlock * E; i += kBlock) hist[i / E][i % E] = 0;
+    __syncthreads();
+
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    int key[kChunksPerWave];
+    int rank[kChunksPerWave];
+    const int64_t wave_first = int64_t(tile) * kTileSlots + int64_t(wave) * kChunksPerWave * kWave;
+#pragma unroll
+    for (int c = 0; c < kChunksPerWave; ++c) {
+        const int64_t s = wave_first + c * kWave + lane;
+        const int e = s < S ? topk_idx[s] : -1;
+        const bool valid = unsigned(e) < unsigned(E);
+        uint64_t peers = ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t bal = ballot(bit);
+            peers &= bit ? bal : ~bal;
+        }
+        const uint64_t below = peers & lanes_below();
+        int old = 0;
+        if (valid && below == 0) old = atomicAdd(&hist[wave][e], popc64(peers));
+        const int leader = valid ? __ffsll((unsigned long long)peers) - 1 : lane;
+        const int base = __shfl(old, leader, kWave);
+        key[c] = valid ? e : -1;
+        rank[c] = base + popc64(below);
+    }
+    __syncthreads();
+
+    // per-wave counts -> per-wave exclusive offsets; tile total per expert
+    for (int e = tid; e < E; e += kBlock) {
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w) {
+            const int c = hist[w][e];
+            hist[w][e] = run;
+            run += c;
+        }
+        cnt[int64_t(e) * nTiles + tile] = run;
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int c = 0; c < kChunksPerWave; ++c) {
+        const int64_t s = wave_first + c * kWave + lane;
+        if (key[c] >= 0) local_rank[s] = hist[wave][key[c]] + rank[c];
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void layout_scan_kernel(
+    const int32_t* __restrict__ cnt, int nCnt, int nTiles, int E,
+    int32_t* __restrict__ base, int32_t* __restrict__ expert_offsets,
+    uint32_t* __restrict__ status, WsHeader* __restrict__ hdr, uint32_t spin_limit)
+{
+    __shared__ int sh_block;
+    __shared__ int sh_wave_total[kWavesPerBlock];
+    __shared__ int sh_exclusive;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = lane_id();
+
+    // Ticket order = launch order of the blocks that are already running, so
+    // every predecessor a block waits for has started (forward progress).
+    if (tid == 0) sh_block = int(fetch_add(&hdr->scan_ticket, 1u));
+    __syncthreads();
+    const int blk = sh_block;
+
+    constexpr int kPer = kScanItems / kBlock;     // 4 counters per thread
+    const int i0 = blk * kScanItems + tid * kPer;
+    int v[kPer];
+    int tsum = 0;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        v[q] = i0 + q < nCnt ? cnt[i0 + q] : 0;
+        tsum += v[q];
+    }
+    const int incl = wave_inclusive_sum(tsum);
+    if (lane == kWave - 1) sh_wave_total[wave] = incl;
+    __syncthreads();
+    int wave_off = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+        if (w < wave) wave_off += sh_wave_total[w];
+        total += sh_wave_total[w];
+    }
+
+    if (wave == 0) {
+        int exclusive = 0;
+        if (blk == 0) {
+            if (lane == 0) st_relaxed(&status[0], kFlagInclusive | uint32_t(total));
+        } else {
+            if (lane == 0) st_relaxed(&status[blk], kFlagAggregate | uint32_t(total));
+            int look = blk - 1;
+            uint32_t spins = 0;
+            while (true) {
+                const int j = look - lane;
+                const uint32_t st = j >= 0 ? ld_relaxed(&status[j]) : kFlagInclusive;
+                if (ballot((st >> 30) == 0) != 0) {       // a predecessor not published yet
+                    if (++spins > spin_limit) {
+                        if (lane == 0) st_relaxed(&hdr->timeout, 1u);
+                        break;
+                    }
+                    backoff();
+                    continue;
+                }
+                const uint64_t inc = ballot((st >> 30) == 2);
+                int val = int(st & kValueMask);
+                if (inc != 0) {
+                    const int first = __ffsll((unsigned long long)inc) - 1;
+                    exclusive += wave_sum(lane <= first ? val : 0);
+                    break;
+                }
+                exclusive += wave_sum(val);
+                look -= kWave;
+            }
+            if (lane == 0) st_relaxed(&status[blk], kFlagInclusive | uint32_t(exclusive + total));
+        }
+        if (lane == 0) sh_exclusive = exclusive;
+    }
+    __syncthreads();
+
+    int run = sh_exclusive + wave_off + incl - tsum;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int i = i0 + q;
+        if (i < nCnt) {
+            base[i] = run;
+            if (i % nTiles == 0) expert_offsets[i / nTiles] = run;
+            run += v[q];
+            if (i == nCnt - 1) expert_offsets[E] = run;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void layout_pos_kernel(
+    const int32_t* __restrict__ topk_idx, int64_t S, int E, int R, int nTiles,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ local_rank,
+    int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
+    int32_t* __restrict__ pos, int32_t* __restrict__ slot_src, WsHeader* __restrict__ hdr)
+{
+    const int64_t s = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+    if (s < S) {
+        const int e = topk_idx[s];
+        if (unsigned(e) < unsigned(E)) {
+            const int p = base[int64_t(e) * nTiles + s / kTileSlots] + local_rank[s];
+            pos[s] = p;
+            if (slot_src) slot_src[p] = int(s);
+        } else {
+            pos[s] = -1;
+        }
+    }
+    if (blockIdx.x == 0) {
+        const int L = E / R;
+        for (int e = threadIdx.x; e < E; e += kBlock)
+            expert_counts[e] = expert_offsets[e + 1] - expert_offsets[e];
+        for (int r = threadIdx.x; r <= R; r += kBlock) {
+            rank_offsets[r] = expert_offsets[r * L];
+            if (r < R) rank_counts[r] = expert_offsets[(r + 1) * L] - expert_offsets[r * L];
+        }
+        if (threadIdx.x == 0) {
+            uint32_t err = kDevOk;
+            if (hdr->timeout) err = kDevTimeout;
+            else if (expert_offsets[E] != S) err = kDevBadExpert;
+            hdr->error = err;
+            hdr->magic = kLayoutMagic;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_layout(const int32_t* topk_idx, int T, int k, int E, int R,
+                                  int32_t* expert_counts, int32_t* expert_offsets,
+                                  int32_t* rank_counts, int32_t* rank_offsets,
+                                  int32_t* pos, int32_t* slot_src, void* ws, hipStream_t s)
+{
+    const LayoutPlan p = layout_plan(T, k, E);
+    char* w = static_cast<char*>(ws);
+    WsHeader* hdr = reinterpret_cast<WsHeader*>(w);
+    uint32_t* status = reinterpret_cast<uint32_t*>(w + p.off_status);
+    int32_t* cnt = reinterpret_cast<int32_t*>(w + p.off_cnt);
+    int32_t* base = reinterpret_cast<int32_t*>(w + p.off_base);
+    int32_t* rank = reinterpret_cast<int32_t*>(w + p.off_rank);
+
+    hipLaunchKernelGGL(layout_hist_kernel, dim3(p.nTiles), dim3(kBlock), 0, s,
+                       topk_idx, p.S, E, p.nTiles, p.nScan, cnt, rank, status, hdr);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(layout_scan_kernel, dim3(p.nScan), dim3(kBlock), 0, s,
+                       cnt, p.nCnt, p.nTiles, E, base, expert_offsets, status, hdr,
+                       uint32_t(1) << 22);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int grid = int((p.S + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL(layout_pos_kernel, dim3(grid), dim3(kBlock), 0, s,
+                       topk_idx, p.S, E, R, p.nTiles, base, rank, expert_counts,
+                       expert_offsets, rank_counts, rank_offsets, pos, slot_src, hdr);
+    return hipGetLastError();
+}
+
+}  // namespace ep

@@ -1,0 +1,269 @@
+"""Python binding of libep_route_topk (include/ep_route_topk.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Tensors live on the GPU (torch is used for device memory and
+streams); bf16 tensors are passed as their raw 16-bit patterns.  Functions
+mirror the C entry points of the same name; outputs may be passed in
+pre-allocated (the benchmark does) or are allocated here with torch.empty.
+
+Importing this module loads the built library and fails loudly if it is
+missing: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libep_route_topk.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; "
+        "g.build()' or python combine_ep_route_topk_amd/_build.py). "
+        "combine_ep_route_topk_amd has no CPU fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_u32 = ctypes.c_uint32
+_sz = ctypes.c_size_t
+
+_SIGS = {
+    "ep_abi_version": ([], ctypes.c_int),
+    "ep_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "ep_last_error": ([], ctypes.c_char_p),
+    "ep_route_topk": ([_P, _i32, _i32, _i32, _i32, _P, _P, _P], ctypes.c_int),
+    "ep_dispatch_layout_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
+    "ep_dispatch_layout": ([_P, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P, _P, _P, _sz, _P],
+                           ctypes.c_int),
+    "ep_dispatch": ([_P, _i32, _i32, _i32, _P, _P, _P], ctypes.c_int),
+    "ep_combine": ([_P, _P, _P, _i32, _i32, _i32, _P, _P], ctypes.c_int),
+    "ep_fused_row_stride_bytes": ([_i32], _sz),
+    "ep_fused_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
+    "ep_fused_workspace_init": ([_P, _sz, _P], ctypes.c_int),
+    "ep_fused_dispatch_combine": ([_P, _P, _P, _i32, _i32, _i32, _i32, _i32, _P, _P, _P, _P,
+                                   _P, _P, _P, _P, _sz, ctypes.POINTER(ctypes.c_uint64), _u32,
+                                   _P], ctypes.c_int),
+    "ep_get_device_error": ([_P, _P], ctypes.c_int),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_WORKSPACE = 0, 1, 2, 3
+EP_ERR_LAUNCH, EP_ERR_DEVICE, EP_ERR_TIMEOUT = 4, 5, 6
+
+
+class EpError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{_lib.ep_status_string(status).decode()}: {detail}")
+
+
+def _check(rc: int) -> None:
+    if rc != EP_OK:
+        raise EpError(rc, _lib.ep_last_error().decode())
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def ep_abi_version() -> int:
+    return _lib.ep_abi_version()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape: tuple | None = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _bits_ok(t: torch.Tensor, name: str, shape: tuple | None = None):
+    """bf16 payloads: torch.bfloat16 (or int16/uint16 holding the bits)."""
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold bf16 bit patterns, got {t.dtype}")
+    _need(t, name, t.dtype, shape)
+
+
+# ------------------------------------------------------------------- route
+def ep_route_topk(logits: torch.Tensor, k: int, normalize: bool = True,
+                  topk_idx: torch.Tensor | None = None, topk_w: torch.Tensor | None = None,
+                  stream=None):
+    """logits f32 [T][E] -> (topk_idx i32 [T][k], topk_w f32 [T][k])."""
+    _need(logits, "logits", torch.float32)
+    T, E = logits.shape
+    dev = logits.device
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _need(topk_idx, "topk_idx", torch.int32, (T, k))
+    _need(topk_w, "topk_w", torch.float32, (T, k))
+    _check(_lib.ep_route_topk(_ptr(logits), T, E, k, int(bool(normalize)), _ptr(topk_idx),
+                              _ptr(topk_w), _P(_stream(stream, dev))))
+    return topk_idx, topk_w
+
+
+# ------------------------------------------------------------------- layout
+def ep_dispatch_layout_workspace_bytes(T: int, k: int, E: int, R: int) -> int:
+    return int(_lib.ep_dispatch_layout_workspace_bytes(T, k, E, R))
+
+
+def layout_outputs(T: int, k: int, E: int, R: int, device, slot_src: bool = True) -> dict:
+    """Allocate the output tensors of ep_dispatch_layout."""
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(
+        expert_counts=torch.empty(E, **i32), expert_offsets=torch.empty(E + 1, **i32),
+        rank_counts=torch.empty(R, **i32), rank_offsets=torch.empty(R + 1, **i32),
+        pos=torch.empty((T, k), **i32),
+        slot_src=torch.empty(T * k, **i32) if slot_src else None,
+        workspace=torch.empty(ep_dispatch_layout_workspace_bytes(T, k, E, R),
+                              dtype=torch.uint8, device=device))
+
+
+def ep_dispatch_layout(topk_idx: torch.Tensor, E: int, R: int, out: dict | None = None,
+                       stream=None) -> dict:
+    """topk_idx i32 [T][k] -> dict(expert_counts, expert_offsets, rank_counts,
+    rank_offsets, pos, slot_src, workspace)."""
+    _need(topk_idx, "topk_idx", torch.int32)
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    if out is None:
+        out = layout_outputs(T, k, E, R, dev)
+    ws = out["workspace"]
+    _need(ws, "workspace", torch.uint8)
+    for name, shape in (("expert_counts", (E,)), ("expert_offsets", (E + 1,)),
+                        ("rank_counts", (R,)), ("rank_offsets", (R + 1,)), ("pos", (T, k))):
+        _need(out[name], name, torch.int32, shape)
+    if out.get("slot_src") is not None:
+        _need(out["slot_src"], "slot_src", torch.int32, (T * k,))
+    _check(_lib.ep_dispatch_layout(
+        _ptr(topk_idx), T, k, E, R, _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
+        _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]), _ptr(out["pos"]),
+        _ptr(out.get("slot_src")), _ptr(ws), ws.numel(), _P(_stream(stream, dev))))
+    return out
+
+
+# ------------------------------------------------------------------- dispatch
+def ep_dispatch(x: torch.Tensor, pos: torch.Tensor, send: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """x bf16 [T][H], pos i32 [T][k] -> send bf16 [T*k][H]."""
+    _bits_ok(x, "x")
+    T, H = x.shape
+    _need(pos, "pos", torch.int32)
+    k = pos.shape[1]
+    if pos.shape[0] != T:
+        raise ValueError("pos must be [T][k]")
+    if send is None:
+        send = torch.empty((T * k, H), dtype=x.dtype, device=x.device)
+    _bits_ok(send, "send", (T * k, H))
+    _check(_lib.ep_dispatch(_ptr(x), T, H, k, _ptr(pos), _ptr(send),
+                            _P(_stream(stream, x.device))))
+    return send
+
+
+# ------------------------------------------------------------------- combine
+def ep_combine(y: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor,
+               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y bf16 [T*k][H] (send order), pos i32 [T][k], topk_w f32 [T][k] -> out bf16 [T][H]."""
+    _need(pos, "pos", torch.int32)
+    T, k = pos.shape
+    _bits_ok(y, "y")
+    H = y.shape[1]
+    if y.shape[0] != T * k:
+        raise ValueError("y must have T*k rows")
+    _need(topk_w, "topk_w", torch.float32, (T, k))
+    if out is None:
+        out = torch.empty((T, H), dtype=y.dtype, device=y.device)
+    _bits_ok(out, "out", (T, H))
+    _check(_lib.ep_combine(_ptr(y), _ptr(pos), _ptr(topk_w), T, H, k, _ptr(out),
+                           _P(_stream(stream, y.device))))
+    return out
+
+
+# ------------------------------------------------------------------- fused
+def ep_fused_row_stride_bytes(H: int) -> int:
+    return int(_lib.ep_fused_row_stride_bytes(H))
+
+
+def ep_fused_workspace_bytes(T: int, k: int, E: int, R: int) -> int:
+    return int(_lib.ep_fused_workspace_bytes(T, k, E, R))
+
+
+def ep_fused_workspace_init(workspace: torch.Tensor, stream=None) -> torch.Tensor:
+    _need(workspace, "workspace", torch.uint8)
+    _check(_lib.ep_fused_workspace_init(_ptr(workspace), workspace.numel(),
+                                        _P(_stream(stream, workspace.device))))
+    return workspace
+
+
+def fused_outputs(T: int, H: int, k: int, E: int, R: int, device) -> dict:
+    """Allocate (and initialise the workspace of) ep_fused_dispatch_combine."""
+    i32 = dict(dtype=torch.int32, device=device)
+    ws = torch.empty(ep_fused_workspace_bytes(T, k, E, R), dtype=torch.uint8, device=device)
+    ep_fused_workspace_init(ws)
+    return dict(
+        expert_counts=torch.empty(E, **i32), expert_offsets=torch.empty(E + 1, **i32),
+        rank_counts=torch.empty(R, **i32), rank_offsets=torch.empty(R + 1, **i32),
+        pos=torch.empty((T, k), **i32),
+        send_rows=torch.empty((T * k, ep_fused_row_stride_bytes(H)), dtype=torch.uint8,
+                              device=device),
+        out=torch.empty((T, H), dtype=torch.bfloat16, device=device),
+        workspace=ws)
+
+
+def ep_fused_dispatch_combine(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                              E: int, R: int, out: dict | None = None, spin_limit: int = 0,
+                              want_epoch: bool = False, stream=None) -> dict:
+    """Layout + dispatch + combine (identity experts) in one persistent launch.
+    Returns the dict of outputs; with want_epoch the call also reads back the
+    epoch written into the trailers (key 'epoch')."""
+    _bits_ok(x, "x")
+    T, H = x.shape
+    _need(topk_idx, "topk_idx", torch.int32)
+    k = topk_idx.shape[1]
+    _need(topk_w, "topk_w", torch.float32, (T, k))
+    if out is None:
+        out = fused_outputs(T, H, k, E, R, x.device)
+    ep = ctypes.c_uint64(0)
+    _check(_lib.ep_fused_dispatch_combine(
+        _ptr(x), _ptr(topk_idx), _ptr(topk_w), T, H, k, E, R, _ptr(out["expert_counts"]),
+        _ptr(out["expert_offsets"]), _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]),
+        _ptr(out["pos"]), _ptr(out["send_rows"]), _ptr(out["out"]), _ptr(out["workspace"]),
+        out["workspace"].numel(), ctypes.byref(ep) if want_epoch else None, int(spin_limit),
+        _P(_stream(stream, x.device))))
+    if want_epoch:
+        out["epoch"] = int(ep.value)
+    return out
+
+
+def ep_get_device_error(workspace: torch.Tensor, stream=None) -> int:
+    """EP_OK, EP_ERR_DEVICE or EP_ERR_TIMEOUT for the last call on `workspace`."""
+    _need(workspace, "workspace", torch.uint8)
+    rc = _lib.ep_get_device_error(_ptr(workspace), _P(_stream(stream, workspace.device)))
+    if rc in (EP_OK, EP_ERR_DEVICE, EP_ERR_TIMEOUT):
+        return rc
+    _check(rc)
+    return rc

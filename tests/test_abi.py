@@ -1,0 +1,138 @@
+"""The C-ABI library: it loads, exports every symbol its header declares, sizes
+workspaces, and rejects bad arguments synchronously -- all without a GPU (no
+call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ep_route_topk.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def ep():
+    from combine_ep_route_topk_amd import ep as mod
+    return mod
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("ep_route_topk", "ep_dispatch_layout", "ep_dispatch", "ep_combine",
+                     "ep_fused_dispatch_combine", "ep_get_device_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(ep):
+    lib = ep.library()
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert ep.ep_abi_version() == 1
+
+
+def test_status_strings(ep):
+    lib = ep.library()
+    assert lib.ep_status_string(0) == b"EP_OK"
+    assert lib.ep_status_string(6) == b"EP_ERR_TIMEOUT"
+    assert lib.ep_status_string(99) == b"EP_ERR_UNKNOWN"
+
+
+def test_workspace_and_stride_queries(ep):
+    lib = ep.library()
+    # one 256 B header, then 256 B-aligned arrays; a bigger problem needs more
+    small = lib.ep_dispatch_layout_workspace_bytes(128, 2, 8, 2)
+    big = lib.ep_dispatch_layout_workspace_bytes(16384, 8, 256, 64)
+    assert small >= 256 and small % 256 == 0 and big > small
+    assert big >= 4 * 16384 * 8          # holds one rank word per slot
+    assert lib.ep_dispatch_layout_workspace_bytes(0, 2, 8, 2) == 0
+    assert lib.ep_fused_workspace_bytes(16384, 8, 256, 64) > big
+    # payload + 16-byte trailer, rounded up to 128-byte lines
+    for H in (8, 256, 4096, 7168, 7176):
+        assert lib.ep_fused_row_stride_bytes(H) == -(-(2 * H + 16) // 128) * 128
+    assert lib.ep_fused_row_stride_bytes(7) == 0
+
+
+FAKE = 0x10000          # aligned, never dereferenced: validation fails first
+
+
+def call(lib, name, *args):
+    f = getattr(lib, name)
+    rc = f(*args)
+    return rc, lib.ep_last_error().decode()
+
+
+def test_route_validation(ep):
+    lib = ep.library()
+    P = ctypes.c_void_p
+    rc, msg = call(lib, "ep_route_topk", P(FAKE), 0, 8, 2, 1, P(FAKE), P(FAKE), None)
+    assert rc == ep.EP_ERR_INVALID_ARG and "T=0" in msg
+    rc, _ = call(lib, "ep_route_topk", P(FAKE), 4, 8, 9, 1, P(FAKE), P(FAKE), None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+    rc, _ = call(lib, "ep_route_topk", P(FAKE), 4, 2048, 8, 1, P(FAKE), P(FAKE), None)
+    assert rc == ep.EP_ERR_UNSUPPORTED
+    rc, _ = call(lib, "ep_route_topk", P(FAKE), 4, 256, 65, 1, P(FAKE), P(FAKE), None)
+    assert rc == ep.EP_ERR_UNSUPPORTED
+    rc, msg = call(lib, "ep_route_topk", None, 4, 8, 2, 1, P(FAKE), P(FAKE), None)
+    assert rc == ep.EP_ERR_INVALID_ARG and "NULL" in msg
+    rc, msg = call(lib, "ep_route_topk", P(FAKE + 2), 4, 8, 2, 1, P(FAKE), P(FAKE), None)
+    assert rc == ep.EP_ERR_INVALID_ARG and "aligned" in msg
+    rc, _ = call(lib, "ep_route_topk", P(FAKE), 1 << 28, 8, 8, 1, P(FAKE), P(FAKE), None)
+    assert rc == ep.EP_ERR_UNSUPPORTED            # T*k >= 2^30
+
+
+def test_layout_validation(ep):
+    lib = ep.library()
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    need = lib.ep_dispatch_layout_workspace_bytes(64, 2, 8, 2)
+    rc, _ = call(lib, "ep_dispatch_layout", f, 64, 2, 8, 3, f, f, f, f, f, None, f, need, None)
+    assert rc == ep.EP_ERR_INVALID_ARG            # E % R != 0
+    rc, _ = call(lib, "ep_dispatch_layout", f, 64, 2, 8, 2, f, f, f, f, f, None, f, need - 1, None)
+    assert rc == ep.EP_ERR_WORKSPACE
+    rc, _ = call(lib, "ep_dispatch_layout", f, 64, 2, 8, 2, f, f, f, f, f, None,
+                 P(FAKE + 64), need, None)
+    assert rc == ep.EP_ERR_INVALID_ARG            # workspace not 256-byte aligned
+    rc, _ = call(lib, "ep_dispatch_layout", f, 64, 2, 8, 2, f, f, None, f, f, None, f, need, None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+
+
+def test_dispatch_combine_validation(ep):
+    lib = ep.library()
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    rc, msg = call(lib, "ep_dispatch", f, 16, 12, 2, f, f, None)
+    assert rc == ep.EP_ERR_INVALID_ARG and "H=12" in msg
+    rc, _ = call(lib, "ep_dispatch", P(FAKE + 8), 16, 16, 2, f, f, None)
+    assert rc == ep.EP_ERR_INVALID_ARG            # x not 16-byte aligned
+    rc, _ = call(lib, "ep_combine", f, f, f, 16, 16, 0, f, None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+    rc, _ = call(lib, "ep_combine", f, f, f, 16, 16, 2, P(FAKE + 4), None)
+    assert rc == ep.EP_ERR_INVALID_ARG            # out not 16-byte aligned
+
+
+def test_fused_validation(ep):
+    lib = ep.library()
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    need = lib.ep_fused_workspace_bytes(64, 2, 8, 2)
+    rc, _ = call(lib, "ep_fused_dispatch_combine", f, f, f, 64, 16, 2, 8, 2, f, f, f, f, f,
+                 P(FAKE + 16), f, f, need, None, 0, None)
+    assert rc == ep.EP_ERR_INVALID_ARG            # send_rows not 128-byte aligned
+    rc, _ = call(lib, "ep_fused_dispatch_combine", f, f, f, 64, 16, 2, 8, 2, f, f, f, f, f,
+                 f, f, f, need - 256, None, 0, None)
+    assert rc == ep.EP_ERR_WORKSPACE
+    rc, _ = call(lib, "ep_fused_workspace_init", f, 16, None)
+    assert rc == ep.EP_ERR_WORKSPACE
+
+
+def test_binding_refuses_cpu_tensors(ep):
+    import torch
+    with pytest.raises(ValueError, match="GPU"):
+        ep.ep_route_topk(torch.zeros((4, 8)), 2)

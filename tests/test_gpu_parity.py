@@ -1,0 +1,236 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle, on the five
+seeded workloads at their full sizes and on edge cases.
+
+Bars: bit-exact for indices, counts, offsets, positions and dispatched
+payloads; route weights and combine within the bounds derived in gpu_util.
+Each kernel is fed the oracle's inputs for its stage, so a failure names the
+stage.  Calls go through the Python binding straight into the C ABI.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_ep_route_topk_amd import workloads as wl
+
+from gpu_util import (DEV, Case, bits, check_combine, check_route_weights, poison_bits, say,
+                      to_dev_bits)
+
+pytestmark = pytest.mark.gpu
+
+@pytest.fixture(scope="module")
+def epm():
+    from combine_ep_route_topk_amd import ep as mod
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return mod
+
+
+_CASES = {}
+
+
+def get_case(name):
+    if name not in _CASES:
+        _CASES.clear()                      # keep host memory bounded
+        _CASES[name] = Case(wl.WORKLOADS[name])
+    return _CASES[name]
+
+
+LAYOUT_KEYS = ("expert_counts", "expert_offsets", "rank_counts", "rank_offsets", "pos",
+               "slot_src")
+
+
+@pytest.mark.parametrize("name", wl.ORDER)
+def test_route(epm, name):
+    c = get_case(name)
+    w = c.w
+    say(f"route {w.describe()}")
+    idx, wt = epm.ep_route_topk(torch.from_numpy(c.logits).to(DEV), w.k, normalize=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), c.idx)
+    check_route_weights(wt.cpu().numpy(), c.wt, c.logits, c.idx, True, w.E)
+
+
+@pytest.mark.parametrize("name", ["tiny", "dsv3"])
+def test_route_unnormalized(epm, name):
+    c = get_case(name)
+    w = c.w
+    say(f"route normalize=0 {w.describe()}")
+    idx, wt = epm.ep_route_topk(torch.from_numpy(c.logits).to(DEV), w.k, normalize=False)
+    torch.cuda.synchronize()
+    o_idx, o_w = oracle.route_topk(c.logits, w.k, 0)
+    np.testing.assert_array_equal(idx.cpu().numpy(), o_idx)
+    check_route_weights(wt.cpu().numpy(), o_w, c.logits, o_idx, False, w.E)
+
+
+@pytest.mark.parametrize("name", wl.ORDER)
+def test_layout(epm, name):
+    c = get_case(name)
+    w = c.w
+    say(f"layout {w.describe()}")
+    lay = epm.ep_dispatch_layout(torch.from_numpy(c.idx).to(DEV), w.E, w.R)
+    assert epm.ep_get_device_error(lay["workspace"]) == epm.EP_OK
+    for key in LAYOUT_KEYS:
+        np.testing.assert_array_equal(lay[key].cpu().numpy(), c.lay[key], err_msg=key)
+    # a second call on the same workspace gives the same answer (state reset)
+    lay2 = epm.ep_dispatch_layout(torch.from_numpy(c.idx).to(DEV), w.E, w.R, out=lay)
+    np.testing.assert_array_equal(lay2["pos"].cpu().numpy(), c.lay["pos"])
+
+
+@pytest.mark.parametrize("name", wl.ORDER)
+def test_dispatch(epm, name):
+    c = get_case(name)
+    w = c.w
+    say(f"dispatch {w.describe()}")
+    send = poison_bits((w.S, w.H))
+    epm.ep_dispatch(to_dev_bits(c.x), torch.from_numpy(c.lay["pos"]).to(DEV), send)
+    torch.cuda.synchronize()
+    got = bits(send)
+    del send
+    assert np.array_equal(got, c.send), "dispatched payload differs from the oracle"
+
+
+@pytest.mark.parametrize("name", wl.ORDER)
+def test_combine_identity_experts(epm, name):
+    """y = the dispatched rows: the oracle's combine, and the round trip to x."""
+    c = get_case(name)
+    w = c.w
+    say(f"combine (identity experts) {w.describe()}")
+    out = epm.ep_combine(to_dev_bits(c.send), torch.from_numpy(c.lay["pos"]).to(DEV),
+                         torch.from_numpy(c.wt).to(DEV))
+    torch.cuda.synchronize()
+    got = bits(out)
+    assert np.array_equal(got, c.x), "combine(dispatch(x)) != x"
+    if w.T * w.H <= 4096 * 7168:
+        ref = oracle.combine(c.send, c.lay["pos"], c.wt)
+        assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "glm45air", "dsv3"])
+def test_combine_random_experts(epm, name):
+    """Distinct random expert outputs and signed weights: exercises the f32
+    accumulation (cancellation included) against the exact oracle."""
+    w = wl.WORKLOADS[name]
+    c = get_case(name)
+    y = wl.make_rows(w.S, w.H, seed=w.seed + 77)
+    wt = (np.random.default_rng(w.seed + 78).random((w.T, w.k), dtype=np.float32)
+          - np.float32(0.25))
+    say(f"combine (random experts) {w.describe()}")
+    out = epm.ep_combine(to_dev_bits(y), torch.from_numpy(c.lay["pos"]).to(DEV),
+                         torch.from_numpy(wt).to(DEV))
+    torch.cuda.synchronize()
+    got = bits(out)
+    ref = oracle.combine(y, c.lay["pos"], wt)
+    frac = check_combine(got, ref, y, c.lay["pos"], wt)
+    print(f"[gpu-test] {name}: {frac:.6f} of combine outputs bit-identical to the exact oracle")
+    assert frac > 0.99
+
+
+@pytest.mark.parametrize("name", wl.ORDER)
+def test_chain_on_gpu(epm, name):
+    """route -> layout -> dispatch -> combine, all on the GPU, one stream."""
+    c = get_case(name)
+    w = c.w
+    say(f"chain {w.describe()}")
+    idx, wt = epm.ep_route_topk(torch.from_numpy(c.logits).to(DEV), w.k)
+    lay = epm.ep_dispatch_layout(idx, w.E, w.R)
+    send = epm.ep_dispatch(to_dev_bits(c.x), lay["pos"])
+    out = epm.ep_combine(send, lay["pos"], wt)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(lay["pos"].cpu().numpy(), c.lay["pos"])
+    assert np.array_equal(bits(out), c.x)
+
+
+# ------------------------------------------------------------------ edge cases
+EDGE = [
+    # T, H, E, R, k, seed
+    (1, 8, 1, 1, 1, 1),           # smallest everything
+    (3, 16, 4, 2, 2, 2),
+    (130, 7176, 64, 8, 6, 3),     # ragged rows (897 vectors) and T % 4 != 0
+    (8192, 64, 1024, 8, 4, 4),    # E = 1024: 8 tiles x 1024 experts -> 8 scan blocks
+    (50000, 24, 8, 4, 2, 5),      # 25 tiles, ragged last tile
+    (257, 520, 33, 3, 5, 6),      # odd E, odd H/8 = 65
+    (64, 4096, 128, 16, 64, 7),   # k = 64 (maximum)
+]
+
+
+@pytest.mark.parametrize("T,H,E,R,k,seed", EDGE)
+def test_edge_shapes(epm, T, H, E, R, k, seed):
+    say(f"edge T={T} H={H} E={E} R={R} k={k}")
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    x = wl.make_rows(T, H, seed)
+    o_idx, o_w = oracle.route_topk(logits, k, 1)
+    o_lay = oracle.dispatch_layout(o_idx, E, R)
+    o_send = oracle.dispatch(x, o_lay["pos"])
+
+    idx, wt = epm.ep_route_topk(torch.from_numpy(logits).to(DEV), k)
+    lay = epm.ep_dispatch_layout(torch.from_numpy(o_idx).to(DEV), E, R)
+    send = poison_bits((T * k, H))
+    epm.ep_dispatch(to_dev_bits(x), torch.from_numpy(o_lay["pos"]).to(DEV), send)
+    y = wl.make_rows(T * k, H, seed + 100)
+    out_rt = epm.ep_combine(send, torch.from_numpy(o_lay["pos"]).to(DEV),
+                            torch.from_numpy(o_w).to(DEV))
+    out_y = epm.ep_combine(to_dev_bits(y), torch.from_numpy(o_lay["pos"]).to(DEV),
+                           torch.from_numpy(o_w).to(DEV))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), o_idx)
+    check_route_weights(wt.cpu().numpy(), o_w, logits, o_idx, True, E)
+    for key in LAYOUT_KEYS:
+        np.testing.assert_array_equal(lay[key].cpu().numpy(), o_lay[key], err_msg=key)
+    assert np.array_equal(bits(send), o_send)
+    assert np.array_equal(bits(out_rt), x)
+    check_combine(bits(out_y), oracle.combine(y, o_lay["pos"], o_w), y, o_lay["pos"], o_w)
+
+
+def test_layout_skewed_and_repeated_ids(epm):
+    """Every token on the same experts (one hot bucket per pick), and rows that
+    repeat an expert: the layout is still the stable counting sort."""
+    T, k, E, R = 9000, 4, 16, 4
+    idx = np.tile(np.array([3, 3, 15, 0], np.int32), (T, 1))
+    idx[::7, 1] = 9
+    say("layout skewed/repeated")
+    lay = epm.ep_dispatch_layout(torch.from_numpy(idx).to(DEV), E, R)
+    o = oracle.dispatch_layout(idx, E, R)
+    for key in LAYOUT_KEYS:
+        np.testing.assert_array_equal(lay[key].cpu().numpy(), o[key], err_msg=key)
+
+
+def test_layout_flags_bad_expert_ids(epm):
+    T, k, E, R = 300, 2, 8, 2
+    rng = np.random.default_rng(9)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    idx[5, 1] = E
+    idx[77, 0] = -1
+    say("layout with bad ids")
+    lay = epm.ep_dispatch_layout(torch.from_numpy(idx).to(DEV), E, R)
+    assert epm.ep_get_device_error(lay["workspace"]) == epm.EP_ERR_DEVICE
+    pos = lay["pos"].cpu().numpy()
+    assert pos[5, 1] == -1 and pos[77, 0] == -1
+    ok = (idx >= 0) & (idx < E)
+    flat_ok = idx[ok]
+    # the valid picks form the stable counting sort of the valid ids
+    perm = np.argsort(flat_ok, kind="stable")
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(len(perm))
+    np.testing.assert_array_equal(pos[ok], inv)
+    # and the next good call clears the error
+    lay = epm.ep_dispatch_layout(torch.from_numpy(np.where(ok, idx, 0).astype(np.int32)).to(DEV),
+                                 E, R, out=lay)
+    assert epm.ep_get_device_error(lay["workspace"]) == epm.EP_OK
+
+
+def test_streams_are_respected(epm):
+    """Work enqueued on a side stream is ordered on that stream."""
+    c = get_case("decode")
+    w = c.w
+    say("side stream chain")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        logits = torch.from_numpy(c.logits).to(DEV)
+        x = to_dev_bits(c.x)
+        idx, wt = epm.ep_route_topk(logits, w.k, stream=s)
+        lay = epm.ep_dispatch_layout(idx, w.E, w.R, stream=s)
+        send = epm.ep_dispatch(x, lay["pos"], stream=s)
+        out = epm.ep_combine(send, lay["pos"], wt, stream=s)
+    s.synchronize()
+    assert np.array_equal(bits(out), c.x)
