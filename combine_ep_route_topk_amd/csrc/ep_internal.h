@@ -70,10 +70,12 @@ inline LayoutPlan layout_plan(int T, int k, int E) {
     return p;
 }
 
-// Fused workspace: the layout part, then Data-as-Flag base words.
+// Fused workspace: the layout part (its cnt and rank arrays are used), then
+// 64-bit epoch-tagged look-back status words and Data-as-Flag base words.
 struct FusedPlan {
     LayoutPlan lay;
-    size_t off_fbase;   // u64 [nCnt]  (epoch32 << 32 | base) published bases
+    size_t off_status64;  // u64 [nScan]  (epoch32 << 32 | flag << 30 | value)
+    size_t off_fbase;     // u64 [nCnt]   (epoch32 << 32 | base) published bases
     size_t bytes;
 };
 
@@ -81,10 +83,15 @@ inline FusedPlan fused_plan(int T, int k, int E) {
     FusedPlan f{};
     f.lay = layout_plan(T, k, E);
     size_t off = f.lay.bytes;
-    f.off_fbase = off; off += align256(sizeof(uint64_t) * f.lay.nCnt);
+    f.off_status64 = off; off += align256(sizeof(uint64_t) * f.lay.nScan);
+    f.off_fbase = off;    off += align256(sizeof(uint64_t) * f.lay.nCnt);
     f.bytes = off;
     return f;
 }
+
+// Default bound of a device-side wait, in polling rounds (each round is one
+// agent-scope load plus a short sleep, roughly a microsecond).
+constexpr uint32_t kDefaultSpinLimit = uint32_t(1) << 20;
 
 inline size_t fused_row_stride(int H) {
     return (size_t(2) * H + 16 + 127) / 128 * 128;

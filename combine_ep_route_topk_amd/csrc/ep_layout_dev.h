@@ -1,0 +1,131 @@
+// ep_layout_dev.h -- device building blocks of the dispatch layout shared by
+// the three-launch layout (layout.hip) and the persistent fused mode
+// (fused.hip): the per-tile histogram with stable ranks, and a block-wide
+// exclusive scan of kScanItems counters.
+#pragma once
+
+#include "ep_device.h"
+#include "ep_internal.h"
+
+namespace ep {
+
+constexpr int kWavesPerBlock = kBlock / kWave;                          // 4
+constexpr int kChunksPerWave = kTileSlots / (kWavesPerBlock * kWave);   // 16
+static_assert(kChunksPerWave * kWavesPerBlock * kWave == kTileSlots, "tile split");
+constexpr int kScanPerThread = kScanItems / kBlock;                     // 4
+static_assert(kScanPerThread * kBlock == kScanItems, "scan split");
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+// Histogram of one tile of kTileSlots slots (UBEP sec. 2.3: per-expert token
+// counts) plus each slot's stable rank among the tile's slots of the same
+// expert (StrataCL appendix: token-local offsets).  Each wave walks its
+// 64-slot chunks in slot order; lanes holding the same expert find each other
+// with ceil(log2 E) ballots; the group's lowest lane adds the group size to
+// the wave's private LDS counter (LDS atomic, returns the old value) and
+// broadcasts the old value, which is the base rank of the group.  Waves then
+// turn their private counts into per-wave offsets.  Deterministic: no result
+// depends on the order in which atomics land.
+// Writes cnt[e * nTiles + tile] for every e < E and local_rank[s] for every
+// valid slot of the tile.  `hist` is the block's LDS scratch.
+__device__ __forceinline__ void hist_tile(const int32_t* __restrict__ topk_idx, int64_t S,
+                                          int E, int nTiles, int tile,
+                                          int32_t* __restrict__ cnt,
+                                          int32_t* __restrict__ local_rank,
+                                          int32_t (*hist)[kMaxE])
+{
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = lane_id();
+
+    for (int i = tid; i < kWavesPerBlock * E; i += kBlock) hist[i / E][i % E] = 0;
+    __syncthreads();
+
+    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
+    int key[kChunksPerWave];
+    int rank[kChunksPerWave];
+    const int64_t wave_first =
+        int64_t(tile) * kTileSlots + int64_t(wave) * kChunksPerWave * kWave;
+#pragma unroll
+    for (int c = 0; c < kChunksPerWave; ++c) {
+        const int64_t s = wave_first + c * kWave + lane;
+        const int e = s < S ? topk_idx[s] : -1;
+        const bool valid = unsigned(e) < unsigned(E);
+        uint64_t peers = ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (e >> b) & 1;
+            const uint64_t bal = ballot(bit);
+            peers &= bit ? bal : ~bal;
+        }
+        const uint64_t below = peers & lanes_below();
+        int old = 0;
+        if (valid && below == 0) old = atomicAdd(&hist[wave][e], popc64(peers));
+        const int leader = valid ? __ffsll((unsigned long long)peers) - 1 : lane;
+        const int base = __shfl(old, leader, kWave);
+        key[c] = valid ? e : -1;
+        rank[c] = base + popc64(below);
+    }
+    __syncthreads();
+
+    for (int e = tid; e < E; e += kBlock) {
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w) {
+            const int c = hist[w][e];
+            hist[w][e] = run;
+            run += c;
+        }
+        cnt[int64_t(e) * nTiles + tile] = run;
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int c = 0; c < kChunksPerWave; ++c) {
+        const int64_t s = wave_first + c * kWave + lane;
+        if (key[c] >= 0) local_rank[s] = hist[wave][key[c]] + rank[c];
+    }
+}
+
+// Block-wide scan of the kScanItems counters of scan block `blk`: loads
+// v[q] = cnt[i0 + q] (0 past nCnt), returns this thread's exclusive offset
+// inside the block and the block total.  `sh_wave_total` is LDS scratch.
+struct BlockScan {
+    int v[kScanPerThread];
+    int i0;
+    int thread_excl;
+    int total;
+};
+
+__device__ __forceinline__ BlockScan block_scan(const int32_t* __restrict__ cnt, int nCnt,
+                                                int blk, int* sh_wave_total)
+{
+    BlockScan r;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = lane_id();
+    r.i0 = blk * kScanItems + tid * kScanPerThread;
+    int tsum = 0;
+#pragma unroll
+    for (int q = 0; q < kScanPerThread; ++q) {
+        r.v[q] = r.i0 + q < nCnt ? cnt[r.i0 + q] : 0;
+        tsum += r.v[q];
+    }
+    const int incl = wave_inclusive_sum(tsum);
+    if (lane == kWave - 1) sh_wave_total[wave] = incl;
+    __syncthreads();
+    int wave_off = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+        if (w < wave) wave_off += sh_wave_total[w];
+        total += sh_wave_total[w];
+    }
+    r.thread_excl = wave_off + incl - tsum;
+    r.total = total;
+    return r;
+}
+
+}  // namespace ep

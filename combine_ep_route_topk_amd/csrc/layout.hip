@@ -29,23 +29,14 @@
 //      block 0 derives the per-expert / per-rank counts and offsets.
 #include "ep_device.h"
 #include "ep_internal.h"
+#include "ep_layout_dev.h"
 
 namespace ep {
 namespace {
 
-constexpr int kWavesPerBlock = kBlock / kWave;                         // 4
-constexpr int kChunksPerWave = kTileSlots / (kWavesPerBlock * kWave);  // 16
-static_assert(kChunksPerWave * kWavesPerBlock * kWave == kTileSlots, "tile split");
-
 constexpr uint32_t kFlagAggregate = 1u << 30;
 constexpr uint32_t kFlagInclusive = 2u << 30;
 constexpr uint32_t kValueMask = (1u << 30) - 1;
-
-__device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
-    return v;
-}
 
 __global__ __launch_bounds__(kBlock) void layout_hist_kernel(
     const int32_t* __restrict__ topk_idx, int64_t S, int E, int nTiles, int nScan,
@@ -53,66 +44,16 @@ __global__ __launch_bounds__(kBlock) void layout_hist_kernel(
     uint32_t* __restrict__ status, WsHeader* __restrict__ hdr)
 {
     __shared__ int32_t hist[kWavesPerBlock][kMaxE];
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int lane = lane_id();
-    const int tile = blockIdx.x;
-
     // Reset the scan state for this call; the scan kernel runs after this
     // kernel completes (stream order).
-    if (tile == 0) {
-        for (int i = tid; i < nScan; i += kBlock) status[i] = 0;
-        if (tid == 0) {
+    if (blockIdx.x == 0) {
+        for (int i = threadIdx.x; i < nScan; i += kBlock) status[i] = 0;
+        if (threadIdx.x == 0) {
             hdr->scan_ticket = 0;
             hdr->timeout = 0;
         }
     }
-    for (int i = tid; i < kWavesPerBlock * E; i += kBlock) hist[i / E][i % E] = 0;
-    __syncthreads();
-
-    const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-    int key[kChunksPerWave];
-    int rank[kChunksPerWave];
-    const int64_t wave_first = int64_t(tile) * kTileSlots + int64_t(wave) * kChunksPerWave * kWave;
-#pragma unroll
-    for (int c = 0; c < kChunksPerWave; ++c) {
-        const int64_t s = wave_first + c * kWave + lane;
-        const int e = s < S ? topk_idx[s] : -1;
-        const bool valid = unsigned(e) < unsigned(E);
-        uint64_t peers = ballot(valid);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t bal = ballot(bit);
-            peers &= bit ? bal : ~bal;
-        }
-        const uint64_t below = peers & lanes_below();
-        int old = 0;
-        if (valid && below == 0) old = atomicAdd(&hist[wave][e], popc64(peers));
-        const int leader = valid ? __ffsll((unsigned long long)peers) - 1 : lane;
-        const int base = __shfl(old, leader, kWave);
-        key[c] = valid ? e : -1;
-        rank[c] = base + popc64(below);
-    }
-    __syncthreads();
-
-    // per-wave counts -> per-wave exclusive offsets; tile total per expert
-    for (int e = tid; e < E; e += kBlock) {
-        int run = 0;
-#pragma unroll
-        for (int w = 0; w < kWavesPerBlock; ++w) {
-            const int c = hist[w][e];
-            hist[w][e] = run;
-            run += c;
-        }
-        cnt[int64_t(e) * nTiles + tile] = run;
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int c = 0; c < kChunksPerWave; ++c) {
-        const int64_t s = wave_first + c * kWave + lane;
-        if (key[c] >= 0) local_rank[s] = hist[wave][key[c]] + rank[c];
-    }
+    hist_tile(topk_idx, S, E, nTiles, blockIdx.x, cnt, local_rank, hist);
 }
 
 __global__ __launch_bounds__(kBlock) void layout_scan_kernel(
@@ -127,37 +68,19 @@ __global__ __launch_bounds__(kBlock) void layout_scan_kernel(
     const int wave = tid / kWave;
     const int lane = lane_id();
 
-    // Ticket order = launch order of the blocks that are already running, so
-    // every predecessor a block waits for has started (forward progress).
+    // Ticket order = order in which blocks started, so every predecessor a
+    // block waits for is already running (forward progress).
     if (tid == 0) sh_block = int(fetch_add(&hdr->scan_ticket, 1u));
     __syncthreads();
     const int blk = sh_block;
-
-    constexpr int kPer = kScanItems / kBlock;     // 4 counters per thread
-    const int i0 = blk * kScanItems + tid * kPer;
-    int v[kPer];
-    int tsum = 0;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-        v[q] = i0 + q < nCnt ? cnt[i0 + q] : 0;
-        tsum += v[q];
-    }
-    const int incl = wave_inclusive_sum(tsum);
-    if (lane == kWave - 1) sh_wave_total[wave] = incl;
-    __syncthreads();
-    int wave_off = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) {
-        if (w < wave) wave_off += sh_wave_total[w];
-        total += sh_wave_total[w];
-    }
+    const BlockScan bs = block_scan(cnt, nCnt, blk, sh_wave_total);
 
     if (wave == 0) {
         int exclusive = 0;
         if (blk == 0) {
-            if (lane == 0) st_relaxed(&status[0], kFlagInclusive | uint32_t(total));
+            if (lane == 0) st_relaxed(&status[0], kFlagInclusive | uint32_t(bs.total));
         } else {
-            if (lane == 0) st_relaxed(&status[blk], kFlagAggregate | uint32_t(total));
+            if (lane == 0) st_relaxed(&status[blk], kFlagAggregate | uint32_t(bs.total));
             int look = blk - 1;
             uint32_t spins = 0;
             while (true) {
@@ -172,7 +95,7 @@ __global__ __launch_bounds__(kBlock) void layout_scan_kernel(
                     continue;
                 }
                 const uint64_t inc = ballot((st >> 30) == 2);
-                int val = int(st & kValueMask);
+                const int val = int(st & kValueMask);
                 if (inc != 0) {
                     const int first = __ffsll((unsigned long long)inc) - 1;
                     exclusive += wave_sum(lane <= first ? val : 0);
@@ -181,20 +104,21 @@ __global__ __launch_bounds__(kBlock) void layout_scan_kernel(
                 exclusive += wave_sum(val);
                 look -= kWave;
             }
-            if (lane == 0) st_relaxed(&status[blk], kFlagInclusive | uint32_t(exclusive + total));
+            if (lane == 0)
+                st_relaxed(&status[blk], kFlagInclusive | uint32_t(exclusive + bs.total));
         }
         if (lane == 0) sh_exclusive = exclusive;
     }
     __syncthreads();
 
-    int run = sh_exclusive + wave_off + incl - tsum;
+    int run = sh_exclusive + bs.thread_excl;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-        const int i = i0 + q;
+    for (int q = 0; q < kScanPerThread; ++q) {
+        const int i = bs.i0 + q;
         if (i < nCnt) {
             base[i] = run;
             if (i % nTiles == 0) expert_offsets[i / nTiles] = run;
-            run += v[q];
+            run += bs.v[q];
             if (i == nCnt - 1) expert_offsets[E] = run;
         }
     }
@@ -257,7 +181,7 @@ hipError_t launch_dispatch_layout(const int32_t* topk_idx, int T, int k, int E, 
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(layout_scan_kernel, dim3(p.nScan), dim3(kBlock), 0, s,
                        cnt, p.nCnt, p.nTiles, E, base, expert_offsets, status, hdr,
-                       uint32_t(1) << 22);
+                       kDefaultSpinLimit);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int grid = int((p.S + kBlock - 1) / kBlock);

@@ -1,0 +1,56 @@
+"""Build tests/emu/_build/libep_emu.so: the library's own HIP sources compiled
+for the host CPU against a small emulation of the HIP device API (lane fibers,
+wave rendezvous, workgroup barriers; see fake/hip/hip_runtime.h).
+
+Test infrastructure only.  It lets the CPU test suite run the real kernel code
+-- including the fused persistent mode, whose GPU launch is switched off in the
+product build -- against the CPU oracle, with a limited number of co-resident
+workgroups."""
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+CSRC = os.path.join(ROOT, "combine_ep_route_topk_amd", "csrc")
+OUT = os.path.join(HERE, "_build")
+LIB = os.path.join(OUT, "libep_emu.so")
+
+
+def compiler():
+    for c in (os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "clang++"),
+              shutil.which("clang++") or ""):
+        if c and os.path.exists(c):
+            return c
+    return None
+
+
+def build(extra=()):
+    cxx = compiler()
+    if cxx is None:
+        raise RuntimeError("clang++ not found")
+    os.makedirs(OUT, exist_ok=True)
+    flags = ["-std=c++17", "-O1", "-g", "-fPIC", "-DEP_ENABLE_FUSED_LAUNCH",
+             "-I", os.path.join(HERE, "fake"), "-I", os.path.join(ROOT, "include"), *extra]
+    jobs = [(os.path.join(CSRC, f), os.path.join(OUT, f + ".o"), True)
+            for f in sorted(os.listdir(CSRC)) if f.endswith(".hip")]
+    jobs.append((os.path.join(HERE, "emu_runtime.cpp"), os.path.join(OUT, "emu_runtime.o"), False))
+
+    def one(job):
+        src, obj, as_cxx = job
+        cmd = [cxx, *flags] + (["-x", "c++"] if as_cxx else []) + ["-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode:
+            raise RuntimeError(f"{' '.join(cmd)}\n{r.stderr}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(one, jobs))
+    subprocess.run([cxx, "-shared", "-o", LIB + ".tmp", *objs, "-lpthread", *extra], check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,129 @@
+// Host emulation of the HIP device subset used by the ep kernels: each
+// workgroup runs on one OS thread as kBlock lane fibers (ucontext); wave ops
+// rendezvous the 64 fibers of a wave; __syncthreads rendezvouses all fibers.
+#pragma once
+#include <ucontext.h>
+#include <atomic>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <cmath>
+#include <thread>
+#include <vector>
+#include <functional>
+#include <stdexcept>
+
+#define __global__
+#define __device__
+#define __host__
+#define __forceinline__ inline
+#define __noinline__ __attribute__((noinline))
+#define __launch_bounds__(x)
+#define __shared__ static thread_local
+#define __restrict__ __restrict
+
+typedef int hipError_t;
+typedef void* hipStream_t;
+enum { hipSuccess = 0, hipErrorNotSupported = 801 };
+struct dim3 { unsigned x, y, z; dim3(unsigned a = 1, unsigned b = 1, unsigned c = 1) : x(a), y(b), z(c) {} };
+
+namespace emu {
+struct Lane;
+struct Group;
+struct U3 { unsigned x, y, z; };
+extern thread_local Group* g_group;
+extern thread_local int g_lane_tid;   // threadIdx.x of the running fiber
+extern thread_local U3 g_block;
+extern U3 g_grid;
+extern long g_op_limit;
+
+enum OpKind { OP_NONE, OP_BALLOT, OP_SHFL, OP_READLANE, OP_READFIRST, OP_SYNC, OP_EXIT };
+
+struct Group {
+    int nthreads;
+    std::vector<ucontext_t> ctx;
+    std::vector<std::vector<char>> stacks;
+    ucontext_t sched;
+    std::vector<int> op;          // pending op per fiber
+    std::vector<uint64_t> val;    // operand per fiber
+    std::vector<int> arg;         // src lane / width etc.
+    std::vector<uint64_t> res;
+    std::vector<long> seq;        // count of wave ops per fiber (to detect mismatch)
+    std::function<void()> body;
+    long steps = 0;
+};
+
+void yield_op(int kind, uint64_t v, int a);
+uint64_t result();
+}  // namespace emu
+
+struct EmuIdx { unsigned operator()() const; };
+#define threadIdx (emu::U3{(unsigned)emu::g_lane_tid, 0u, 0u})
+#define blockIdx (emu::g_block)
+#define gridDim (emu::g_grid)
+
+inline int __lane_id() { return emu::g_lane_tid % 64; }
+inline uint64_t __ballot(int p) { emu::yield_op(emu::OP_BALLOT, p ? 1 : 0, 0); return emu::result(); }
+template <class T> inline T emu_shfl_idx(T v, int src, int width) {
+    static_assert(sizeof(T) <= 8, "");
+    uint64_t bits = 0; std::memcpy(&bits, &v, sizeof(T));
+    int self = __lane_id();
+    int base = self & ~(width - 1);
+    int s = base + (src & (width - 1));
+    emu::yield_op(emu::OP_SHFL, bits, s);
+    uint64_t r = emu::result(); T out; std::memcpy(&out, &r, sizeof(T)); return out;
+}
+template <class T> inline T __shfl(T v, int src, int width = 64) { return emu_shfl_idx(v, src, width); }
+template <class T> inline T __shfl_xor(T v, int m, int width = 64) {
+    int self = __lane_id(); int idx = self ^ m;
+    if (idx >= ((self + width) & ~(width - 1))) idx = self;
+    uint64_t bits = 0; std::memcpy(&bits, &v, sizeof(T));
+    emu::yield_op(emu::OP_SHFL, bits, idx);
+    uint64_t r = emu::result(); T out; std::memcpy(&out, &r, sizeof(T)); return out;
+}
+template <class T> inline T __shfl_up(T v, unsigned d, int width = 64) {
+    int self = __lane_id(); int idx = self - (int)d;
+    if (idx < (self & ~(width - 1))) idx = self;
+    uint64_t bits = 0; std::memcpy(&bits, &v, sizeof(T));
+    emu::yield_op(emu::OP_SHFL, bits, idx);
+    uint64_t r = emu::result(); T out; std::memcpy(&out, &r, sizeof(T)); return out;
+}
+template <class T> inline T emu_readlane(T v, int l) { return emu_shfl_idx(v, l, 64); }
+template <class T> inline T emu_readfirst(T v) { return emu_shfl_idx(v, 0, 64); }
+#define __builtin_amdgcn_readlane(v, l) emu_readlane((v), (l))
+#define __builtin_amdgcn_readfirstlane(v) emu_readfirst((v))
+inline void __syncthreads() { emu::yield_op(emu::OP_SYNC, 0, 0); }
+#define __builtin_amdgcn_s_sleep(n) emu::yield_op(emu::OP_NONE, 0, 0)
+#define __builtin_amdgcn_fence(order, scope) std::atomic_thread_fence(std::memory_order_seq_cst)
+inline int __popcll(unsigned long long x) { return __builtin_popcountll(x); }
+inline int __ffsll(unsigned long long x) { return __builtin_ffsll((long long)x); }
+inline int __clz(int x) { return x == 0 ? 32 : __builtin_clz((unsigned)x); }
+inline float __uint_as_float(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
+#define __HIP_MEMORY_SCOPE_AGENT 3
+template <class T> inline T emu_atomic_load(const T* p) {
+    emu::yield_op(emu::OP_NONE, 0, 0);   // let other fibers / threads progress
+    return __atomic_load_n(p, __ATOMIC_SEQ_CST);
+}
+template <class T, class U> inline void emu_atomic_store(T* p, U v) { __atomic_store_n(p, (T)v, __ATOMIC_SEQ_CST); }
+template <class T, class U> inline T emu_atomic_fetch_add(T* p, U v) { return __atomic_fetch_add(p, (T)v, __ATOMIC_SEQ_CST); }
+#define __hip_atomic_load(p, o, s) emu_atomic_load((p))
+#define __hip_atomic_store(p, v, o, s) emu_atomic_store((p), (v))
+#define __hip_atomic_fetch_add(p, v, o, s) emu_atomic_fetch_add((p), (v))
+template <class T, class U> inline T atomicAdd(T* p, U v) { return __atomic_fetch_add(p, (T)v, __ATOMIC_SEQ_CST); }
+
+inline hipError_t hipGetLastError() { return hipSuccess; }
+inline hipError_t hipGetDevice(int* d) { *d = 0; return 0; }
+inline hipError_t hipOccupancyMaxActiveBlocksPerMultiprocessor(int* n, const void*, int, int) { *n = 2; return 0; }
+enum { hipDeviceAttributeMultiprocessorCount = 1 };
+inline hipError_t hipDeviceGetAttribute(int* v, int, int) { *v = 4; return 0; }
+
+namespace emu {
+void launch(dim3 grid, dim3 block, std::function<void()> body);
+}
+#define hipLaunchKernelGGL(K, G, B, SH, S, ...) emu::launch(dim3(G), dim3(B), [=]() { K(__VA_ARGS__); })
+
+enum hipMemcpyKind { hipMemcpyHostToDevice = 1, hipMemcpyDeviceToHost = 2, hipMemcpyDeviceToDevice = 3 };
+inline hipError_t hipStreamSynchronize(hipStream_t) { return 0; }
+inline hipError_t hipMemcpy(void* d, const void* s, size_t n, hipMemcpyKind) { std::memcpy(d, s, n); return 0; }
+inline const char* hipGetErrorString(hipError_t) { return "emu"; }

@@ -1,0 +1,198 @@
+"""The library's kernel sources run on the CPU under a host emulation of the
+HIP device API (tests/emu), checked against the CPU oracle.
+
+This covers the fused flag-in-payload mode, whose GPU launch is switched off
+in the product build, with the same source the GPU would run: the persistent
+ticket loop, the epoch-tagged look-back and base words, the per-row trailers,
+the bounded waits, and the last-workgroup reset of the workspace -- with only
+a handful of workgroups resident at a time, which exercises the forward-progress
+argument (an item only waits for smaller tickets).  The unfused kernels run
+too, as a check of the emulation itself against the results the GPU gives.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from combine_ep_route_topk_amd import workloads as wl
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def emu():
+    import sys
+    sys.path.insert(0, os.path.join(HERE, "emu"))
+    import build as emu_build
+    if emu_build.compiler() is None:
+        pytest.skip("clang++ not available")
+    L = ctypes.CDLL(emu_build.build())
+    L.ep_dispatch_layout_workspace_bytes.restype = ctypes.c_size_t
+    L.ep_fused_workspace_bytes.restype = ctypes.c_size_t
+    L.ep_fused_row_stride_bytes.restype = ctypes.c_size_t
+    L.ep_last_error.restype = ctypes.c_char_p
+    L.emu_set_pool(4)
+    return L
+
+
+def p(a):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def aligned(nbytes, align=256):
+    buf = np.zeros(nbytes + align, np.uint8)
+    off = (-buf.ctypes.data) % align
+    return buf[off:off + nbytes]
+
+
+class Emu:
+    def __init__(self, L, T, H, E, R, k):
+        self.L, self.T, self.H, self.E, self.R, self.k = L, T, H, E, R, k
+
+    def check(self, rc):
+        assert rc == 0, self.L.ep_last_error().decode()
+
+    def layout_arrays(self):
+        E, R, T, k = self.E, self.R, self.T, self.k
+        return dict(expert_counts=np.zeros(E, np.int32), expert_offsets=np.zeros(E + 1, np.int32),
+                    rank_counts=np.zeros(R, np.int32), rank_offsets=np.zeros(R + 1, np.int32),
+                    pos=np.zeros((T, k), np.int32))
+
+    def unfused(self, logits, x):
+        L, T, H, E, R, k = self.L, self.T, self.H, self.E, self.R, self.k
+        idx = np.zeros((T, k), np.int32)
+        wt = np.zeros((T, k), np.float32)
+        self.check(L.ep_route_topk(p(logits), T, E, k, 1, p(idx), p(wt), None))
+        lay = self.layout_arrays()
+        lay["slot_src"] = np.zeros(T * k, np.int32)
+        ws = aligned(L.ep_dispatch_layout_workspace_bytes(T, k, E, R))
+        self.check(L.ep_dispatch_layout(p(idx), T, k, E, R, p(lay["expert_counts"]),
+                                        p(lay["expert_offsets"]), p(lay["rank_counts"]),
+                                        p(lay["rank_offsets"]), p(lay["pos"]), p(lay["slot_src"]),
+                                        p(ws), ctypes.c_size_t(ws.size), None))
+        xa = aligned(x.nbytes, 16).view(np.uint16).reshape(x.shape)
+        xa[:] = x
+        send = aligned(T * k * H * 2, 16).view(np.uint16).reshape(T * k, H)
+        self.check(L.ep_dispatch(p(xa), T, H, k, p(lay["pos"]), p(send), None))
+        out = aligned(T * H * 2, 16).view(np.uint16).reshape(T, H)
+        self.check(L.ep_combine(p(send), p(lay["pos"]), p(wt), T, H, k, p(out), None))
+        return idx, wt, lay, send, out
+
+    def fused_setup(self):
+        L = self.L
+        self.ws = aligned(L.ep_fused_workspace_bytes(self.T, self.k, self.E, self.R))
+        self.check(L.ep_fused_workspace_init(p(self.ws), ctypes.c_size_t(self.ws.size), None))
+        self.stride = L.ep_fused_row_stride_bytes(self.H)
+        self.rows = aligned(self.T * self.k * self.stride, 128).reshape(self.T * self.k, self.stride)
+        self.flay = self.layout_arrays()
+        self.out = aligned(self.T * self.H * 2, 16).view(np.uint16).reshape(self.T, self.H)
+
+    def fused(self, x, idx, wt, spin_limit=1 << 26):
+        L = self.L
+        xa = aligned(x.nbytes, 16).view(np.uint16).reshape(x.shape)
+        xa[:] = x
+        e = ctypes.c_uint64(0)
+        lay = self.flay
+        rc = L.ep_fused_dispatch_combine(
+            p(xa), p(np.ascontiguousarray(idx)), p(np.ascontiguousarray(wt)), self.T, self.H,
+            self.k, self.E, self.R, p(lay["expert_counts"]), p(lay["expert_offsets"]),
+            p(lay["rank_counts"]), p(lay["rank_offsets"]), p(lay["pos"]), p(self.rows),
+            p(self.out), p(self.ws), ctypes.c_size_t(self.ws.size), ctypes.byref(e),
+            ctypes.c_uint32(spin_limit), None)
+        self.check(rc)
+        return e.value, L.ep_get_device_error(p(self.ws), None)
+
+
+SHAPES = [
+    # T, H, E, R, k, seed
+    (128, 256, 8, 2, 2, 1001),      # the tiny workload's shape
+    (128, 7168, 256, 32, 8, 1002),  # the decode-like workload's shape (k = 8 path)
+    (5, 16, 4, 2, 2, 3),
+    (130, 7176, 64, 8, 6, 4),       # ragged rows, runtime-k path
+    (600, 64, 256, 32, 8, 5),       # two layout tiles
+    (1, 8, 1, 1, 1, 6),
+    (3000, 24, 33, 3, 5, 7),        # four tiles, odd E
+    (8192, 16, 1024, 8, 4, 8),      # eight look-back blocks
+]
+
+
+@pytest.mark.parametrize("T,H,E,R,k,seed", SHAPES)
+def test_emulated_kernels_match_oracle(emu, T, H, E, R, k, seed):
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    x = wl.make_rows(T, H, seed)
+    o_idx, o_w = oracle.route_topk(logits, k, 1)
+    o_lay = oracle.dispatch_layout(o_idx, E, R)
+    o_send = oracle.dispatch(x, o_lay["pos"])
+    m = Emu(emu, T, H, E, R, k)
+
+    # unfused chain (the emulation reproduces what the GPU computes)
+    idx, wt, lay, send, out = m.unfused(logits, x)
+    np.testing.assert_array_equal(idx, o_idx)
+    np.testing.assert_allclose(wt, o_w, rtol=(k + 4 + 8) * 2.0 ** -24)
+    for key in lay:
+        np.testing.assert_array_equal(lay[key], o_lay[key], err_msg=key)
+    assert np.array_equal(send, o_send)
+    assert np.array_equal(out, x)
+
+    # fused: two calls on one workspace, the second on different rows
+    m.fused_setup()
+    x2 = wl.make_rows(T, H, seed + 1)
+    e1, st1 = m.fused(x2, o_idx, o_w)
+    assert st1 == 0 and np.array_equal(m.out, x2)
+    e2, st2 = m.fused(x, o_idx, o_w)
+    assert st2 == 0
+    assert e2 == e1 + 1 or (e1 + 1) % (1 << 32) == 0
+    for key in m.flay:
+        np.testing.assert_array_equal(m.flay[key], o_lay[key], err_msg=key)
+    payload = m.rows[:, :2 * H].copy().view(np.uint16)
+    assert np.array_equal(payload, o_send), "fused payload"
+    assert np.array_equal(m.rows[:, 2 * H:2 * H + 16],
+                          oracle.fused_trailers(e2, o_lay["slot_src"])), "fused trailers"
+    assert np.array_equal(m.out, x), "fused combine"
+
+
+def test_emulated_fused_random_experts_equals_combine(emu):
+    """Non-uniform weights: the fused reduction is bit-identical to ep_combine
+    over the same rows (they share the arithmetic)."""
+    T, H, E, R, k = 200, 520, 16, 4, 8
+    rng = np.random.default_rng(11)
+    o_idx, _ = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
+    wt = rng.random((T, k), dtype=np.float32) - np.float32(0.3)
+    x = wl.make_rows(T, H, 12)
+    m = Emu(emu, T, H, E, R, k)
+    m.fused_setup()
+    _, st = m.fused(x, o_idx, wt)
+    assert st == 0
+    o_lay = oracle.dispatch_layout(o_idx, E, R)
+    o_send = oracle.dispatch(x, o_lay["pos"])
+    # reference: the unfused combine kernel over the same rows
+    out_ref = aligned(T * H * 2, 16).view(np.uint16).reshape(T, H)
+    send = aligned(o_send.nbytes, 16).view(np.uint16).reshape(o_send.shape)
+    send[:] = o_send
+    m.check(emu.ep_combine(p(send), p(o_lay["pos"]), p(wt), T, H, k, p(out_ref), None))
+    assert np.array_equal(m.out, out_ref)
+
+
+def test_emulated_bounded_waits_and_bad_ids(emu):
+    T, H, E, R, k = 256, 32, 8, 2, 2
+    rng = np.random.default_rng(13)
+    o_idx, o_w = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
+    x = wl.make_rows(T, H, 14)
+    m = Emu(emu, T, H, E, R, k)
+    m.fused_setup()
+    # a spin limit of one polling round: the call drains with OK or TIMEOUT
+    _, st = m.fused(x, o_idx, o_w, spin_limit=1)
+    assert st in (0, 6)
+    # and the workspace is usable again right away
+    _, st = m.fused(x, o_idx, o_w)
+    assert st == 0 and np.array_equal(m.out, x)
+    # an id outside [0, E) is reported and gets pos = -1
+    bad = o_idx.copy()
+    bad[7, 1] = E + 3
+    _, st = m.fused(x, bad, o_w)
+    assert st == 5 and m.flay["pos"][7, 1] == -1
+    _, st = m.fused(x, o_idx, o_w)
+    assert st == 0

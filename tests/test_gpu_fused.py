@@ -1,0 +1,176 @@
+"""GPU parity of the fused flag-in-payload mode (ep_fused_dispatch_combine):
+layout outputs, payload rows, trailers and the combined output against the
+CPU oracle, equality with the three-launch path, epochs across calls, the
+bounded-wait error path and bad expert ids."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_ep_route_topk_amd import workloads as wl
+
+from gpu_util import DEV, Case, bits, say, to_dev_bits
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skip(reason="the fused persistent launch is switched off on the GPU: its first "
+                            "MI355X launch did not return and the cause is not identified; the "
+                            "same kernel source is checked on the CPU by tests/test_emu_kernels.py"),
+]
+
+LAYOUT_KEYS = ("expert_counts", "expert_offsets", "rank_counts", "rank_offsets", "pos")
+
+
+@pytest.fixture(scope="module")
+def epm():
+    from combine_ep_route_topk_amd import ep as mod
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return mod
+
+
+def split_rows(rows: np.ndarray, H: int):
+    payload = rows[:, :2 * H].copy().view(np.uint16)
+    trailer = rows[:, 2 * H:2 * H + 16]
+    return payload, trailer
+
+
+def check_fused(epm, fz, x_bits, idx, wt, E, R, H, k, expect_out=None):
+    o_lay = oracle.dispatch_layout(idx, E, R)
+    for key in LAYOUT_KEYS:
+        np.testing.assert_array_equal(fz[key].cpu().numpy(), o_lay[key], err_msg=key)
+    payload, trailer = split_rows(fz["send_rows"].cpu().numpy(), H)
+    o_send = oracle.dispatch(x_bits, o_lay["pos"])
+    assert np.array_equal(payload, o_send), "fused payload differs from the oracle"
+    assert np.array_equal(trailer, oracle.fused_trailers(fz["epoch"], o_lay["slot_src"])), \
+        "fused trailers differ from the oracle"
+    out = bits(fz["out"])
+    ref = oracle.combine(o_send, o_lay["pos"], wt) if expect_out is None else expect_out
+    assert np.array_equal(out, ref), "fused combine differs from the oracle"
+    return o_lay, o_send
+
+
+@pytest.mark.parametrize("name", wl.ORDER)
+def test_fused_matches_oracle(epm, name):
+    w = wl.WORKLOADS[name]
+    c = Case(w)
+    say(f"fused {w.describe()}")
+    x = to_dev_bits(c.x)
+    idx = torch.from_numpy(c.idx).to(DEV)
+    wt = torch.from_numpy(c.wt).to(DEV)
+    fz = epm.ep_fused_dispatch_combine(x, idx, wt, w.E, w.R, want_epoch=True)
+    torch.cuda.synchronize()
+    assert epm.ep_get_device_error(fz["workspace"]) == epm.EP_OK
+    # identity experts: the round trip returns x exactly
+    check_fused(epm, fz, c.x, c.idx, c.wt, w.E, w.R, w.H, w.k, expect_out=c.x)
+    # and equals the three-launch path bit for bit
+    lay = epm.ep_dispatch_layout(idx, w.E, w.R)
+    send = epm.ep_dispatch(x, lay["pos"])
+    out = epm.ep_combine(send, lay["pos"], wt)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), fz["out"].view(torch.int16))
+
+
+def test_fused_epochs_and_reuse(epm):
+    """Repeated calls on one workspace: the epoch advances by one per call, and
+    a call on new inputs over rows holding the previous call's trailers reads
+    only its own rows."""
+    w = wl.WORKLOADS["glm45air"]
+    c = Case(w)
+    idx = torch.from_numpy(c.idx).to(DEV)
+    wt = torch.from_numpy(c.wt).to(DEV)
+    x1 = to_dev_bits(c.x)
+    x2_bits = wl.make_rows(w.T, w.H, seed=4242)
+    x2 = to_dev_bits(x2_bits)
+    say("fused epochs")
+    fz = epm.ep_fused_dispatch_combine(x1, idx, wt, w.E, w.R, want_epoch=True)
+    e1 = fz["epoch"]
+    for rep in range(6):
+        xin, xb = (x2, x2_bits) if rep % 2 == 0 else (x1, c.x)
+        fz = epm.ep_fused_dispatch_combine(xin, idx, wt, w.E, w.R, out=fz, want_epoch=True)
+        torch.cuda.synchronize()
+        assert fz["epoch"] == e1 + rep + 1
+        assert epm.ep_get_device_error(fz["workspace"]) == epm.EP_OK
+        assert np.array_equal(bits(fz["out"]), xb), f"call {rep}: stale rows were read"
+    check_fused(epm, fz, c.x, c.idx, c.wt, w.E, w.R, w.H, w.k, expect_out=c.x)
+
+
+def test_fused_back_to_back_without_sync(epm):
+    w = wl.WORKLOADS["dsv3"]
+    c = Case(w)
+    idx = torch.from_numpy(c.idx).to(DEV)
+    wt = torch.from_numpy(c.wt).to(DEV)
+    x = to_dev_bits(c.x)
+    say("fused back-to-back x20")
+    fz = epm.fused_outputs(w.T, w.H, w.k, w.E, w.R, DEV)
+    for _ in range(20):
+        epm.ep_fused_dispatch_combine(x, idx, wt, w.E, w.R, out=fz)
+    torch.cuda.synchronize()
+    assert epm.ep_get_device_error(fz["workspace"]) == epm.EP_OK
+    assert np.array_equal(bits(fz["out"]), c.x)
+
+
+FUSED_EDGE = [
+    (1, 8, 1, 1, 1, 11),
+    (5, 16, 4, 2, 2, 12),
+    (130, 7176, 64, 8, 6, 13),     # ragged rows, runtime-k path
+    (8192, 64, 1024, 8, 4, 14),    # 8 scan blocks
+    (3000, 520, 33, 3, 5, 15),
+    (64, 4096, 128, 16, 64, 16),   # k = 64
+    (20000, 256, 16, 4, 8, 17),    # many items, k = 8 path, small rows
+]
+
+
+@pytest.mark.parametrize("T,H,E,R,k,seed", FUSED_EDGE)
+def test_fused_edge_shapes(epm, T, H, E, R, k, seed):
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, E), dtype=np.float32)
+    x = wl.make_rows(T, H, seed)
+    o_idx, o_w = oracle.route_topk(logits, k, 1)
+    say(f"fused edge T={T} H={H} E={E} R={R} k={k}")
+    fz = epm.ep_fused_dispatch_combine(to_dev_bits(x), torch.from_numpy(o_idx).to(DEV),
+                                       torch.from_numpy(o_w).to(DEV), E, R, want_epoch=True)
+    torch.cuda.synchronize()
+    assert epm.ep_get_device_error(fz["workspace"]) == epm.EP_OK
+    check_fused(epm, fz, x, o_idx, o_w, E, R, H, k, expect_out=x)
+
+
+def test_fused_bounded_waits_drain_and_recover(epm):
+    """With a spin limit of one polling round, unsatisfied waits give up at
+    once: the call ends with EP_OK or EP_ERR_TIMEOUT (never hangs), and the
+    next call on the same workspace is correct."""
+    w = wl.WORKLOADS["dsv3"]
+    c = Case(w)
+    idx = torch.from_numpy(c.idx).to(DEV)
+    wt = torch.from_numpy(c.wt).to(DEV)
+    x = to_dev_bits(c.x)
+    say("fused spin_limit=1")
+    fz = epm.fused_outputs(w.T, w.H, w.k, w.E, w.R, DEV)
+    epm.ep_fused_dispatch_combine(x, idx, wt, w.E, w.R, out=fz, spin_limit=1)
+    rc = epm.ep_get_device_error(fz["workspace"])
+    assert rc in (epm.EP_OK, epm.EP_ERR_TIMEOUT)
+    print(f"[gpu-test] spin_limit=1 -> {rc}")
+    say("fused after a bounded-wait call")
+    epm.ep_fused_dispatch_combine(x, idx, wt, w.E, w.R, out=fz)
+    torch.cuda.synchronize()
+    assert epm.ep_get_device_error(fz["workspace"]) == epm.EP_OK
+    assert np.array_equal(bits(fz["out"]), c.x)
+
+
+def test_fused_flags_bad_expert_ids(epm):
+    T, H, k, E, R = 300, 64, 2, 8, 2
+    rng = np.random.default_rng(21)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    idx[10, 0] = 99
+    x = wl.make_rows(T, H, 21)
+    wt = np.full((T, k), 0.5, np.float32)
+    say("fused with bad ids")
+    fz = epm.ep_fused_dispatch_combine(to_dev_bits(x), torch.from_numpy(idx).to(DEV),
+                                       torch.from_numpy(wt).to(DEV), E, R)
+    torch.cuda.synchronize()
+    assert epm.ep_get_device_error(fz["workspace"]) == epm.EP_ERR_DEVICE
+    assert fz["pos"].cpu().numpy()[10, 0] == -1
+    # the next good call clears it
+    idx[10, 0] = 3
+    epm.ep_fused_dispatch_combine(to_dev_bits(x), torch.from_numpy(idx).to(DEV),
+                                  torch.from_numpy(wt).to(DEV), E, R, out=fz)
+    assert epm.ep_get_device_error(fz["workspace"]) == epm.EP_OK
