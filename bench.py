@@ -9,8 +9,10 @@ The fused flag-in-payload mode is timed beside it on the same inputs.
 
 Prints ONE JSON line.  `value` = algorithmic HBM bytes of a whole step /
 step time (GB/s); tokens/s and the fraction of the 8 TB/s HBM peak ride along.
-`roofline` is measured live with HIP events around the dominant kernel on
-the stream it runs on; `cpu_baseline` times the CPU oracle on this host.
+`roofline` is measured live: every op of every timed step is bracketed by two
+hipEvent_t that its own kernels' dispatch packets record (the library's
+timing hook), on the stream they run on -- the interval a kernel-trace
+profiler reports; `cpu_baseline` times the CPU oracle on this host.
 """
 from __future__ import annotations
 
@@ -40,10 +42,38 @@ def parse():
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device-to-device copy --steps times "
+                         "(scales the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
-def src_digest(*names) -> str:
+def copy_calibration(steps: int) -> None:
+    import torch
+    n = 512 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "steps": steps,
+                      "us_per_copy": round(us, 2), "gbps": round(2 * n / us / 1e3, 1)}),
+          flush=True)
+
+
+# Source files whose text determines each kernel's memory traffic.
+KERNEL_SOURCES = {
+    "dispatch": ["dispatch.hip", "ep_device.h", "ep_internal.h"],
+    "combine": ["combine.hip", "ep_combine_dev.h", "ep_device.h", "ep_internal.h"],
+}
+
+
+def src_digest(names) -> str:
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(ROOT, "combine_ep_route_topk_amd", "csrc", n), "rb") as f:
@@ -51,9 +81,9 @@ def src_digest(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str, workload: str, src: str):
+def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 PMC summary, or None
-    when absent or when the kernel source changed since it was taken."""
+    when absent or when the kernel's sources changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -62,13 +92,16 @@ def traffic_for(kernel: str, workload: str, src: str):
         for ln in f:
             if ln.startswith("json:"):
                 rec = json.loads(ln[5:])
-    if rec.get("source_sha256_16") != src_digest(src):
+    if rec.get("source_sha256_16") != src_digest(KERNEL_SOURCES[kernel]):
         return None
     return rec.get("hbm_bytes_per_launch")
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: the multi-GPU "
                                    "exchange is not part of it; run with --gpus 1"}))
@@ -94,21 +127,23 @@ def main():
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    hip = ep.HipEvents()
+
     def step(ev=None):
+        # ev: per-op (start, stop) hipEvent_t pairs, recorded by the ops' own
+        # kernel dispatch packets through the library's timing hook
         if ev is not None:
-            ev[0].record(stream)
+            ep.ep_set_timing_events(*ev[0])
         ep.ep_route_topk(logits, k, True, idx, wt, stream=stream)
         if ev is not None:
-            ev[1].record(stream)
+            ep.ep_set_timing_events(*ev[1])
         ep.ep_dispatch_layout(idx, E, R, out=lay, stream=stream)
         if ev is not None:
-            ev[2].record(stream)
+            ep.ep_set_timing_events(*ev[2])
         ep.ep_dispatch(x, lay["pos"], send, stream=stream)
         if ev is not None:
-            ev[3].record(stream)
+            ep.ep_set_timing_events(*ev[3])
         ep.ep_combine(send, lay["pos"], wt, out, stream=stream)
-        if ev is not None:
-            ev[4].record(stream)
 
     # correctness gate before timing: the identity-expert round trip is exact
     step()
@@ -125,7 +160,7 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    evs = [[(hip.create(), hip.create()) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -137,7 +172,11 @@ def main():
     per_op = {n: [] for n in names}
     for e in evs:
         for j, n in enumerate(names):
-            per_op[n].append(e[j].elapsed_time(e[j + 1]) * 1e3)     # us
+            per_op[n].append(hip.elapsed_ms(*e[j]) * 1e3)     # us
+    for e in evs:
+        for a, b in e:
+            hip.destroy(a)
+            hip.destroy(b)
     mean_us = {n: float(np.mean(v)) for n, v in per_op.items()}
     p10_us = {n: float(np.percentile(v, 10)) for n, v in per_op.items()}
     p90_us = {n: float(np.percentile(v, 90)) for n, v in per_op.items()}
@@ -158,7 +197,7 @@ def main():
         "peak": HBM_PEAK_GBPS,
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": traffic_for(dom, w.name, f"{dom}.hip"),
+        "traffic": traffic_for(dom, w.name),
         "algorithmic_bytes_per_launch": ab[dom],
         "avg_launch_us": round(mean_us[dom], 2),
     }

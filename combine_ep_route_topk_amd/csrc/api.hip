@@ -14,9 +14,21 @@
 #include "../../include/ep_route_topk.h"
 #include "ep_internal.h"
 
+namespace ep {
+LaunchTiming& launch_timing() {
+    static thread_local LaunchTiming t;
+    return t;
+}
+}  // namespace ep
+
 namespace {
 
 thread_local char g_err[512] = "";
+
+// Clears the one-shot timing hook when a compute entry point returns.
+struct TimingScope {
+    ~TimingScope() { ep::launch_timing() = ep::LaunchTiming{}; }
+};
 
 ep_status fail(ep_status st, const char* fmt, ...) {
     va_list ap;
@@ -97,10 +109,18 @@ const char* ep_status_string(int status) {
 
 const char* ep_last_error(void) { return g_err; }
 
+ep_status ep_set_timing_events(void* start_event, void* stop_event)
+{
+    ep::launch_timing() = ep::LaunchTiming{static_cast<hipEvent_t>(start_event),
+                                           static_cast<hipEvent_t>(stop_event)};
+    return ok();
+}
+
 ep_status ep_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
                         int32_t normalize, int32_t* topk_idx, float* topk_w, void* stream)
 {
     const char* fn = "ep_route_topk";
+    TimingScope timing_scope;
     EP_TRY(check_routing_sizes(fn, T, k, E));
     EP_REQUIRE_PTR(fn, logits, 4);
     EP_REQUIRE_PTR(fn, topk_idx, 4);
@@ -123,6 +143,7 @@ ep_status ep_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t k, int3
                              void* stream)
 {
     const char* fn = "ep_dispatch_layout";
+    TimingScope timing_scope;
     EP_TRY(check_routing_sizes(fn, T, k, E));
     if (R < 1 || E % R != 0)
         return fail(EP_ERR_INVALID_ARG, "%s: R=%d must be >= 1 and divide E=%d", fn, R, E);
@@ -150,6 +171,7 @@ ep_status ep_dispatch(const uint16_t* x, int32_t T, int32_t H, int32_t k,
                       const int32_t* pos, uint16_t* send, void* stream)
 {
     const char* fn = "ep_dispatch";
+    TimingScope timing_scope;
     EP_TRY(check_rows(fn, T, H, k));
     EP_REQUIRE_PTR(fn, x, 16);
     EP_REQUIRE_PTR(fn, pos, 4);
@@ -163,6 +185,7 @@ ep_status ep_combine(const uint16_t* y, const int32_t* pos, const float* topk_w,
                      int32_t T, int32_t H, int32_t k, uint16_t* out, void* stream)
 {
     const char* fn = "ep_combine";
+    TimingScope timing_scope;
     EP_TRY(check_rows(fn, T, H, k));
     EP_REQUIRE_PTR(fn, y, 16);
     EP_REQUIRE_PTR(fn, pos, 4);
@@ -219,6 +242,7 @@ ep_status ep_fused_dispatch_combine(const uint16_t* x, const int32_t* topk_idx,
                                     uint64_t* epoch_out, uint32_t spin_limit, void* stream)
 {
     const char* fn = "ep_fused_dispatch_combine";
+    TimingScope timing_scope;
     EP_TRY(check_routing_sizes(fn, T, k, E));
     EP_TRY(check_rows(fn, T, H, k));
     if (R < 1 || E % R != 0)

@@ -126,10 +126,10 @@ hipError_t launch_u(const uint16_t* y, const int32_t* pos, const float* w, int T
     const int segs = (nvec + kWave * U - 1) / (kWave * U);
     const dim3 grid((T + kWavesPerBlock - 1) / kWavesPerBlock, segs);
     if (k == 8)
-        hipLaunchKernelGGL((combine_kernel<U, 8>), grid, dim3(kBlock), 0, s,
+        EP_LAUNCH((combine_kernel<U, 8>), grid, dim3(kBlock), 0, s,
                            y, pos, w, T, nvec, k, out);
     else
-        hipLaunchKernelGGL((combine_kernel<U, 0>), grid, dim3(kBlock), 0, s,
+        EP_LAUNCH((combine_kernel<U, 0>), grid, dim3(kBlock), 0, s,
                            y, pos, w, T, nvec, k, out);
     return hipGetLastError();
 }

@@ -84,7 +84,7 @@ hipError_t launch_u(const uint16_t* x, int T, int nvec, int k, const int32_t* po
 {
     const int segs = (nvec + kWave * U - 1) / (kWave * U);
     const dim3 grid((T + kWavesPerBlock - 1) / kWavesPerBlock, segs);
-    hipLaunchKernelGGL((dispatch_kernel<U>), grid, dim3(kBlock), 0, s, x, T, nvec, k, pos,
+    EP_LAUNCH((dispatch_kernel<U>), grid, dim3(kBlock), 0, s, x, T, nvec, k, pos,
                        send);
     return hipGetLastError();
 }

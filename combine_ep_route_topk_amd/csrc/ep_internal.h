@@ -2,16 +2,39 @@
 // shared by the host API (api.hip) and the kernel files of libep_route_topk.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace ep {
 
+// One-shot measurement hook (ep_set_timing_events): when set, the next
+// entry point's first kernel launch records `start` from its own dispatch
+// packet and every launch records `stop`, so the pair brackets exactly the
+// entry point's kernels.  Thread-local; api.hip clears it after each call.
+struct LaunchTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+LaunchTiming& launch_timing();
+
+#define EP_LAUNCH(K, G, B, SHM, S, ...)                                                \
+    do {                                                                               \
+        ::ep::LaunchTiming& ep_t_ = ::ep::launch_timing();                             \
+        if (ep_t_.start || ep_t_.stop) {                                               \
+            hipExtLaunchKernelGGL(K, G, B, SHM, S, ep_t_.start, ep_t_.stop, 0,         \
+                                  __VA_ARGS__);                                        \
+            ep_t_.start = nullptr;                                                     \
+        } else {                                                                       \
+            hipLaunchKernelGGL(K, G, B, SHM, S, __VA_ARGS__);                          \
+        }                                                                              \
+    } while (0)
+
 // ----------------------------------------------------------------- tuning
 constexpr int kBlock = 256;          // threads per workgroup (4 waves of 64)
-constexpr int kTileSlots = 4096;     // slots per layout tile (histogram unit)
-constexpr int kScanItems = 1024;     // (expert, tile) counters per scan block
+constexpr int kTileSlots = 1024;     // slots per layout tile (histogram unit)
+constexpr int kScanItems = 2048;     // (expert, tile) counters per scan block
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 

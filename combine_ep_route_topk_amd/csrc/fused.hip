@@ -441,7 +441,7 @@ int resident_grid(const void* kernel) {
 
 hipError_t launch_fused_init(void* ws, uint64_t first_epoch, hipStream_t s) {
     if (uint32_t(first_epoch) == 0) first_epoch += 1;
-    hipLaunchKernelGGL(fused_init_kernel, dim3(1), dim3(64), 0, s,
+    EP_LAUNCH(fused_init_kernel, dim3(1), dim3(64), 0, s,
                        static_cast<WsHeader*>(ws), first_epoch);
     return hipGetLastError();
 }
@@ -491,9 +491,9 @@ hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float*
     int g = grid > 0 ? grid : resident_grid(kern);
     if (g > items) g = items;
     if (k == 8)
-        hipLaunchKernelGGL((fused_kernel<8>), dim3(g), dim3(kBlock), 0, s, a);
+        EP_LAUNCH((fused_kernel<8>), dim3(g), dim3(kBlock), 0, s, a);
     else
-        hipLaunchKernelGGL((fused_kernel<0>), dim3(g), dim3(kBlock), 0, s, a);
+        EP_LAUNCH((fused_kernel<0>), dim3(g), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 

@@ -175,17 +175,17 @@ hipError_t launch_dispatch_layout(const int32_t* topk_idx, int T, int k, int E, 
     int32_t* base = reinterpret_cast<int32_t*>(w + p.off_base);
     int32_t* rank = reinterpret_cast<int32_t*>(w + p.off_rank);
 
-    hipLaunchKernelGGL(layout_hist_kernel, dim3(p.nTiles), dim3(kBlock), 0, s,
+    EP_LAUNCH(layout_hist_kernel, dim3(p.nTiles), dim3(kBlock), 0, s,
                        topk_idx, p.S, E, p.nTiles, p.nScan, cnt, rank, status, hdr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(layout_scan_kernel, dim3(p.nScan), dim3(kBlock), 0, s,
+    EP_LAUNCH(layout_scan_kernel, dim3(p.nScan), dim3(kBlock), 0, s,
                        cnt, p.nCnt, p.nTiles, E, base, expert_offsets, status, hdr,
                        kDefaultSpinLimit);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int grid = int((p.S + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL(layout_pos_kernel, dim3(grid), dim3(kBlock), 0, s,
+    EP_LAUNCH(layout_pos_kernel, dim3(grid), dim3(kBlock), 0, s,
                        topk_idx, p.S, E, R, p.nTiles, base, rank, expert_counts,
                        expert_offsets, rank_counts, rank_offsets, pos, slot_src, hdr);
     return hipGetLastError();

@@ -5,107 +5,158 @@
 // scores.  Gating is a softmax; selection runs on the raw fp32 logits (the
 // softmax is monotone, so the picks are the same and stay exact).
 //
-// Mapping: a group of LPT lanes (a power of two <= 64) owns one token; lane g
-// of the group holds logits e = i*LPT + g, i < NV, so every load instruction
-// reads LPT consecutive floats (coalesced).  Each of the k rounds takes a
-// local best over the lane's untaken logits and a log2(LPT)-step xor-shuffle
-// reduction on (value, index): larger value first, equal values -> lower
-// index.  Lane j of the group keeps pick j, so the softmax over the picks is
-// one more xor-shuffle sum.  All lanes of a group see bit-identical sums
-// (each butterfly level adds the same two operands, only commuted).
+// Mapping: a group of G lanes (a power of two, G >= k) owns one token; lane g
+// holds logits e = i*G + g for i < nv = ceil(E/G) <= 16, so each load
+// instruction reads G consecutive floats of a row.  A pick is one 64-bit key:
+// the logit's bits made order-preserving as an unsigned integer (with -0.0
+// read as +0.0, since the two compare equal) in the high half and ~e in the
+// low half, so the largest key is the largest logit with the lowest expert
+// id.  Each of the k rounds takes every lane's largest untaken key and a
+// group-wide maximum through DPP row moves (quad permutes, half-row and row
+// mirrors: VALU instructions, no LDS round trip), a 16-lane swizzle for G=32
+// and a lane-0/lane-32 read for G=64.  The owner zeroes the winning key; lane
+// j keeps pick j.  The softmax sum uses the same pattern: every lane adds the
+// same pairs of operands, so all lanes hold bit-identical sums.
 #include "ep_device.h"
 #include "ep_internal.h"
 
 namespace ep {
 namespace {
 
-__device__ __forceinline__ bool ranks_before(float a, int ia, float b, int ib) {
-    return a > b || (a == b && ia < ib);
+constexpr int kMaxNv = 16;
+
+__device__ __forceinline__ uint32_t order_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0;                    // -0.0 ranks as +0.0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_order_bits(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-template <int NV, int LPT>
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+    return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+    return (uint64_t(dpp32<CTRL>(uint32_t(v >> 32))) << 32) | dpp32<CTRL>(uint32_t(v));
+}
+__device__ __forceinline__ uint64_t swap16_64(uint64_t v) {     // lane ^ 16
+    const uint32_t lo = uint32_t(__builtin_amdgcn_ds_swizzle(int(uint32_t(v)), 0x401F));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_ds_swizzle(int(uint32_t(v >> 32)), 0x401F));
+    return (uint64_t(hi) << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+    const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), l));
+    const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), l));
+    return (uint64_t(hi) << 32) | lo;
+}
+
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kHalfMirror = 0x141, kMirror = 0x140;
+
+template <int G>
+__device__ __forceinline__ uint64_t group_max(uint64_t k) {
+    if constexpr (G >= 2) { const uint64_t o = dpp64<kQuadXor1>(k); k = o > k ? o : k; }
+    if constexpr (G >= 4) { const uint64_t o = dpp64<kQuadXor2>(k); k = o > k ? o : k; }
+    if constexpr (G >= 8) { const uint64_t o = dpp64<kHalfMirror>(k); k = o > k ? o : k; }
+    if constexpr (G >= 16) { const uint64_t o = dpp64<kMirror>(k); k = o > k ? o : k; }
+    if constexpr (G >= 32) { const uint64_t o = swap16_64(k); k = o > k ? o : k; }
+    if constexpr (G >= 64) {
+        const uint64_t a = readlane64(k, 0), b = readlane64(k, 32);
+        k = a > b ? a : b;
+    }
+    return k;
+}
+
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+    if constexpr (G >= 2) x += __uint_as_float(dpp32<kQuadXor1>(__float_as_uint(x)));
+    if constexpr (G >= 4) x += __uint_as_float(dpp32<kQuadXor2>(__float_as_uint(x)));
+    if constexpr (G >= 8) x += __uint_as_float(dpp32<kHalfMirror>(__float_as_uint(x)));
+    if constexpr (G >= 16) x += __uint_as_float(dpp32<kMirror>(__float_as_uint(x)));
+    if constexpr (G >= 32)
+        x += __uint_as_float(uint32_t(__builtin_amdgcn_ds_swizzle(int(__float_as_uint(x)), 0x401F)));
+    if constexpr (G >= 64) {
+        const float a = __uint_as_float(uint32_t(__builtin_amdgcn_readlane(int(__float_as_uint(x)), 0)));
+        const float b = __uint_as_float(uint32_t(__builtin_amdgcn_readlane(int(__float_as_uint(x)), 32)));
+        x = a + b;
+    }
+    return x;
+}
+
+template <int G>
 __global__ __launch_bounds__(kBlock) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int normalize,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w)
 {
-    const int g = threadIdx.x % LPT;
-    const int64_t tok = (int64_t(blockIdx.x) * kBlock + threadIdx.x) / LPT;
-    if (tok >= T) return;                   // whole LPT-lane groups leave together
-    const float* row = logits + tok * E;
+    const int g = threadIdx.x % G;
+    const int64_t tok = (int64_t(blockIdx.x) * kBlock + threadIdx.x) / G;
+    // Out-of-range groups keep running (with no row) so that every DPP move
+    // reads an active lane; they just store nothing.
+    const bool live = tok < T;
+    const float* row = logits + (live ? tok : 0) * E;
+    const int nv = (E + G - 1) / G;
 
-    float v[NV];
+    float v[kMaxNv];
+    uint64_t key[kMaxNv];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int e = i * LPT + g;
-        v[i] = e < E ? row[e] : 0.0f;
+    for (int i = 0; i < kMaxNv; ++i) {
+        const int e = i * G + g;
+        const bool ok = live && i < nv && e < E;
+        v[i] = ok ? row[e] : 0.0f;
+        key[i] = ok ? (uint64_t(order_bits(v[i])) << 32) | uint32_t(~uint32_t(e)) : 0;
     }
-    uint32_t avail = 0;                     // bit i: logit i is in range and untaken
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-        if (i * LPT + g < E) avail |= 1u << i;
 
-    int my_pick = 0;
-    float my_val = 0.0f;
+    uint64_t my_key = 0, top_key = 0;
     for (int j = 0; j < k; ++j) {
-        float bv = 0.0f;
-        int bi = -1;
+        uint64_t best = 0;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int e = i * LPT + g;
-            if (((avail >> i) & 1u) && (bi < 0 || ranks_before(v[i], e, bv, bi))) {
-                bv = v[i];
-                bi = e;
-            }
-        }
+        for (int i = 0; i < kMaxNv; ++i) best = key[i] > best ? key[i] : best;
+        best = group_max<G>(best);
 #pragma unroll
-        for (int d = LPT / 2; d >= 1; d >>= 1) {
-            const float ov = __shfl_xor(bv, d, LPT);
-            const int oi = __shfl_xor(bi, d, LPT);
-            if (oi >= 0 && (bi < 0 || ranks_before(ov, oi, bv, bi))) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if (bi % LPT == g) avail &= ~(1u << (bi / LPT));
-        if (g == j) {
-            my_pick = bi;
-            my_val = bv;
-        }
+        for (int i = 0; i < kMaxNv; ++i) key[i] = key[i] == best ? 0 : key[i];
+        if (j == 0) top_key = best;
+        if (g == j) my_key = best;
     }
 
     // The first pick holds the largest logit m: exp(l - m) keeps every
     // softmax ratio and cannot overflow.
-    const float m = __shfl(my_val, 0, LPT);
+    const float m = from_order_bits(uint32_t(top_key >> 32));
+    const float my_val = from_order_bits(uint32_t(my_key >> 32));
+    const int my_pick = int(~uint32_t(my_key));
     const float ex = g < k ? expf(my_val - m) : 0.0f;
     float denom;
     if (normalize) {
-        denom = ex;
-#pragma unroll
-        for (int d = LPT / 2; d >= 1; d >>= 1) denom += __shfl_xor(denom, d, LPT);
+        denom = group_sum<G>(ex);
     } else {
         float z = 0.0f;
 #pragma unroll
-        for (int i = 0; i < NV; ++i)
-            if (i * LPT + g < E) z += expf(v[i] - m);
-#pragma unroll
-        for (int d = LPT / 2; d >= 1; d >>= 1) z += __shfl_xor(z, d, LPT);
-        denom = z;
+        for (int i = 0; i < kMaxNv; ++i)
+            if (i < nv && i * G + g < E) z += expf(v[i] - m);
+        denom = group_sum<G>(z);
     }
-    if (g < k) {
+    if (live && g < k) {
         topk_idx[tok * k + g] = my_pick;
         topk_w[tok * k + g] = ex / denom;
     }
 }
 
-template <int NV, int LPT>
-hipError_t launch_t(const float* logits, int T, int E, int k, int normalize,
+template <int G>
+hipError_t launch_g(const float* logits, int T, int E, int k, int normalize,
                     int32_t* idx, float* w, hipStream_t s)
 {
-    const int64_t threads = int64_t(T) * LPT;
+    const int64_t threads = int64_t(T) * G;
     const int grid = int((threads + kBlock - 1) / kBlock);
-    hipLaunchKernelGGL((route_topk_kernel<NV, LPT>), dim3(grid), dim3(kBlock), 0, s,
-                       logits, T, E, k, normalize, idx, w);
+    EP_LAUNCH((route_topk_kernel<G>), dim3(grid), dim3(kBlock), 0, s,
+              logits, T, E, k, normalize, idx, w);
     return hipGetLastError();
+}
+
+int pow2_at_least(int x) {
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
 }
 
 }  // namespace
@@ -113,17 +164,19 @@ hipError_t launch_t(const float* logits, int T, int E, int k, int normalize,
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int normalize,
                              int32_t* idx, float* w, hipStream_t s)
 {
-    if (E <= 1) return launch_t<1, 1>(logits, T, E, k, normalize, idx, w, s);
-    if (E <= 2) return launch_t<1, 2>(logits, T, E, k, normalize, idx, w, s);
-    if (E <= 4) return launch_t<1, 4>(logits, T, E, k, normalize, idx, w, s);
-    if (E <= 8) return launch_t<1, 8>(logits, T, E, k, normalize, idx, w, s);
-    if (E <= 16) return launch_t<1, 16>(logits, T, E, k, normalize, idx, w, s);
-    if (E <= 32) return launch_t<1, 32>(logits, T, E, k, normalize, idx, w, s);
-    if (E <= 64) return launch_t<1, 64>(logits, T, E, k, normalize, idx, w, s);
-    if (E <= 128) return launch_t<2, 64>(logits, T, E, k, normalize, idx, w, s);
-    if (E <= 256) return launch_t<4, 64>(logits, T, E, k, normalize, idx, w, s);
-    if (E <= 512) return launch_t<8, 64>(logits, T, E, k, normalize, idx, w, s);
-    return launch_t<16, 64>(logits, T, E, k, normalize, idx, w, s);
+    // smallest group that holds the k picks and at most kMaxNv logits per lane
+    int G = pow2_at_least(k);
+    const int need = pow2_at_least((E + kMaxNv - 1) / kMaxNv);
+    if (need > G) G = need;
+    switch (G) {
+        case 1: return launch_g<1>(logits, T, E, k, normalize, idx, w, s);
+        case 2: return launch_g<2>(logits, T, E, k, normalize, idx, w, s);
+        case 4: return launch_g<4>(logits, T, E, k, normalize, idx, w, s);
+        case 8: return launch_g<8>(logits, T, E, k, normalize, idx, w, s);
+        case 16: return launch_g<16>(logits, T, E, k, normalize, idx, w, s);
+        case 32: return launch_g<32>(logits, T, E, k, normalize, idx, w, s);
+        default: return launch_g<64>(logits, T, E, k, normalize, idx, w, s);
+    }
 }
 
 }  // namespace ep

@@ -48,6 +48,7 @@ _SIGS = {
                                    _P, _P, _P, _P, _sz, ctypes.POINTER(ctypes.c_uint64), _u32,
                                    _P], ctypes.c_int),
     "ep_get_device_error": ([_P, _P], ctypes.c_int),
+    "ep_set_timing_events": ([_P, _P], ctypes.c_int),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -257,6 +258,44 @@ def ep_fused_dispatch_combine(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: t
     if want_epoch:
         out["epoch"] = int(ep.value)
     return out
+
+
+def ep_set_timing_events(start_event, stop_event) -> None:
+    """Bracket the next entry point's kernels with two hipEvent_t handles
+    (raw pointers; see HipEvents) -- the kernels' own start and end times."""
+    _check(_lib.ep_set_timing_events(_P(start_event), _P(stop_event)))
+
+
+class HipEvents:
+    """Minimal hipEvent_t helper over the HIP runtime already loaded in the
+    process (created on the current device, with timing)."""
+
+    def __init__(self):
+        self._rt = ctypes.CDLL("libamdhip64.so.7")
+        self._rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _P, _P]
+        self._rt.hipEventDestroy.argtypes = [_P]
+        self._rt.hipEventSynchronize.argtypes = [_P]
+
+    def create(self) -> int:
+        ev = ctypes.c_void_p()
+        rc = self._rt.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev.value
+
+    def elapsed_ms(self, start: int, stop: int) -> float:
+        ms = ctypes.c_float()
+        rc = self._rt.hipEventElapsedTime(ctypes.byref(ms), _P(start), _P(stop))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def synchronize(self, ev: int) -> None:
+        self._rt.hipEventSynchronize(_P(ev))
+
+    def destroy(self, ev: int) -> None:
+        self._rt.hipEventDestroy(_P(ev))
 
 
 def ep_get_device_error(workspace: torch.Tensor, stream=None) -> int:

@@ -19,8 +19,9 @@
  * Conventions shared by every entry point:
  *   - Every pointer argument is a device pointer owned by the caller (e.g. a
  *     torch tensor's data_ptr()).  The library allocates no device memory and
- *     keeps no hidden state between calls; scratch space is the caller's
- *     `workspace`, sized by the matching *_workspace_bytes() query.
+ *     keeps no state between calls other than the one-shot, thread-local
+ *     measurement hook below; scratch space is the caller's `workspace`,
+ *     sized by the matching *_workspace_bytes() query.
  *   - bf16 values travel as uint16_t bit patterns.  Row-major, contiguous.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *   - Arguments are validated synchronously.  On any return other than EP_OK
@@ -63,6 +64,21 @@ const char* ep_status_string(int status);
 /* Detail of the last non-OK status returned on the calling thread (static
  * thread-local storage; valid until the next call on that thread). */
 const char* ep_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Measurement hook.  Operator latency is what the pages measure (UBEP sec. 5;
+ * RailWave's execution protocol times each run with GPU events around the
+ * device work only).  After this call, the NEXT compute entry point called on
+ * the same thread (ep_route_topk, ep_dispatch_layout, ep_dispatch, ep_combine,
+ * ep_fused_dispatch_combine) records `start_event` when its first kernel
+ * starts and `stop_event` when its last kernel ends, taken from the kernels'
+ * own dispatch packets -- the same interval a kernel-trace profiler reports,
+ * with no marker packet in between.  Either event may be NULL.  The hook then
+ * clears itself, also when that call fails validation.  Events are hipEvent_t
+ * handles created by the caller on the current device; the library does not
+ * own them.  Always returns EP_OK.
+ * ------------------------------------------------------------------------- */
+ep_status ep_set_timing_events(void* start_event, void* stop_event);
 
 /* ---------------------------------------------------------------------------
  * Route: top-k gating.  [HPMOE sec. 2.2] the router picks a small subset of
@@ -142,7 +158,12 @@ ep_status ep_combine(const uint16_t* y, const int32_t* pos, const float* topk_w,
 
 /* ---------------------------------------------------------------------------
  * Fused flag-in-payload mode: layout + dispatch + combine with identity
- * experts in ONE persistent launch, no kernel-boundary barrier.  [UBEP sec.
+ * experts in ONE persistent launch, no kernel-boundary barrier.
+ * STATUS: in this build ep_fused_workspace_init and ep_fused_dispatch_combine
+ * validate their arguments and then return EP_ERR_UNSUPPORTED without
+ * launching: the persistent kernel's first launch on an MI355X did not return
+ * and the cause is not yet identified (the same kernel source passes its
+ * checks when run under a host emulation of the device).  [UBEP sec.
  * 3.2] tasks wait on published data instead of global barriers; [UBEP sec.
  * 3.4, Fig. 6] Data-as-Flag: the readiness flag travels inside the data;
  * [UBEP sec. 6, Table 5] without large atomic writes, fences are needed;

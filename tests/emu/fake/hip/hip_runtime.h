@@ -92,6 +92,28 @@ template <class T> inline T __shfl_up(T v, unsigned d, int width = 64) {
 template <class T> inline T emu_readlane(T v, int l) { return emu_shfl_idx(v, l, 64); }
 template <class T> inline T emu_readfirst(T v) { return emu_shfl_idx(v, 0, 64); }
 #define __builtin_amdgcn_readlane(v, l) emu_readlane((v), (l))
+// DPP row moves and the ds_swizzle patterns the kernels use, as shuffles.
+inline int emu_dpp_src(int lane, int ctrl) {
+    if (ctrl <= 0xFF) return (lane & ~3) | ((ctrl >> (2 * (lane & 3))) & 3);   // quad_perm
+    if (ctrl == 0x140) return (lane & ~15) | (15 - (lane & 15));               // row_mirror
+    if (ctrl == 0x141) return (lane & ~7) | (7 - (lane & 7));                  // row_half_mirror
+    std::fprintf(stderr, "[emu] unsupported DPP control %#x\n", ctrl);
+    std::abort();
+}
+inline int emu_update_dpp(int old, int src, int ctrl, int, int, bool) {
+    (void)old;
+    return emu_shfl_idx(src, emu_dpp_src(__lane_id(), ctrl), 64);
+}
+inline int emu_ds_swizzle(int v, int pattern) {
+    if (pattern & 0x8000) { std::fprintf(stderr, "[emu] unsupported swizzle %#x\n", pattern); std::abort(); }
+    const int and_m = pattern & 0x1F, or_m = (pattern >> 5) & 0x1F, xor_m = (pattern >> 10) & 0x1F;
+    const int lane = __lane_id();
+    const int src = (lane & ~31) | ((((lane & 31) & and_m) | or_m) ^ xor_m);
+    return emu_shfl_idx(v, src, 64);
+}
+#define __builtin_amdgcn_update_dpp(o, s, c, r, b, bc) emu_update_dpp((o), (s), (c), (r), (b), (bc))
+#define __builtin_amdgcn_ds_swizzle(v, p) emu_ds_swizzle((v), (p))
+inline unsigned __float_as_uint(float f) { unsigned u; std::memcpy(&u, &f, 4); return u; }
 #define __builtin_amdgcn_readfirstlane(v) emu_readfirst((v))
 inline void __syncthreads() { emu::yield_op(emu::OP_SYNC, 0, 0); }
 #define __builtin_amdgcn_s_sleep(n) emu::yield_op(emu::OP_NONE, 0, 0)
