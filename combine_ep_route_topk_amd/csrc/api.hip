@@ -71,6 +71,8 @@ ep_status check_rows(const char* fn, int32_t T, int32_t H, int32_t k) {
     if (H > (1 << 20)) return fail(EP_ERR_UNSUPPORTED, "%s: H=%d exceeds 2^20", fn, H);
     if (int64_t(T) * k >= (int64_t(1) << 30))
         return fail(EP_ERR_UNSUPPORTED, "%s: T*k=%lld must be < 2^30", fn, (long long)T * k);
+    if (int64_t(T) * H >= (int64_t(1) << 40))
+        return fail(EP_ERR_UNSUPPORTED, "%s: T*H=%lld must be < 2^40", fn, (long long)T * H);
     return EP_OK;
 }
 

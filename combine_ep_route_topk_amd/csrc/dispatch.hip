@@ -55,37 +55,46 @@ __device__ __noinline__ void copy_tail(const char* __restrict__ src, char* __res
     }
 }
 
-// grid.x: groups of 4 tokens (one per wave); grid.y: row segments of
-// kWave*U vectors.
+// Work items are (group of 4 tokens, row segment of kWave*U vectors) pairs,
+// one wave per token, numbered segment-fastest: the workgroups resident at
+// one time cover whole rows, so each destination row is written as one
+// contiguous run (measured on MI355X at T=4096, H=7168, k=8: 1-2 us less
+// than token-fastest order).  A 1-D grid strides over the items, so any T
+// fits the launch limits.
 template <int U>
 __global__ __launch_bounds__(kBlock) void dispatch_kernel(
     const uint16_t* __restrict__ x, int T, int nvec, int k,
-    const int32_t* __restrict__ pos, uint16_t* __restrict__ send)
+    const int32_t* __restrict__ pos, uint16_t* __restrict__ send,
+    uint32_t segs, uint32_t items)
 {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int t = int(blockIdx.x) * kWavesPerBlock + wave;
-    if (t >= T) return;
-    const int seg = int(blockIdx.y);
     const uint32_t S = uint32_t(T) * uint32_t(k);
     const int64_t row_bytes = int64_t(nvec) * 16;
-    const char* src = reinterpret_cast<const char*>(x) + int64_t(t) * row_bytes;
     char* dst = reinterpret_cast<char*>(send);
-    const int32_t* prow = pos + int64_t(t) * k;
-    const int v0 = seg * kWave * U + lane_id();
-    if ((seg + 1) * kWave * U <= nvec)
-        copy_whole<U>(src, dst, row_bytes, prow, k, S, v0);
-    else
-        copy_tail(src, dst, row_bytes, prow, k, S, v0, U, nvec);
+    for (uint32_t b = blockIdx.x; b < items; b += gridDim.x) {
+        const uint32_t group = b / segs;
+        const int seg = int(b - group * segs);
+        const int t = int(group) * kWavesPerBlock + wave;
+        if (t >= T) continue;
+        const char* src = reinterpret_cast<const char*>(x) + int64_t(t) * row_bytes;
+        const int32_t* prow = pos + int64_t(t) * k;
+        const int v0 = seg * kWave * U + lane_id();
+        if ((seg + 1) * kWave * U <= nvec)
+            copy_whole<U>(src, dst, row_bytes, prow, k, S, v0);
+        else
+            copy_tail(src, dst, row_bytes, prow, k, S, v0, U, nvec);
+    }
 }
 
 template <int U>
 hipError_t launch_u(const uint16_t* x, int T, int nvec, int k, const int32_t* pos,
                     uint16_t* send, hipStream_t s)
 {
-    const int segs = (nvec + kWave * U - 1) / (kWave * U);
-    const dim3 grid((T + kWavesPerBlock - 1) / kWavesPerBlock, segs);
-    EP_LAUNCH((dispatch_kernel<U>), grid, dim3(kBlock), 0, s, x, T, nvec, k, pos,
-                       send);
+    const uint32_t segs = uint32_t((nvec + kWave * U - 1) / (kWave * U));
+    const uint32_t items = uint32_t((T + kWavesPerBlock - 1) / kWavesPerBlock) * segs;
+    const uint32_t grid = items < kMaxGrid ? items : kMaxGrid;
+    EP_LAUNCH((dispatch_kernel<U>), dim3(grid), dim3(kBlock), 0, s, x, T, nvec, k, pos,
+              send, segs, items);
     return hipGetLastError();
 }
 

@@ -37,6 +37,8 @@ constexpr int kTileSlots = 1024;     // slots per layout tile (histogram unit)
 constexpr int kScanItems = 2048;     // (expert, tile) counters per scan block
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
+// Cap on the 1-D grid of the row kernels, which stride over their items.
+constexpr uint32_t kMaxGrid = uint32_t(1) << 20;
 
 // Error codes stored in a workspace's error word (host maps them to ep_status).
 enum : uint32_t { kDevOk = 0, kDevBadExpert = 1, kDevTimeout = 2 };

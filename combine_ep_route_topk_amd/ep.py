@@ -260,6 +260,81 @@ def ep_fused_dispatch_combine(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: t
     return out
 
 
+# ------------------------------------------------------------------- bound calls
+class BoundCall:
+    """One entry point with its arguments validated and marshalled once.
+    Calling it repeats the C call only -- for tight loops, where re-checking
+    every tensor would cost more host time than the kernels take.  The
+    tensors it refers to are kept alive by the object."""
+
+    __slots__ = ("_fn", "_args", "_keep")
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, tuple(args), keep
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc != EP_OK:
+            _check(rc)
+
+
+def bind_route_topk(logits, k, normalize, topk_idx, topk_w, stream) -> BoundCall:
+    _need(logits, "logits", torch.float32)
+    T, E = logits.shape
+    _need(topk_idx, "topk_idx", torch.int32, (T, k))
+    _need(topk_w, "topk_w", torch.float32, (T, k))
+    return BoundCall(_lib.ep_route_topk,
+                     (_ptr(logits), T, E, k, int(bool(normalize)), _ptr(topk_idx),
+                      _ptr(topk_w), _P(_stream(stream, logits.device))),
+                     (logits, topk_idx, topk_w, stream))
+
+
+def bind_dispatch_layout(topk_idx, E, R, out, stream) -> BoundCall:
+    _need(topk_idx, "topk_idx", torch.int32)
+    T, k = topk_idx.shape
+    ws = out["workspace"]
+    _need(ws, "workspace", torch.uint8)
+    for name, shape in (("expert_counts", (E,)), ("expert_offsets", (E + 1,)),
+                        ("rank_counts", (R,)), ("rank_offsets", (R + 1,)), ("pos", (T, k))):
+        _need(out[name], name, torch.int32, shape)
+    if out.get("slot_src") is not None:
+        _need(out["slot_src"], "slot_src", torch.int32, (T * k,))
+    return BoundCall(_lib.ep_dispatch_layout,
+                     (_ptr(topk_idx), T, k, E, R, _ptr(out["expert_counts"]),
+                      _ptr(out["expert_offsets"]), _ptr(out["rank_counts"]),
+                      _ptr(out["rank_offsets"]), _ptr(out["pos"]), _ptr(out.get("slot_src")),
+                      _ptr(ws), ws.numel(), _P(_stream(stream, topk_idx.device))),
+                     (topk_idx, out, stream))
+
+
+def bind_dispatch(x, pos, send, stream) -> BoundCall:
+    _bits_ok(x, "x")
+    T, H = x.shape
+    _need(pos, "pos", torch.int32)
+    k = pos.shape[1]
+    if pos.shape[0] != T:
+        raise ValueError("pos must be [T][k]")
+    _bits_ok(send, "send", (T * k, H))
+    return BoundCall(_lib.ep_dispatch,
+                     (_ptr(x), T, H, k, _ptr(pos), _ptr(send), _P(_stream(stream, x.device))),
+                     (x, pos, send, stream))
+
+
+def bind_combine(y, pos, topk_w, out, stream) -> BoundCall:
+    _need(pos, "pos", torch.int32)
+    T, k = pos.shape
+    _bits_ok(y, "y")
+    H = y.shape[1]
+    if y.shape[0] != T * k:
+        raise ValueError("y must have T*k rows")
+    _need(topk_w, "topk_w", torch.float32, (T, k))
+    _bits_ok(out, "out", (T, H))
+    return BoundCall(_lib.ep_combine,
+                     (_ptr(y), _ptr(pos), _ptr(topk_w), T, H, k, _ptr(out),
+                      _P(_stream(stream, y.device))),
+                     (y, pos, topk_w, out, stream))
+
+
 def ep_set_timing_events(start_event, stop_event) -> None:
     """Bracket the next entry point's kernels with two hipEvent_t handles
     (raw pointers; see HipEvents) -- the kernels' own start and end times."""

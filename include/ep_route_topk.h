@@ -28,8 +28,9 @@
  *     nothing was enqueued and ep_last_error() describes the problem.  On
  *     EP_OK the work is enqueued on `stream` and runs asynchronously.
  *   - Sizes: T >= 1, 1 <= k <= min(E, 64), E <= 1024, R >= 1, E % R == 0,
- *     T*k < 2^30.  Rows: H >= 8, H % 8 == 0 (16-byte vectors); bf16 buffers
- *     16-byte aligned, int32/float buffers 4-byte aligned.
+ *     T*k < 2^30.  Rows: 8 <= H <= 2^20, H % 8 == 0 (16-byte vectors),
+ *     T*H < 2^40; bf16 buffers 16-byte aligned, int32/float buffers 4-byte
+ *     aligned.
  *   - Calls on different streams are independent as long as they do not share
  *     an output buffer or a workspace.
  */

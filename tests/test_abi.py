@@ -115,6 +115,11 @@ def test_dispatch_combine_validation(ep):
     assert rc == ep.EP_ERR_INVALID_ARG
     rc, _ = call(lib, "ep_combine", f, f, f, 16, 16, 2, P(FAKE + 4), None)
     assert rc == ep.EP_ERR_INVALID_ARG            # out not 16-byte aligned
+    # T*H >= 2^40 elements is refused before anything is launched
+    rc, msg = call(lib, "ep_dispatch", f, 1 << 21, 1 << 19, 1, f, f, None)
+    assert rc == ep.EP_ERR_UNSUPPORTED and "T*H" in msg
+    rc, msg = call(lib, "ep_combine", f, f, f, 1 << 21, 1 << 19, 1, f, None)
+    assert rc == ep.EP_ERR_UNSUPPORTED and "T*H" in msg
 
 
 def test_fused_validation(ep):
