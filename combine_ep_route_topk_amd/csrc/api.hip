@@ -217,11 +217,6 @@ ep_status ep_fused_workspace_init(void* workspace, size_t workspace_bytes, void*
     if (workspace_bytes < sizeof(ep::WsHeader))
         return fail(EP_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs at least %zu", fn,
                     workspace_bytes, sizeof(ep::WsHeader));
-#ifndef EP_ENABLE_FUSED_LAUNCH
-    (void)stream;
-    return fail(EP_ERR_UNSUPPORTED,
-                "%s: the fused persistent mode is switched off on the GPU in this build", fn);
-#else
     // The first epoch is unpredictable across workspaces and processes, so a
     // trailer left in a reused send buffer by another workspace's call can
     // never be mistaken for one of this workspace's.
@@ -232,7 +227,6 @@ ep_status ep_fused_workspace_init(void* workspace, size_t workspace_bytes, void*
                  (counter.fetch_add(1) * 0x9E3779B97F4A7C15ull);
     if (e == 0) e = 1;
     return launched(ep::launch_fused_init(workspace, e, static_cast<hipStream_t>(stream)), fn);
-#endif
 }
 
 ep_status ep_fused_dispatch_combine(const uint16_t* x, const int32_t* topk_idx,
@@ -265,17 +259,6 @@ ep_status ep_fused_dispatch_combine(const uint16_t* x, const int32_t* topk_idx,
         return fail(EP_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn,
                     workspace_bytes, need);
     hipStream_t s = static_cast<hipStream_t>(stream);
-#ifndef EP_ENABLE_FUSED_LAUNCH
-    // The persistent fused kernel is complete and passes its checks when the
-    // same source is run on a host emulation of the device, but its first
-    // launch on an MI355X did not return (no fault was reported) and the
-    // cause has not been identified, so the GPU launch stays switched off.
-    (void)s;
-    (void)epoch_out;
-    (void)spin_limit;
-    return fail(EP_ERR_UNSUPPORTED,
-                "%s: the fused persistent launch is switched off on the GPU in this build", fn);
-#else
     if (epoch_out) {
         // The epoch this call will write is the one the workspace holds once
         // the work queued before it has finished.
@@ -293,7 +276,6 @@ ep_status ep_fused_dispatch_combine(const uint16_t* x, const int32_t* topk_idx,
                                      expert_offsets, rank_counts, rank_offsets, pos, send_rows,
                                      out, workspace, spin_limit, 0, s),
                     fn);
-#endif
 }
 
 ep_status ep_get_device_error(const void* workspace, void* stream)

@@ -47,22 +47,32 @@ enum : uint32_t { kDevOk = 0, kDevBadExpert = 1, kDevTimeout = 2 };
 constexpr uint32_t kLayoutMagic = 0x45504C57u;   // "EPLW"
 constexpr uint32_t kFusedMagic = 0x45504657u;    // "EPFW"
 
-// Common 256-byte header at the start of every workspace.
+// One 32-bit word alone in a 128-byte line.  The counters that many
+// workgroups poll or update at once each get their own line: a line that
+// every waiting wave re-reads serialises all requests to it, and an atomic on
+// a word sharing that line queues behind them.
+struct alignas(128) LineWord {
+    uint32_t v;
+    uint32_t pad[31];
+};
+
+// Common 1 KiB header at the start of every workspace.
 struct WsHeader {
+    // line 0: written once per call, read by the host
     uint32_t magic;
     uint32_t error;         // result of the last call (kDev*)
-    uint32_t scan_ticket;   // decoupled-lookback block ticket
-    uint32_t timeout;       // set by any expired bounded wait
-    // fused mode only
-    uint32_t work_ticket;   // next work item to claim
-    uint32_t hist_done;     // histogram tiles finished
-    uint32_t exit_count;    // workgroups that left the persistent loop
-    uint32_t pad0;
-    uint64_t epoch;         // epoch of the NEXT fused call
-    uint64_t last_epoch;    // epoch of the last fused call
-    uint32_t reserved[52];
+    uint64_t epoch;         // fused mode: epoch of the NEXT call
+    uint64_t last_epoch;    // fused mode: epoch of the last call
+    uint32_t pad0[26];
+    LineWord scan_ticket;   // decoupled-lookback block ticket
+    LineWord timeout;       // set by any expired bounded wait
+    LineWord work_ticket;   // fused mode: next work item to claim
+    LineWord hist_done;     // fused mode: histogram tiles finished
+    LineWord exit_count;    // fused mode: workgroups that left the loop
+    LineWord reserved[2];
 };
-static_assert(sizeof(WsHeader) == 256, "header is one 256-byte block");
+static_assert(sizeof(WsHeader) == 1024, "header is eight 128-byte lines");
+static_assert(offsetof(WsHeader, error) == 4, "the host reads magic and error as two words");
 
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

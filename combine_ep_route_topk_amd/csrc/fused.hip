@@ -78,13 +78,17 @@ struct FusedArgs {
     uint32_t spin_limit;
 };
 
-// Bounded wait helper state: returns false once the call has timed out.
+// Bounded wait helper state: returns false once this wait has used up its
+// polling rounds (it then raises the call's timeout word) or once another
+// wait has raised it.  The shared word is read only every 64th round: all
+// waiting waves reading one line on every round would serialise behind it.
 struct Waiter {
     uint32_t spins = 0;
     __device__ bool tick(WsHeader* hdr, uint32_t limit) {
-        if (ld_relaxed(&hdr->timeout) != 0) return false;
-        if (++spins > limit) {
-            st_relaxed(&hdr->timeout, 1u);
+        ++spins;
+        if ((spins & 63) == 0 && ld_relaxed(&hdr->timeout.v) != 0) return false;
+        if (spins > limit) {
+            st_relaxed(&hdr->timeout.v, 1u);
             return false;
         }
         backoff();
@@ -101,7 +105,7 @@ __device__ void do_hist(const FusedArgs& a, int tile, int32_t (*hist)[kMaxE]) {
     hist_tile(a.idx, a.S, a.E, a.nTiles, tile, a.cnt, a.local_rank, hist);
     fence_release();                       // this wave's cnt / local_rank writes
     __syncthreads();
-    if (threadIdx.x == 0) fetch_add(&a.hdr->hist_done, 1u);
+    if (threadIdx.x == 0) fetch_add(&a.hdr->hist_done.v, 1u);
 }
 
 // ---------------------------------------------------------------- scan item
@@ -114,13 +118,13 @@ __device__ void do_scan(const FusedArgs& a, int blk, uint32_t ep32, int* sh_wave
     if (tid == 0) {
         Waiter wt;
         bool ok = true;
-        while (ld_relaxed(&a.hdr->hist_done) < uint32_t(a.nTiles))
+        while (ld_relaxed(&a.hdr->hist_done.v) < uint32_t(a.nTiles))
             if (!(ok = wt.tick(a.hdr, a.spin_limit))) break;
         sh_word[0] = ok;
     }
     __syncthreads();
     fence_acquire();
-    if (!sh_word[0]) return;
+    if (!__builtin_amdgcn_readfirstlane(sh_word[0])) return;
 
     const BlockScan bs = block_scan(a.cnt, a.nCnt, blk, sh_wave_total);
     const uint64_t tag = uint64_t(ep32) << 32;
@@ -363,11 +367,17 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs a) {
     const int first_combine = first_scatter + a.nItems;
     const int total = first_combine + a.nItems;
 
+    // The barrier opens each round, BEFORE thread 0 claims the ticket: a
+    // divergent thread-0 block must never follow another one (the end of a
+    // hist item) with no barrier in between, or the compiler may merge the
+    // two and build an inner loop that only lane 0 leaves -- the other 255
+    // threads would then cycle on a stale ticket forever.  The ticket is made
+    // wave-uniform so every branch on it is a scalar branch.
     while (true) {
-        if (tid == 0) sh_ticket = int(fetch_add(&a.hdr->work_ticket, 1u));
+        __syncthreads();                  // everyone has read the last ticket
+        if (tid == 0) sh_ticket = int(fetch_add(&a.hdr->work_ticket.v, 1u));
         __syncthreads();
-        const int ticket = sh_ticket;
-        __syncthreads();
+        const int ticket = __builtin_amdgcn_readfirstlane(sh_ticket);
         if (ticket >= total) break;
         if (ticket < first_scan) do_hist(a, ticket, hist);
         else if (ticket < first_scatter) do_scan(a, ticket - first_scan, uint32_t(epoch), sh_wave_total, sh_word);
@@ -378,9 +388,9 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs a) {
     // Leave: the last workgroup out finishes the outputs and resets the state.
     fence_release();
     __syncthreads();
-    if (tid == 0) sh_word[0] = fetch_add_acq_rel(&a.hdr->exit_count, 1u) == gridDim.x - 1;
+    if (tid == 0) sh_word[0] = fetch_add_acq_rel(&a.hdr->exit_count.v, 1u) == gridDim.x - 1;
     __syncthreads();
-    if (!sh_word[0]) return;
+    if (!__builtin_amdgcn_readfirstlane(sh_word[0])) return;
     fence_acquire();
     const int L = a.E / a.R;
     for (int e = tid; e < a.E; e += kBlock)
@@ -392,13 +402,13 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs a) {
     if (tid == 0) {
         WsHeader* h = a.hdr;
         uint32_t err = kDevOk;
-        if (h->timeout) err = kDevTimeout;
+        if (h->timeout.v) err = kDevTimeout;
         else if (a.expert_offsets[a.E] != a.S) err = kDevBadExpert;
         h->error = err;
-        h->timeout = 0;
-        h->work_ticket = 0;
-        h->hist_done = 0;
-        h->exit_count = 0;
+        h->timeout.v = 0;
+        h->work_ticket.v = 0;
+        h->hist_done.v = 0;
+        h->exit_count.v = 0;
         h->last_epoch = epoch;
         uint64_t next = epoch + 1;
         if (uint32_t(next) == 0) next += 1;       // the 32-bit tag is never 0
@@ -410,11 +420,11 @@ __global__ void fused_init_kernel(WsHeader* hdr, uint64_t first_epoch) {
     if (threadIdx.x == 0) {
         hdr->magic = kFusedMagic;
         hdr->error = kDevOk;
-        hdr->scan_ticket = 0;
-        hdr->timeout = 0;
-        hdr->work_ticket = 0;
-        hdr->hist_done = 0;
-        hdr->exit_count = 0;
+        hdr->scan_ticket.v = 0;
+        hdr->timeout.v = 0;
+        hdr->work_ticket.v = 0;
+        hdr->hist_done.v = 0;
+        hdr->exit_count.v = 0;
         hdr->epoch = first_epoch;
         hdr->last_epoch = 0;
     }

@@ -49,8 +49,8 @@ __global__ __launch_bounds__(kBlock) void layout_hist_kernel(
     if (blockIdx.x == 0) {
         for (int i = threadIdx.x; i < nScan; i += kBlock) status[i] = 0;
         if (threadIdx.x == 0) {
-            hdr->scan_ticket = 0;
-            hdr->timeout = 0;
+            hdr->scan_ticket.v = 0;
+            hdr->timeout.v = 0;
         }
     }
     hist_tile(topk_idx, S, E, nTiles, blockIdx.x, cnt, local_rank, hist);
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kBlock) void layout_scan_kernel(
 
     // Ticket order = order in which blocks started, so every predecessor a
     // block waits for is already running (forward progress).
-    if (tid == 0) sh_block = int(fetch_add(&hdr->scan_ticket, 1u));
+    if (tid == 0) sh_block = int(fetch_add(&hdr->scan_ticket.v, 1u));
     __syncthreads();
     const int blk = sh_block;
     const BlockScan bs = block_scan(cnt, nCnt, blk, sh_wave_total);
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kBlock) void layout_scan_kernel(
                 const uint32_t st = j >= 0 ? ld_relaxed(&status[j]) : kFlagInclusive;
                 if (ballot((st >> 30) == 0) != 0) {       // a predecessor not published yet
                     if (++spins > spin_limit) {
-                        if (lane == 0) st_relaxed(&hdr->timeout, 1u);
+                        if (lane == 0) st_relaxed(&hdr->timeout.v, 1u);
                         break;
                     }
                     backoff();
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(kBlock) void layout_pos_kernel(
         }
         if (threadIdx.x == 0) {
             uint32_t err = kDevOk;
-            if (hdr->timeout) err = kDevTimeout;
+            if (hdr->timeout.v) err = kDevTimeout;
             else if (expert_offsets[E] != S) err = kDevBadExpert;
             hdr->error = err;
             hdr->magic = kLayoutMagic;

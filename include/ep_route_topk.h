@@ -159,12 +159,7 @@ ep_status ep_combine(const uint16_t* y, const int32_t* pos, const float* topk_w,
 
 /* ---------------------------------------------------------------------------
  * Fused flag-in-payload mode: layout + dispatch + combine with identity
- * experts in ONE persistent launch, no kernel-boundary barrier.
- * STATUS: in this build ep_fused_workspace_init and ep_fused_dispatch_combine
- * validate their arguments and then return EP_ERR_UNSUPPORTED without
- * launching: the persistent kernel's first launch on an MI355X did not return
- * and the cause is not yet identified (the same kernel source passes its
- * checks when run under a host emulation of the device).  [UBEP sec.
+ * experts in ONE persistent launch, no kernel-boundary barrier.  [UBEP sec.
  * 3.2] tasks wait on published data instead of global barriers; [UBEP sec.
  * 3.4, Fig. 6] Data-as-Flag: the readiness flag travels inside the data;
  * [UBEP sec. 6, Table 5] without large atomic writes, fences are needed;

@@ -31,7 +31,7 @@ def build(extra=()):
     if cxx is None:
         raise RuntimeError("clang++ not found")
     os.makedirs(OUT, exist_ok=True)
-    flags = ["-std=c++17", "-O1", "-g", "-fPIC", "-DEP_ENABLE_FUSED_LAUNCH",
+    flags = ["-std=c++17", "-O1", "-g", "-fPIC",
              "-I", os.path.join(HERE, "fake"), "-I", os.path.join(ROOT, "include"), *extra]
     jobs = [(os.path.join(CSRC, f), os.path.join(OUT, f + ".o"), True)
             for f in sorted(os.listdir(CSRC)) if f.endswith(".hip")]

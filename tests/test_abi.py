@@ -46,10 +46,10 @@ def test_status_strings(ep):
 
 def test_workspace_and_stride_queries(ep):
     lib = ep.library()
-    # one 256 B header, then 256 B-aligned arrays; a bigger problem needs more
+    # one 1 KiB header, then 256 B-aligned arrays; a bigger problem needs more
     small = lib.ep_dispatch_layout_workspace_bytes(128, 2, 8, 2)
     big = lib.ep_dispatch_layout_workspace_bytes(16384, 8, 256, 64)
-    assert small >= 256 and small % 256 == 0 and big > small
+    assert small >= 1024 and small % 256 == 0 and big > small
     assert big >= 4 * 16384 * 8          # holds one rank word per slot
     assert lib.ep_dispatch_layout_workspace_bytes(0, 2, 8, 2) == 0
     assert lib.ep_fused_workspace_bytes(16384, 8, 256, 64) > big

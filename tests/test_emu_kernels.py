@@ -1,13 +1,15 @@
 """The library's kernel sources run on the CPU under a host emulation of the
 HIP device API (tests/emu), checked against the CPU oracle.
 
-This covers the fused flag-in-payload mode, whose GPU launch is switched off
-in the product build, with the same source the GPU would run: the persistent
-ticket loop, the epoch-tagged look-back and base words, the per-row trailers,
-the bounded waits, and the last-workgroup reset of the workspace -- with only
-a handful of workgroups resident at a time, which exercises the forward-progress
-argument (an item only waits for smaller tickets).  The unfused kernels run
-too, as a check of the emulation itself against the results the GPU gives.
+This covers the fused flag-in-payload mode with the same source the GPU runs:
+the persistent ticket loop, the epoch-tagged look-back and base words, the
+per-row trailers, the bounded waits, and the last-workgroup reset of the
+workspace -- with only a handful of workgroups resident at a time, which
+exercises the forward-progress argument (an item only waits for smaller
+tickets).  Each lane is one thread of the source program here, so these tests
+check the program's logic, not how the compiler maps divergent control flow
+onto a wave.  The unfused kernels run too, as a check of the emulation itself
+against the results the GPU gives.
 """
 import ctypes
 import os

@@ -11,12 +11,7 @@ from combine_ep_route_topk_amd import workloads as wl
 
 from gpu_util import DEV, Case, bits, say, to_dev_bits
 
-pytestmark = [
-    pytest.mark.gpu,
-    pytest.mark.skip(reason="the fused persistent launch is switched off on the GPU: its first "
-                            "MI355X launch did not return and the cause is not identified; the "
-                            "same kernel source is checked on the CPU by tests/test_emu_kernels.py"),
-]
+pytestmark = pytest.mark.gpu
 
 LAYOUT_KEYS = ("expert_counts", "expert_offsets", "rank_counts", "rank_offsets", "pos")
 
