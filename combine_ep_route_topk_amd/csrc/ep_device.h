@@ -45,6 +45,31 @@ __device__ __forceinline__ u32x4 load16_nt(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
+// ---------------------------------------------------------------- coherent stores
+// A buffer descriptor over `bytes` bytes at `base` (raw, unstrided): buffer
+// accesses through it are bounds-checked by the hardware against `bytes`.
+constexpr uint32_t kRawBufferWord3 = 0x00020000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, int(bytes), kRawBufferWord3);
+}
+// 16-byte store with the agent-scope coherence bit (sc1) and the streaming
+// hint (nt): it is written through this XCD's L2 instead of staying dirty
+// there, so once it has completed it is visible to agent-scope loads on
+// every XCD -- the same guarantee an agent-scope atomic store (also sc1)
+// has.  `off` is a byte offset inside the descriptor's range.
+constexpr int kCpolNtSc1 = 2 | 16;
+__device__ __forceinline__ void store16_coherent(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolNtSc1);
+}
+// Wait until every store this wave issued has completed (s_waitcnt vmcnt(0)
+// on gfx9-family ISAs, where stores count in vmcnt); the compiler may move
+// no memory access across it.
+__device__ __forceinline__ void wait_own_stores() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---------------------------------------------------------------- wave64
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 __device__ __forceinline__ uint64_t lanes_below() {

@@ -35,6 +35,9 @@ LaunchTiming& launch_timing();
 constexpr int kBlock = 256;          // threads per workgroup (4 waves of 64)
 constexpr int kTileSlots = 1024;     // slots per layout tile (histogram unit)
 constexpr int kScanItems = 2048;     // (expert, tile) counters per scan block
+// Counters per scan item of the persistent fused mode: one item covers the
+// 8192 counters of the dsv3-sized layout, so its look-back chain is empty.
+constexpr int kFusedScanItems = 8192;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 // Cap on the 1-D grid of the row kernels, which stride over their items.
@@ -68,8 +71,7 @@ struct WsHeader {
     LineWord timeout;       // set by any expired bounded wait
     LineWord work_ticket;   // fused mode: next work item to claim
     LineWord hist_done;     // fused mode: histogram tiles finished
-    LineWord exit_count;    // fused mode: workgroups that left the loop
-    LineWord reserved[2];
+    LineWord reserved[3];
 };
 static_assert(sizeof(WsHeader) == 1024, "header is eight 128-byte lines");
 static_assert(offsetof(WsHeader, error) == 4, "the host reads magic and error as two words");

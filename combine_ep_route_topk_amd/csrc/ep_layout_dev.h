@@ -1,7 +1,7 @@
 // ep_layout_dev.h -- device building blocks of the dispatch layout shared by
 // the three-launch layout (layout.hip) and the persistent fused mode
 // (fused.hip): the per-tile histogram with stable ranks, and a block-wide
-// exclusive scan of kScanItems counters.
+// exclusive scan of ITEMS counters.
 #pragma once
 
 #include "ep_device.h"
@@ -10,10 +10,8 @@
 namespace ep {
 
 constexpr int kWavesPerBlock = kBlock / kWave;                          // 4
-constexpr int kChunksPerWave = kTileSlots / (kWavesPerBlock * kWave);   // 16
+constexpr int kChunksPerWave = kTileSlots / (kWavesPerBlock * kWave);   // 4
 static_assert(kChunksPerWave * kWavesPerBlock * kWave == kTileSlots, "tile split");
-constexpr int kScanPerThread = kScanItems / kBlock;                     // 4
-static_assert(kScanPerThread * kBlock == kScanItems, "scan split");
 
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
@@ -31,7 +29,10 @@ __device__ __forceinline__ int wave_sum(int v) {
 // turn their private counts into per-wave offsets.  Deterministic: no result
 // depends on the order in which atomics land.
 // Writes cnt[e * nTiles + tile] for every e < E and local_rank[s] for every
-// valid slot of the tile.  `hist` is the block's LDS scratch.
+// valid slot of the tile, with agent-coherent stores: once the wave's stores
+// have completed they are visible on every XCD, so a persistent caller can
+// publish "tile done" after a wait for its own stores instead of an L2
+// write-back.  `hist` is the block's LDS scratch.
 __device__ __forceinline__ void hist_tile(const int32_t* __restrict__ topk_idx, int64_t S,
                                           int E, int nTiles, int tile,
                                           int32_t* __restrict__ cnt,
@@ -79,41 +80,60 @@ __device__ __forceinline__ void hist_tile(const int32_t* __restrict__ topk_idx, 
             hist[w][e] = run;
             run += c;
         }
-        cnt[int64_t(e) * nTiles + tile] = run;
+        st_relaxed(reinterpret_cast<uint32_t*>(&cnt[int64_t(e) * nTiles + tile]), uint32_t(run));
     }
     __syncthreads();
 
 #pragma unroll
     for (int c = 0; c < kChunksPerWave; ++c) {
         const int64_t s = wave_first + c * kWave + lane;
-        if (key[c] >= 0) local_rank[s] = hist[wave][key[c]] + rank[c];
+        if (key[c] >= 0)
+            st_relaxed(reinterpret_cast<uint32_t*>(&local_rank[s]),
+                       uint32_t(hist[wave][key[c]] + rank[c]));
     }
 }
 
-// Block-wide scan of the kScanItems counters of scan block `blk`: loads
-// v[q] = cnt[i0 + q] (0 past nCnt), returns this thread's exclusive offset
-// inside the block and the block total.  `sh_wave_total` is LDS scratch.
+// Block-wide scan of the ITEMS counters of scan block `blk`: loads
+// v[q] = cnt[i0 + q] (0 past nCnt) as 16-byte vectors, returns this thread's
+// exclusive offset inside the block and the block total.  `sh_wave_total`
+// is LDS scratch.
+template <int ITEMS>
 struct BlockScan {
-    int v[kScanPerThread];
+    static constexpr int kPer = ITEMS / kBlock;      // counters per thread
+    static_assert(kPer * kBlock == ITEMS && kPer % 4 == 0, "scan split");
+    int v[kPer];
     int i0;
     int thread_excl;
     int total;
 };
 
-__device__ __forceinline__ BlockScan block_scan(const int32_t* __restrict__ cnt, int nCnt,
-                                                int blk, int* sh_wave_total)
+template <int ITEMS>
+__device__ __forceinline__ BlockScan<ITEMS> block_scan(const int32_t* __restrict__ cnt, int nCnt,
+                                                       int blk, int* sh_wave_total)
 {
-    BlockScan r;
+    constexpr int kScanPerThread = BlockScan<ITEMS>::kPer;
+    BlockScan<ITEMS> r;
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = lane_id();
-    r.i0 = blk * kScanItems + tid * kScanPerThread;
+    r.i0 = blk * ITEMS + tid * kScanPerThread;
     int tsum = 0;
 #pragma unroll
-    for (int q = 0; q < kScanPerThread; ++q) {
-        r.v[q] = r.i0 + q < nCnt ? cnt[r.i0 + q] : 0;
-        tsum += r.v[q];
+    for (int m = 0; m < kScanPerThread / 4; ++m) {
+        const int i = r.i0 + 4 * m;
+        if (i + 3 < nCnt) {
+            const int4 x = *reinterpret_cast<const int4*>(cnt + i);
+            r.v[4 * m] = x.x;
+            r.v[4 * m + 1] = x.y;
+            r.v[4 * m + 2] = x.z;
+            r.v[4 * m + 3] = x.w;
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) r.v[4 * m + c] = i + c < nCnt ? cnt[i + c] : 0;
+        }
     }
+#pragma unroll
+    for (int q = 0; q < kScanPerThread; ++q) tsum += r.v[q];
     const int incl = wave_inclusive_sum(tsum);
     if (lane == kWave - 1) sh_wave_total[wave] = incl;
     __syncthreads();

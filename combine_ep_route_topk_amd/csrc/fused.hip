@@ -17,29 +17,43 @@
 // whatever the number of co-resident workgroups:
 //   [hist]    one per tile: tile histogram + stable ranks (shared with the
 //             three-launch layout), then hist_done += 1 (release).
-//   [scan]    one per kScanItems counters: waits for hist_done == nTiles
+//   [scan]    one per kFusedScanItems counters: waits for hist_done == nTiles
 //             (an event counter with a static threshold), block scan, then
 //             decoupled look-back over 64-bit status words that carry the
 //             call's epoch next to flag and value, then publishes every
 //             base as a 64-bit word (epoch << 32 | base): the base value is
 //             its own readiness flag.
-//   [scatter] tokens [8i, 8i+8): polls the base words of its picks, computes
-//             pos, copies each x row into its k send rows (streaming stores),
-//             writes {slot_src, 0} into the rows' trailers, one release fence
-//             per wave, then the 64-bit epoch into every trailer.
-//   [combine] tokens [8i, 8i+8): recomputes pos, polls the k trailers of
-//             each token until they hold this call's epoch, one acquire fence
-//             per wave, then the same fp32 reduction as ep_combine.
+//   [scatter] kScatTok tokens: wave 0 polls the base words of the item's
+//             picks and puts the positions in LDS; two waves per token copy
+//             one half row each into the token's k send rows with
+//             agent-coherent streaming stores; every wave waits for its
+//             stores to complete, and after a barrier wave 0 writes pos and
+//             {slot_src, 0} into the rows' trailers, then the 64-bit epoch.
+//   [combine] kCombTok tokens: wave 0 recomputes the positions, polls the
+//             item's trailers until they hold this call's epoch, issues one
+//             acquire fence; after a barrier each wave reduces one token's k
+//             rows with the same fp32 arithmetic as ep_combine.
 // A row's trailer is its flag: on gfx950 a 64-bit aligned store is
 // single-copy atomic but a 14 KiB row is not, hence payload -> release ->
-// trailer, and trailer -> acquire -> payload on the reading side.  Fences
-// are amortised over a wave's 2 tokens x k rows.
+// trailer, and trailer -> acquire -> payload on the reading side.  An
+// agent-scope release FENCE writes back the whole L2 of the XCD (measured at
+// dsv3: 2048 of them cost ~160 us of a 400 us call), so the scatter side
+// releases the way an agent-scope atomic store does instead: the payload is
+// stored agent-coherent (sc1), each wave waits for its stores to complete,
+// then the flags are stored.  The combine side keeps one acquire fence (an
+// L2 invalidate, cheap) per item.
+//
+// Scatter items are small (2 tokens) and outnumber the resident workgroups
+// at the shapes that matter, so the first ticket of almost every workgroup is
+// layout or scatter work: no workgroup sits on a combine item waiting for
+// rows that nobody is writing yet.
 //
 // Every wait is bounded by spin_limit polling rounds; an expired wait sets
-// the workspace's timeout word and every later wait gives up at once, so the
-// grid always drains.  The last workgroup to leave derives the per-expert /
-// per-rank counts, records the error word and resets the counters and the
-// epoch for the next call (the workspace is reused without a memset).
+// the workspace's timeout word and every later wait gives up soon after, so
+// the grid always drains.  The workgroup whose final ticket claim is the last
+// of all finishes the per-expert / per-rank counts, records the error word
+// and resets the counters and the epoch for the next call (the workspace is
+// reused without a memset).
 #include "ep_combine_dev.h"
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -48,8 +62,14 @@
 namespace ep {
 namespace {
 
-constexpr int kTokPerWave = 2;                               // per scatter/combine item
-constexpr int kTokPerItem = kTokPerWave * kWavesPerBlock;    // 8
+constexpr int kScatTok = 2;                    // tokens per scatter item (2 waves each)
+constexpr int kCombTok = kWavesPerBlock;       // tokens per combine item (1 wave each)
+static_assert(kWavesPerBlock % kCombTok == 0, "whole waves per combine token");
+constexpr int kScatU = 7;                      // 16-byte vectors per lane per row segment
+constexpr int kSegVec = kWave * kScatU;        // vectors per scatter row segment
+constexpr int kMaxItemPicks = kCombTok * kMaxK;
+constexpr int kPickRounds = kMaxItemPicks / kWave;   // lanes cover the picks in <= 4 rounds
+static_assert(kScatTok * 2 == kWavesPerBlock, "two waves per scatter token");
 constexpr uint64_t kStFlagAggregate = uint64_t(1) << 30;
 constexpr uint64_t kStFlagInclusive = uint64_t(2) << 30;
 constexpr uint64_t kStValueMask = (uint64_t(1) << 30) - 1;
@@ -60,7 +80,7 @@ struct FusedArgs {
     const float* w;
     int T, k, E, R, nvec;
     int64_t S;
-    int nTiles, nCnt, nScan, nItems;      // nItems scatter items == combine items
+    int nTiles, nCnt, nScan, nScat, nComb;
     int64_t stride;                       // bytes per send row (payload + trailer + pad)
     int64_t trailer_off;                  // = 2H
     int32_t* expert_counts;
@@ -82,6 +102,9 @@ struct FusedArgs {
 // polling rounds (it then raises the call's timeout word) or once another
 // wait has raised it.  The shared word is read only every 64th round: all
 // waiting waves reading one line on every round would serialise behind it.
+// The pause between rounds grows (about 0.05, 0.4, then 1.7 us): a wait that
+// lasts is for work still well ahead, and the polls of many waiting waves
+// would otherwise take memory bandwidth from the work they wait for.
 struct Waiter {
     uint32_t spins = 0;
     __device__ bool tick(WsHeader* hdr, uint32_t limit) {
@@ -89,9 +112,12 @@ struct Waiter {
         if ((spins & 63) == 0 && ld_relaxed(&hdr->timeout.v) != 0) return false;
         if (spins > limit) {
             st_relaxed(&hdr->timeout.v, 1u);
+            fence_release();
             return false;
         }
-        backoff();
+        if (spins < 16) __builtin_amdgcn_s_sleep(2);
+        else if (spins < 256) __builtin_amdgcn_s_sleep(16);
+        else __builtin_amdgcn_s_sleep(64);
         return true;
     }
 };
@@ -103,7 +129,9 @@ __device__ __forceinline__ bool published(uint64_t word, uint32_t ep32) {
 // ---------------------------------------------------------------- hist item
 __device__ void do_hist(const FusedArgs& a, int tile, int32_t (*hist)[kMaxE]) {
     hist_tile(a.idx, a.S, a.E, a.nTiles, tile, a.cnt, a.local_rank, hist);
-    fence_release();                       // this wave's cnt / local_rank writes
+    // cnt / local_rank are agent-coherent stores: once every wave has seen
+    // its own complete, the tile is visible on every XCD and can be counted.
+    wait_own_stores();
     __syncthreads();
     if (threadIdx.x == 0) fetch_add(&a.hdr->hist_done.v, 1u);
 }
@@ -126,7 +154,8 @@ __device__ void do_scan(const FusedArgs& a, int blk, uint32_t ep32, int* sh_wave
     fence_acquire();
     if (!__builtin_amdgcn_readfirstlane(sh_word[0])) return;
 
-    const BlockScan bs = block_scan(a.cnt, a.nCnt, blk, sh_wave_total);
+    const BlockScan<kFusedScanItems> bs =
+        block_scan<kFusedScanItems>(a.cnt, a.nCnt, blk, sh_wave_total);
     const uint64_t tag = uint64_t(ep32) << 32;
     if (wave == 0) {
         int exclusive = 0;
@@ -162,43 +191,70 @@ __device__ void do_scan(const FusedArgs& a, int blk, uint32_t ep32, int* sh_wave
     }
     __syncthreads();
 
+    // The ranks a reader of these bases will use were stored agent-coherent
+    // and completed before hist_done counted their tile, so publishing needs
+    // no write-back first.
     int run = sh_word[1] + bs.thread_excl;
-    fence_release();                       // local_rank (acquired above) before the bases
 #pragma unroll
-    for (int q = 0; q < kScanPerThread; ++q) {
+    for (int q = 0; q < BlockScan<kFusedScanItems>::kPer; ++q) {
         const int i = bs.i0 + q;
         if (i < a.nCnt) {
-            if (i % a.nTiles == 0) a.expert_offsets[i / a.nTiles] = run;
+            if (i % a.nTiles == 0)
+                st_relaxed(reinterpret_cast<uint32_t*>(&a.expert_offsets[i / a.nTiles]),
+                           uint32_t(run));
             st_relaxed64(&a.fbase[i], tag | uint32_t(run));
             run += bs.v[q];
-            if (i == a.nCnt - 1) a.expert_offsets[a.E] = run;
+            if (i == a.nCnt - 1)
+                st_relaxed(reinterpret_cast<uint32_t*>(&a.expert_offsets[a.E]), uint32_t(run));
         }
     }
+    // expert_offsets (agent-coherent) complete before this workgroup's next
+    // ticket claim: the workgroup that makes the last claim of all reads them
+    // after an acquire.
+    wait_own_stores();
 }
 
-// Positions of the picks of this wave's tokens: lane j < k of token slot i
-// gets p[i] (or -1).  Polls the published bases; false on timeout.
-__device__ __forceinline__ bool wave_positions(const FusedArgs& a, int t_first, uint32_t ep32,
-                                               int (&p)[kTokPerWave], int64_t (&s)[kTokPerWave])
+// Positions of the picks of tokens [t0, t0 + ntok), run by ONE wave: pick
+// q = i*k + j (slot s = t0*k + q) is handled by lane q % 64 in round q / 64.
+// Polls the published base words, then p = base + local rank (or -1 for an id
+// outside [0, E) or a token past T).  Writes sh_pos[q] and returns the
+// positions in p[round]; false on timeout.
+__device__ bool item_positions(const FusedArgs& a, int t0, int ntok, uint32_t ep32,
+                               int* sh_pos, int (&p)[kPickRounds])
 {
     const int lane = lane_id();
-    uint64_t word[kTokPerWave];
-    int e[kTokPerWave];
+    const int npick = ntok * a.k;
+    const int64_t s0 = int64_t(t0) * a.k;
+    int e[kPickRounds];
+    uint64_t word[kPickRounds];
 #pragma unroll
-    for (int i = 0; i < kTokPerWave; ++i) {
-        const int t = t_first + i;
-        s[i] = int64_t(t) * a.k + lane;
-        e[i] = (lane < a.k && t < a.T) ? a.idx[s[i]] : -1;
-        word[i] = 0;
+    for (int r = 0; r < kPickRounds; ++r) {
+        const int q = r * kWave + lane;
+        const int64_t s = s0 + q;
+        e[r] = (q < npick && s < a.S) ? a.idx[s] : -1;
+        word[r] = 0;
+    }
+    // One word first: every lane reads the base word of pick 0, so a wave
+    // sends one request per polling round instead of one per pick (thousands
+    // of waves wait here while the layout runs, and their polls would slow
+    // it).  The scan publishes all bases within a short window, so the full
+    // poll below rarely needs a second round.
+    const int e0 = __builtin_amdgcn_readfirstlane(e[0]);
+    if (unsigned(e0) < unsigned(a.E)) {
+        const uint64_t* w0 = &a.fbase[int64_t(e0) * a.nTiles + s0 / kTileSlots];
+        Waiter wt0;
+        while (!published(ld_relaxed64(w0), ep32))
+            if (!wt0.tick(a.hdr, a.spin_limit)) return false;
     }
     Waiter wt;
     while (true) {
         bool ready = true;
 #pragma unroll
-        for (int i = 0; i < kTokPerWave; ++i) {
-            if (unsigned(e[i]) < unsigned(a.E) && !published(word[i], ep32)) {
-                word[i] = ld_relaxed64(&a.fbase[int64_t(e[i]) * a.nTiles + s[i] / kTileSlots]);
-                ready = ready && published(word[i], ep32);
+        for (int r = 0; r < kPickRounds; ++r) {
+            const int64_t s = s0 + r * kWave + lane;
+            if (unsigned(e[r]) < unsigned(a.E) && !published(word[r], ep32)) {
+                word[r] = ld_relaxed64(&a.fbase[int64_t(e[r]) * a.nTiles + s / kTileSlots]);
+                ready = ready && published(word[r], ep32);
             }
         }
         if (ballot(!ready) == 0) break;
@@ -206,150 +262,236 @@ __device__ __forceinline__ bool wave_positions(const FusedArgs& a, int t_first, 
     }
     fence_acquire();                       // the ranks written by the hist items
 #pragma unroll
-    for (int i = 0; i < kTokPerWave; ++i) {
-        p[i] = unsigned(e[i]) < unsigned(a.E) ? int(uint32_t(word[i])) + a.local_rank[s[i]] : -1;
-        if (uint64_t(uint32_t(p[i])) >= uint64_t(a.S)) p[i] = -1;   // never address outside the rows
+    for (int r = 0; r < kPickRounds; ++r) {
+        const int q = r * kWave + lane;
+        const int64_t s = s0 + q;
+        int pr = -1;
+        if (unsigned(e[r]) < unsigned(a.E)) {
+            pr = int(uint32_t(word[r])) + a.local_rank[s];
+            if (uint64_t(uint32_t(pr)) >= uint64_t(a.S)) pr = -1;   // never address outside the rows
+        }
+        p[r] = pr;
+        if (q < npick) sh_pos[q] = pr;
     }
     return true;
 }
 
-// ---------------------------------------------------------------- scatter item
-__device__ void do_scatter(const FusedArgs& a, int item, uint64_t epoch) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int lane = lane_id();
-    const int t_first = item * kTokPerItem + wave * kTokPerWave;
-    if (t_first >= a.T) return;
-    int p[kTokPerWave];
-    int64_t s[kTokPerWave];
-    if (!wave_positions(a, t_first, uint32_t(epoch), p, s)) return;
+__device__ __forceinline__ uint64_t* trailer(const FusedArgs& a, int p) {
+    return reinterpret_cast<uint64_t*>(a.send_rows + int64_t(p) * a.stride + a.trailer_off);
+}
 
-    for (int i = 0; i < kTokPerWave; ++i) {
-        const int t = t_first + i;
-        if (t >= a.T) break;
-        if (lane < a.k) a.pos[s[i]] = p[i];
-        const char* src = reinterpret_cast<const char*>(a.x) + int64_t(t) * a.nvec * 16;
-        // payload: 8 vectors per lane per round, then k streaming stores each
-        for (int c0 = 0; c0 < a.nvec; c0 += kWave * 8) {
-            u32x4 v[8];
+// ---------------------------------------------------------------- scatter item
+// One row segment of kSegVec vectors that lies inside the row: kScatU loads
+// per lane, then kScatU streaming stores per valid pick.
+__device__ __forceinline__ void scatter_whole(const char* __restrict__ src, const FusedArgs& a,
+                                              const int* prow, uint32_t lane_off)
+{
+    u32x4 v[kScatU];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int vi = c0 + u * kWave + lane;
-                if (vi < a.nvec) v[u] = load16(src + int64_t(vi) * 16);
-            }
-            for (int j = 0; j < a.k; ++j) {
-                const int pj = __builtin_amdgcn_readlane(p[i], j);
-                if (pj < 0) continue;
-                char* row = reinterpret_cast<char*>(a.send_rows) + int64_t(pj) * a.stride;
+    for (int u = 0; u < kScatU; ++u) v[u] = load16(src + lane_off + u * kWave * 16);
+    char* rows = reinterpret_cast<char*>(a.send_rows);
+    for (int j = 0; j < a.k; ++j) {
+        const int p = __builtin_amdgcn_readfirstlane(prow[j]);
+        if (p < 0) continue;
+        const __amdgpu_buffer_rsrc_t row = buffer_rsrc(rows + int64_t(p) * a.stride, a.stride);
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int vi = c0 + u * kWave + lane;
-                    if (vi < a.nvec) store16_nt(row + int64_t(vi) * 16, v[u]);
-                }
-            }
-        }
-        // trailer bytes 8..15: the slot's source index, then zero
-        if (lane < a.k && p[i] >= 0) {
-            uint64_t* tr = reinterpret_cast<uint64_t*>(a.send_rows + int64_t(p[i]) * a.stride +
-                                                       a.trailer_off);
-            tr[1] = uint64_t(uint32_t(s[i]));
+        for (int u = 0; u < kScatU; ++u)
+            store16_coherent(row, int(lane_off) + u * kWave * 16, v[u]);
+    }
+}
+
+// The last, partial segment of a row: one vector at a time.  Plain scalar
+// arguments: a call that took the argument struct by reference would force
+// the whole struct into scratch memory.
+__device__ __noinline__ void scatter_tail(const char* __restrict__ src, char* __restrict__ rows,
+                                          int64_t stride, const int* prow, int k, int nvec,
+                                          int v0)
+{
+    for (int u = 0; u < kScatU; ++u) {
+        const int vi = v0 + u * kWave;
+        if (vi >= nvec) break;
+        const u32x4 v = load16(src + int64_t(vi) * 16);
+        for (int j = 0; j < k; ++j) {
+            const int p = prow[j];         // lanes may have left: no wave op here
+            if (p >= 0) store16_coherent(buffer_rsrc(rows + int64_t(p) * stride, stride), vi * 16, v);
         }
     }
-    fence_release();                       // payloads + trailer tails before the flags
-    for (int i = 0; i < kTokPerWave; ++i) {
-        if (lane < a.k && p[i] >= 0 && t_first + i < a.T) {
-            uint64_t* tr = reinterpret_cast<uint64_t*>(a.send_rows + int64_t(p[i]) * a.stride +
-                                                       a.trailer_off);
-            st_relaxed64(tr, epoch);
+}
+
+__device__ void do_scatter(const FusedArgs& a, int item, uint64_t epoch, int* sh_pos,
+                           int* sh_word)
+{
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = lane_id();
+    const int t0 = item * kScatTok;
+    if (wave == 0) {
+        int p[kPickRounds];
+        const bool ok = item_positions(a, t0, kScatTok, uint32_t(epoch), sh_pos, p);
+        if (lane == 0) sh_word[0] = ok;
+    }
+    __syncthreads();
+    if (!__builtin_amdgcn_readfirstlane(sh_word[0])) return;
+
+    // payload: waves 2i and 2i+1 copy token t0 + i, alternating row segments
+    const int i = wave >> 1;
+    const int t = t0 + i;
+    if (t < a.T) {
+        const char* src = reinterpret_cast<const char*>(a.x) + int64_t(t) * a.nvec * 16;
+        const int* prow = sh_pos + i * a.k;
+        for (int seg = wave & 1; seg * kSegVec < a.nvec; seg += 2) {
+            const int v0 = seg * kSegVec + lane;
+            if ((seg + 1) * kSegVec <= a.nvec)
+                scatter_whole(src, a, prow, uint32_t(v0) * 16u);
+            else
+                scatter_tail(src, reinterpret_cast<char*>(a.send_rows), a.stride, prow, a.k,
+                             a.nvec, v0);
+        }
+    }
+    // Release without an L2 write-back: every payload store is agent-coherent
+    // (sc1), so once each wave has seen its own stores complete and the
+    // workgroup has met at the barrier, the whole item's payload is visible
+    // on every XCD.  This is the sequence an agent-scope release store
+    // lowers to (wait for prior stores, then the sc1 flag store), minus the
+    // L2 write-back that exists only for non-coherent stores -- and that
+    // write-back, once per item, cost more than the copy itself.
+    wait_own_stores();
+    __syncthreads();
+
+    // wave 0: pos, trailer tails (agent-coherent), then the epochs
+    if (wave == 0) {
+        const int npick = kScatTok * a.k;
+        const int64_t s0 = int64_t(t0) * a.k;
+        for (int q = lane; q < npick; q += kWave) {
+            const int64_t s = s0 + q;
+            if (s >= a.S) break;
+            const int p = sh_pos[q];
+            a.pos[s] = p;
+            if (p >= 0) st_relaxed64(trailer(a, p) + 1, uint64_t(uint32_t(s)));
+        }
+        wait_own_stores();                 // trailer tails before the flags
+        for (int q = lane; q < npick; q += kWave) {
+            const int64_t s = s0 + q;
+            if (s >= a.S) break;
+            const int p = sh_pos[q];
+            if (p >= 0) st_relaxed64(trailer(a, p), epoch);
         }
     }
 }
 
 // ---------------------------------------------------------------- combine item
+// One 64-vector segment that lies inside the row: all picks' loads first (KC
+// unrolled), then the fixed-order reduction.
 template <int KC>
-__device__ void do_combine(const FusedArgs& a, int item, uint64_t epoch) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int lane = lane_id();
-    const int k = KC > 0 ? KC : a.k;
-    const int t_first = item * kTokPerItem + wave * kTokPerWave;
-    if (t_first >= a.T) return;
-    int p[kTokPerWave];
-    int64_t s[kTokPerWave];
-    if (!wave_positions(a, t_first, uint32_t(epoch), p, s)) return;
-
-    // wait for the k trailers of each token to carry this call's epoch
-    Waiter wt;
-    while (true) {
-        bool ready = true;
-#pragma unroll
-        for (int i = 0; i < kTokPerWave; ++i) {
-            if (lane < k && p[i] >= 0) {
-                const uint64_t* tr = reinterpret_cast<const uint64_t*>(
-                    a.send_rows + int64_t(p[i]) * a.stride + a.trailer_off);
-                ready = ready && ld_relaxed64(tr) == epoch;
-            }
-        }
-        if (ballot(!ready) == 0) break;
-        if (!wt.tick(a.hdr, a.spin_limit)) return;
-    }
-    fence_acquire();                       // the rows' payloads
-
+__device__ __forceinline__ void combine_whole(const FusedArgs& a, const int (&pj)[KC > 0 ? KC : 1],
+                                              const int* prow, const float* wrow,
+                                              uint32_t off, char* dst)
+{
     const uint32_t S = uint32_t(a.S);
     const char* rows = reinterpret_cast<const char*>(a.send_rows);
-    for (int i = 0; i < kTokPerWave; ++i) {
-        const int t = t_first + i;
-        if (t >= a.T) break;
-        const float wl = lane < k ? a.w[int64_t(t) * k + lane] : 0.0f;
-        char* dst = reinterpret_cast<char*>(a.out) + int64_t(t) * a.nvec * 16;
-        constexpr int U = 2;
-        for (int c0 = 0; c0 < a.nvec; c0 += kWave * U) {
-            const int v0 = c0 + lane;
-            if (c0 + kWave * U <= a.nvec) {
-                const uint32_t off = uint32_t(v0) * 16u;
-                float acc[U][8];
-                if constexpr (KC > 0) {
-                    u32x4 r[KC][U];
+    float acc[1][8];
+    if constexpr (KC > 0) {
+        u32x4 r[KC][1];
 #pragma unroll
-                    for (int j = 0; j < KC; ++j) {
-                        const int pj = __builtin_amdgcn_readlane(p[i], j);
-                        const char* src = rows + int64_t(pj < 0 ? 0 : pj) * a.stride + off;
+        for (int j = 0; j < KC; ++j)
+            r[j][0] = uint32_t(pj[j]) < S ? load16_nt(rows + int64_t(pj[j]) * a.stride + off)
+                                          : u32x4{0, 0, 0, 0};
 #pragma unroll
-                        for (int u = 0; u < U; ++u)
-                            r[j][u] = uint32_t(pj) < S ? load16_nt(src + u * kWave * 16)
-                                                       : u32x4{0, 0, 0, 0};
+        for (int j = 0; j < KC; ++j) accumulate<1>(acc, r[j], wrow[j], j == 0);
+    } else {
+        for (int j = 0; j < a.k; ++j) {
+            const int p = __builtin_amdgcn_readfirstlane(prow[j]);
+            u32x4 r[1];
+            r[0] = uint32_t(p) < S ? load16_nt(rows + int64_t(p) * a.stride + off)
+                                   : u32x4{0, 0, 0, 0};
+            accumulate<1>(acc, r, wrow[j], j == 0);
+        }
+    }
+    store_acc<1>(dst + off, acc);
+}
+
+// The last, partial segment of a row (scalar arguments, as scatter_tail).
+__device__ __noinline__ void combine_tail(const char* __restrict__ rows, int64_t stride,
+                                          uint32_t S, const int* prow, const float* wrow,
+                                          int k, int nvec, int v0, char* dst)
+{
+    if (v0 >= nvec) return;
+    const uint32_t off = uint32_t(v0) * 16u;
+    float acc[1][8];
+    for (int j = 0; j < k; ++j) {
+        const int p = prow[j];             // lanes may have left: no wave op here
+        u32x4 r[1];
+        r[0] = uint32_t(p) < S ? load16_nt(rows + int64_t(p) * stride + off)
+                               : u32x4{0, 0, 0, 0};
+        accumulate<1>(acc, r, wrow[j], j == 0);
+    }
+    store_acc<1>(dst + off, acc);
+}
+
+template <int KC>
+__device__ void do_combine(const FusedArgs& a, int item, uint64_t epoch, int* sh_pos,
+                           int* sh_word)
+{
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = lane_id();
+    const int t0 = item * kCombTok;
+    if (wave == 0) {
+        int p[kPickRounds];
+        bool ok = item_positions(a, t0, kCombTok, uint32_t(epoch), sh_pos, p);
+        if (ok) {
+            // One trailer first, as for the bases: the first pick of token
+            // t0 + 2, whose scatter item was claimed after token t0's.
+            const int q = (kCombTok / 2) * a.k;
+            const int pr = q < kWave ? p[0] : q < 2 * kWave ? p[1] : q < 3 * kWave ? p[2] : p[3];
+            const int ps = __builtin_amdgcn_readlane(pr, q % kWave);
+            if (ps >= 0) {
+                Waiter wt0;
+                while (ld_relaxed64(trailer(a, ps)) != epoch)
+                    if (!wt0.tick(a.hdr, a.spin_limit)) {
+                        ok = false;
+                        break;
                     }
-#pragma unroll
-                    for (int j = 0; j < KC; ++j)
-                        accumulate<U>(acc, r[j], __shfl(wl, j, kWave), j == 0);
-                } else {
-                    for (int j = 0; j < k; ++j) {
-                        const int pj = __builtin_amdgcn_readlane(p[i], j);
-                        const char* src = rows + int64_t(pj < 0 ? 0 : pj) * a.stride + off;
-                        u32x4 r[U];
-#pragma unroll
-                        for (int u = 0; u < U; ++u)
-                            r[u] = uint32_t(pj) < S ? load16_nt(src + u * kWave * 16)
-                                                    : u32x4{0, 0, 0, 0};
-                        accumulate<U>(acc, r, __shfl(wl, j, kWave), j == 0);
-                    }
-                }
-                store_acc<U>(dst + off, acc);
-            } else {
-                for (int u = 0; u < U; ++u) {
-                    const int vi = v0 + u * kWave;
-                    const uint32_t off = uint32_t(vi < a.nvec ? vi : 0) * 16u;
-                    float acc[1][8];
-                    for (int j = 0; j < k; ++j) {
-                        const int pj = __builtin_amdgcn_readlane(p[i], j);
-                        const char* src = rows + int64_t(pj < 0 ? 0 : pj) * a.stride + off;
-                        u32x4 r[1];
-                        r[0] = (uint32_t(pj) < S && vi < a.nvec) ? load16_nt(src)
-                                                                 : u32x4{0, 0, 0, 0};
-                        accumulate<1>(acc, r, __shfl(wl, j, kWave), j == 0);
-                    }
-                    if (vi < a.nvec) store_acc<1>(dst + off, acc);
-                }
             }
         }
+        if (ok) {
+            // then the item's trailers, all of them carrying this call's epoch
+            Waiter wt;
+            while (true) {
+                bool ready = true;
+#pragma unroll
+                for (int r = 0; r < kPickRounds; ++r)
+                    if (p[r] >= 0) ready = ready && ld_relaxed64(trailer(a, p[r])) == epoch;
+                if (ballot(!ready) == 0) break;
+                if (!wt.tick(a.hdr, a.spin_limit)) {
+                    ok = false;
+                    break;
+                }
+            }
+            fence_acquire();               // the rows' payloads
+        }
+        if (lane == 0) sh_word[0] = ok;
+    }
+    __syncthreads();
+    if (!__builtin_amdgcn_readfirstlane(sh_word[0])) return;
+
+    // kWavesPerBlock / kCombTok waves per token, alternating 64-vector segments
+    constexpr int kWpt = kWavesPerBlock / kCombTok;
+    const int i = wave / kWpt;
+    const int t = t0 + i;
+    if (t >= a.T) return;
+    const int k = KC > 0 ? KC : a.k;
+    const int* prow = sh_pos + i * k;
+    const float* wrow = a.w + int64_t(t) * k;
+    char* dst = reinterpret_cast<char*>(a.out) + int64_t(t) * a.nvec * 16;
+    int pj[KC > 0 ? KC : 1];
+#pragma unroll
+    for (int j = 0; j < (KC > 0 ? KC : 1); ++j)
+        pj[j] = KC > 0 ? __builtin_amdgcn_readfirstlane(prow[j]) : 0;
+    for (int v0 = (wave % kWpt) * kWave + lane; v0 - lane < a.nvec; v0 += kWpt * kWave) {
+        if (v0 - lane + kWave <= a.nvec)
+            combine_whole<KC>(a, pj, prow, wrow, uint32_t(v0) * 16u, dst);
+        else
+            combine_tail(reinterpret_cast<const char*>(a.send_rows), a.stride, uint32_t(a.S),
+                         prow, wrow, a.k, a.nvec, v0, dst);
     }
 }
 
@@ -357,6 +499,7 @@ __device__ void do_combine(const FusedArgs& a, int item, uint64_t epoch) {
 template <int KC>
 __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs a) {
     __shared__ int32_t hist[kWavesPerBlock][kMaxE];
+    __shared__ int sh_pos[kMaxItemPicks];
     __shared__ int sh_wave_total[kWavesPerBlock];
     __shared__ int sh_word[2];
     __shared__ int sh_ticket;
@@ -364,8 +507,8 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs a) {
     const uint64_t epoch = a.hdr->epoch;          // constant during the call
     const int first_scan = a.nTiles;
     const int first_scatter = first_scan + a.nScan;
-    const int first_combine = first_scatter + a.nItems;
-    const int total = first_combine + a.nItems;
+    const int first_combine = first_scatter + a.nScat;
+    const int total = first_combine + a.nComb;
 
     // The barrier opens each round, BEFORE thread 0 claims the ticket: a
     // divergent thread-0 block must never follow another one (the end of a
@@ -373,24 +516,24 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs a) {
     // two and build an inner loop that only lane 0 leaves -- the other 255
     // threads would then cycle on a stale ticket forever.  The ticket is made
     // wave-uniform so every branch on it is a scalar branch.
+    int ticket;
     while (true) {
         __syncthreads();                  // everyone has read the last ticket
         if (tid == 0) sh_ticket = int(fetch_add(&a.hdr->work_ticket.v, 1u));
         __syncthreads();
-        const int ticket = __builtin_amdgcn_readfirstlane(sh_ticket);
+        ticket = __builtin_amdgcn_readfirstlane(sh_ticket);
         if (ticket >= total) break;
         if (ticket < first_scan) do_hist(a, ticket, hist);
         else if (ticket < first_scatter) do_scan(a, ticket - first_scan, uint32_t(epoch), sh_wave_total, sh_word);
-        else if (ticket < first_combine) do_scatter(a, ticket - first_scatter, epoch);
-        else do_combine<KC>(a, ticket - first_combine, epoch);
+        else if (ticket < first_combine) do_scatter(a, ticket - first_scatter, epoch, sh_pos, sh_word);
+        else do_combine<KC>(a, ticket - first_combine, epoch, sh_pos, sh_word);
     }
 
-    // Leave: the last workgroup out finishes the outputs and resets the state.
-    fence_release();
-    __syncthreads();
-    if (tid == 0) sh_word[0] = fetch_add_acq_rel(&a.hdr->exit_count.v, 1u) == gridDim.x - 1;
-    __syncthreads();
-    if (!__builtin_amdgcn_readfirstlane(sh_word[0])) return;
+    // Every workgroup makes exactly one claim past the last item, after all
+    // its work; the one whose claim came last of all (total + gridDim.x - 1)
+    // therefore runs after every other workgroup has finished.  It derives
+    // the counts, records the error word and resets the state.
+    if (ticket != total + int(gridDim.x) - 1) return;
     fence_acquire();
     const int L = a.E / a.R;
     for (int e = tid; e < a.E; e += kBlock)
@@ -402,13 +545,12 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs a) {
     if (tid == 0) {
         WsHeader* h = a.hdr;
         uint32_t err = kDevOk;
-        if (h->timeout.v) err = kDevTimeout;
+        if (ld_relaxed(&h->timeout.v)) err = kDevTimeout;
         else if (a.expert_offsets[a.E] != a.S) err = kDevBadExpert;
         h->error = err;
         h->timeout.v = 0;
         h->work_ticket.v = 0;
         h->hist_done.v = 0;
-        h->exit_count.v = 0;
         h->last_epoch = epoch;
         uint64_t next = epoch + 1;
         if (uint32_t(next) == 0) next += 1;       // the 32-bit tag is never 0
@@ -424,18 +566,18 @@ __global__ void fused_init_kernel(WsHeader* hdr, uint64_t first_epoch) {
         hdr->timeout.v = 0;
         hdr->work_ticket.v = 0;
         hdr->hist_done.v = 0;
-        hdr->exit_count.v = 0;
         hdr->epoch = first_epoch;
         hdr->last_epoch = 0;
     }
 }
 
 int resident_grid(const void* kernel) {
-    static int cached[64] = {0};
+    static int cached[64][2] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
     const int slot = dev < 64 ? dev : 63;
-    if (cached[slot] > 0) return cached[slot];
+    const int which = kernel == reinterpret_cast<const void*>(&fused_kernel<8>) ? 0 : 1;
+    if (cached[slot][which] > 0) return cached[slot][which];
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess ||
         per_cu < 1)
@@ -443,8 +585,8 @@ int resident_grid(const void* kernel) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 1)
         cus = 256;
-    cached[slot] = per_cu * cus;
-    return cached[slot];
+    cached[slot][which] = per_cu * cus;
+    return cached[slot][which];
 }
 
 }  // namespace
@@ -452,7 +594,7 @@ int resident_grid(const void* kernel) {
 hipError_t launch_fused_init(void* ws, uint64_t first_epoch, hipStream_t s) {
     if (uint32_t(first_epoch) == 0) first_epoch += 1;
     EP_LAUNCH(fused_init_kernel, dim3(1), dim3(64), 0, s,
-                       static_cast<WsHeader*>(ws), first_epoch);
+              static_cast<WsHeader*>(ws), first_epoch);
     return hipGetLastError();
 }
 
@@ -477,8 +619,9 @@ hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float*
     a.S = f.lay.S;
     a.nTiles = f.lay.nTiles;
     a.nCnt = f.lay.nCnt;
-    a.nScan = f.lay.nScan;
-    a.nItems = (T + kTokPerItem - 1) / kTokPerItem;
+    a.nScan = (f.lay.nCnt + kFusedScanItems - 1) / kFusedScanItems;   // <= f.lay.nScan
+    a.nScat = (T + kScatTok - 1) / kScatTok;
+    a.nComb = (T + kCombTok - 1) / kCombTok;
     a.stride = int64_t(fused_row_stride(H));
     a.trailer_off = int64_t(2) * H;
     a.expert_counts = expert_counts;
@@ -497,7 +640,7 @@ hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float*
 
     const void* kern = k == 8 ? reinterpret_cast<const void*>(&fused_kernel<8>)
                               : reinterpret_cast<const void*>(&fused_kernel<0>);
-    const int items = a.nTiles + a.nScan + 2 * a.nItems;
+    const int items = a.nTiles + a.nScan + a.nScat + a.nComb;
     int g = grid > 0 ? grid : resident_grid(kern);
     if (g > items) g = items;
     if (k == 8)

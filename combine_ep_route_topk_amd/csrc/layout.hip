@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kBlock) void layout_scan_kernel(
     if (tid == 0) sh_block = int(fetch_add(&hdr->scan_ticket.v, 1u));
     __syncthreads();
     const int blk = sh_block;
-    const BlockScan bs = block_scan(cnt, nCnt, blk, sh_wave_total);
+    const BlockScan<kScanItems> bs = block_scan<kScanItems>(cnt, nCnt, blk, sh_wave_total);
 
     if (wave == 0) {
         int exclusive = 0;
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kBlock) void layout_scan_kernel(
 
     int run = sh_exclusive + bs.thread_excl;
 #pragma unroll
-    for (int q = 0; q < kScanPerThread; ++q) {
+    for (int q = 0; q < BlockScan<kScanItems>::kPer; ++q) {
         const int i = bs.i0 + q;
         if (i < nCnt) {
             base[i] = run;

@@ -26,6 +26,7 @@
 typedef int hipError_t;
 typedef void* hipStream_t;
 enum { hipSuccess = 0, hipErrorNotSupported = 801 };
+struct alignas(16) int4 { int x, y, z, w; };
 struct dim3 { unsigned x, y, z; dim3(unsigned a = 1, unsigned b = 1, unsigned c = 1) : x(a), y(b), z(c) {} };
 
 namespace emu {
@@ -133,6 +134,24 @@ template <class T, class U> inline T emu_atomic_fetch_add(T* p, U v) { return __
 #define __hip_atomic_store(p, v, o, s) emu_atomic_store((p), (v))
 #define __hip_atomic_fetch_add(p, v, o, s) emu_atomic_fetch_add((p), (v))
 template <class T, class U> inline T atomicAdd(T* p, U v) { return __atomic_fetch_add(p, (T)v, __ATOMIC_SEQ_CST); }
+
+// Buffer descriptors and buffer stores: the emulation keeps base and size
+// and aborts on an access outside the range (the hardware would drop it).
+struct emu_buffer_rsrc { char* base; uint32_t n; };
+#define __amdgpu_buffer_rsrc_t emu_buffer_rsrc
+inline emu_buffer_rsrc emu_make_buffer_rsrc(void* p, int, int n, unsigned) {
+    return emu_buffer_rsrc{static_cast<char*>(p), uint32_t(n)};
+}
+template <class V> inline void emu_buffer_store(V v, emu_buffer_rsrc r, int off) {
+    if (off < 0 || uint64_t(uint32_t(off)) + sizeof(V) > r.n) {
+        std::fprintf(stderr, "[emu] buffer store at %d outside a %u-byte range\n", off, r.n);
+        std::abort();
+    }
+    std::memcpy(r.base + off, &v, sizeof(V));
+}
+#define __builtin_amdgcn_make_buffer_rsrc(p, s, n, f) emu_make_buffer_rsrc((void*)(p), (s), (n), (f))
+#define __builtin_amdgcn_raw_buffer_store_b128(v, r, off, soff, aux) emu_buffer_store((v), (r), (off))
+#define __builtin_amdgcn_s_waitcnt(x) ((void)0)
 
 inline hipError_t hipGetLastError() { return hipSuccess; }
 inline hipError_t hipGetDevice(int* d) { *d = 0; return 0; }

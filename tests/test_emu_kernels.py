@@ -113,10 +113,10 @@ SHAPES = [
     (128, 7168, 256, 32, 8, 1002),  # the decode-like workload's shape (k = 8 path)
     (5, 16, 4, 2, 2, 3),
     (130, 7176, 64, 8, 6, 4),       # ragged rows, runtime-k path
-    (600, 64, 256, 32, 8, 5),       # two layout tiles
+    (600, 64, 256, 32, 8, 5),       # five layout tiles
     (1, 8, 1, 1, 1, 6),
-    (3000, 24, 33, 3, 5, 7),        # four tiles, odd E
-    (8192, 16, 1024, 8, 4, 8),      # eight look-back blocks
+    (3000, 24, 33, 3, 5, 7),        # fifteen tiles, odd E
+    (8192, 16, 1024, 8, 4, 8),      # four look-back scan blocks
 ]
 
 
