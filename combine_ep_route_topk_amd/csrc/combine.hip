@@ -16,7 +16,9 @@
 // expert-output row is read exactly once, and keeping them out of the
 // Infinity Cache leaves it to the data the next kernels re-read (measured on
 // MI355X at T=4096, H=7168, k=8: combine 108 -> 97 us and the following
-// dispatch 111 -> 95 us).
+// dispatch 111 -> 95 us).  The output rows are stored streaming and
+// agent-coherent, through a descriptor over the token's row, so they do not
+// stay dirty in the L2 for the next kernel to flush.
 #include "ep_combine_dev.h"
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -70,7 +72,7 @@ __device__ __forceinline__ void combine_whole(const char* __restrict__ y,
             accumulate<U>(acc, r, wrow[j], false);
         }
     }
-    store_acc<U>(dst + lane_off, acc);
+    store_acc_coherent<U>(buffer_rsrc(dst, row_bytes), lane_off, acc);
 }
 
 // The last, partial segment of a row: one vector at a time.

@@ -32,6 +32,23 @@ __device__ __forceinline__ void accumulate(float (&acc)[U][8], const u32x4 (&r)[
     }
 }
 
+// Rounds acc[u][0..7] to bf16 and stores vector u at byte offset
+// off + u*kWave*16 of the row that descriptor `row` covers, streaming and
+// agent-coherent (written through the L2, so no dirty output lines are left
+// for the next kernel to wait on).
+template <int U>
+__device__ __forceinline__ void store_acc_coherent(__amdgpu_buffer_rsrc_t row, uint32_t off,
+                                                   const float (&acc)[U][8])
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[u][2 * q], acc[u][2 * q + 1]);
+        store16_coherent(row, int(off) + u * kWave * 16, o);
+    }
+}
+
 // Rounds acc[u][0..7] to bf16 and stores vector u at dst + u*kWave*16.
 template <int U>
 __device__ __forceinline__ void store_acc(char* __restrict__ dst, const float (&acc)[U][8])

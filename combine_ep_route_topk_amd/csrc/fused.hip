@@ -406,7 +406,7 @@ __device__ __forceinline__ void combine_whole(const FusedArgs& a, const int (&pj
             accumulate<1>(acc, r, wrow[j], j == 0);
         }
     }
-    store_acc<1>(dst + off, acc);
+    store_acc_coherent<1>(buffer_rsrc(dst, int64_t(a.nvec) * 16), off, acc);
 }
 
 // The last, partial segment of a row (scalar arguments, as scatter_tail).
