@@ -35,6 +35,10 @@ LaunchTiming& launch_timing();
 constexpr int kBlock = 256;          // threads per workgroup (4 waves of 64)
 constexpr int kTileSlots = 1024;     // slots per layout tile (histogram unit)
 constexpr int kScanItems = 2048;     // (expert, tile) counters per scan block
+// Up to this many (expert, tile) counters the layout computes every tile's
+// bases inside the positions launch (each workgroup re-reads all counters)
+// instead of a separate device-wide scan.
+constexpr int kRedundantScanMax = 32768;
 // Counters per scan item of the persistent fused mode: one item covers the
 // 8192 counters of the dsv3-sized layout, so its look-back chain is empty.
 constexpr int kFusedScanItems = 8192;

@@ -27,6 +27,13 @@
 //      expert e's slots from that tile; base[e][0] is expert e's offset.
 //   3. pos   -- pos[s] = base[e][tile(s)] + rank(s); slot_src[pos[s]] = s;
 //      block 0 derives the per-expert / per-rank counts and offsets.
+// When the counters are few (nCnt <= kRedundantScanMax: 32 K, i.e. 128 KiB),
+// steps 2 and 3 are one launch instead: every tile's workgroup reads all of
+// cnt (from L2) and computes the bases of its own tile itself,
+//   base[e][tile] = offset[e] + sum_{t < tile} cnt[e][t],
+//   offset = exclusive scan over e of sum_t cnt[e][t],
+// which costs each workgroup a 32 KiB read at T=4096, k=8, E=256 and saves a
+// launch and the look-back (measured on MI355X: layout 14.3 -> ~10 us).
 #include "ep_device.h"
 #include "ep_internal.h"
 #include "ep_layout_dev.h"
@@ -160,6 +167,131 @@ __global__ __launch_bounds__(kBlock) void layout_pos_kernel(
     }
 }
 
+// Scan + positions in one launch, one workgroup per tile (see the header).
+// Experts are split contiguously, kExpPerThread per thread, so the scan over
+// experts is a thread-local run plus one block-wide scan.
+constexpr int kExpPerThread = kMaxE / kBlock;    // 4
+static_assert(kExpPerThread * kBlock == kMaxE, "expert split");
+__global__ __launch_bounds__(kBlock) void layout_scanpos_kernel(
+    const int32_t* __restrict__ topk_idx, int64_t S, int E, int R, int nTiles,
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ local_rank,
+    int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
+    int32_t* __restrict__ pos, int32_t* __restrict__ slot_src, WsHeader* __restrict__ hdr)
+{
+    __shared__ int sh_off[kMaxE + 1];      // expert offsets (exclusive scan)
+    __shared__ int sh_base[kMaxE];         // first row of (expert, this tile)
+    __shared__ int sh_wave_total[kWavesPerBlock];
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = lane_id();
+    const int tile = blockIdx.x;
+
+    // per expert: its total over all tiles and its count before this tile.
+    // Each round issues all its loads (kExpPerThread experts x 4 vectors of 4
+    // counters) before adding any: the counters come from L2, and a loop of
+    // dependent load-add steps would pay one L2 latency per step.
+    int tot[kExpPerThread], pre[kExpPerThread];
+#pragma unroll
+    for (int q = 0; q < kExpPerThread; ++q) tot[q] = pre[q] = 0;
+    const int e0 = tid * kExpPerThread;
+    if (nTiles % 4 == 0) {                      // rows are 16-byte aligned
+        for (int t0 = 0; t0 < nTiles; t0 += 16) {
+            int4 c[kExpPerThread][4];
+#pragma unroll
+            for (int q = 0; q < kExpPerThread; ++q)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int t = t0 + 4 * m;
+                    c[q][m] = (e0 + q < E && t < nTiles)
+                                  ? *reinterpret_cast<const int4*>(cnt + int64_t(e0 + q) * nTiles + t)
+                                  : make_int4(0, 0, 0, 0);
+                }
+#pragma unroll
+            for (int q = 0; q < kExpPerThread; ++q)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int t = t0 + 4 * m;
+                    tot[q] += c[q][m].x + c[q][m].y + c[q][m].z + c[q][m].w;
+                    pre[q] += (t < tile ? c[q][m].x : 0) + (t + 1 < tile ? c[q][m].y : 0) +
+                              (t + 2 < tile ? c[q][m].z : 0) + (t + 3 < tile ? c[q][m].w : 0);
+                }
+        }
+    } else {
+        for (int t0 = 0; t0 < nTiles; t0 += 4) {
+            int c[kExpPerThread][4];
+#pragma unroll
+            for (int q = 0; q < kExpPerThread; ++q)
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    c[q][m] = (e0 + q < E && t0 + m < nTiles)
+                                  ? cnt[int64_t(e0 + q) * nTiles + t0 + m] : 0;
+#pragma unroll
+            for (int q = 0; q < kExpPerThread; ++q)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    tot[q] += c[q][m];
+                    pre[q] += t0 + m < tile ? c[q][m] : 0;
+                }
+        }
+    }
+    int tsum = 0;
+#pragma unroll
+    for (int q = 0; q < kExpPerThread; ++q) tsum += tot[q];
+    // block-wide exclusive scan of the per-thread totals
+    const int incl = wave_inclusive_sum(tsum);
+    if (lane == kWave - 1) sh_wave_total[wave] = incl;
+    __syncthreads();
+    int run = incl - tsum;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w)
+        if (w < wave) run += sh_wave_total[w];
+#pragma unroll
+    for (int q = 0; q < kExpPerThread; ++q) {
+        const int e = tid * kExpPerThread + q;
+        if (e < E) {
+            sh_off[e] = run;
+            sh_base[e] = run + pre[q];
+            if (tile == 0) {
+                expert_offsets[e] = run;
+                expert_counts[e] = tot[q];
+            }
+            if (e == E - 1) {
+                sh_off[E] = run + tot[q];
+                if (tile == 0) expert_offsets[E] = run + tot[q];
+            }
+        }
+        run += tot[q];
+    }
+    __syncthreads();
+
+    if (tile == 0) {
+        const int L = E / R;
+        for (int r = tid; r <= R; r += kBlock) {
+            rank_offsets[r] = sh_off[r * L];
+            if (r < R) rank_counts[r] = sh_off[(r + 1) * L] - sh_off[r * L];
+        }
+        if (tid == 0) {
+            hdr->error = sh_off[E] != S ? kDevBadExpert : kDevOk;
+            hdr->magic = kLayoutMagic;
+        }
+    }
+
+    // positions of this tile's slots
+    for (int i = tid; i < kTileSlots; i += kBlock) {
+        const int64_t s = int64_t(tile) * kTileSlots + i;
+        if (s >= S) break;
+        const int e = topk_idx[s];
+        if (unsigned(e) < unsigned(E)) {
+            const int p = sh_base[e] + local_rank[s];
+            pos[s] = p;
+            if (slot_src) slot_src[p] = int(s);
+        } else {
+            pos[s] = -1;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_dispatch_layout(const int32_t* topk_idx, int T, int k, int E, int R,
@@ -179,6 +311,12 @@ hipError_t launch_dispatch_layout(const int32_t* topk_idx, int T, int k, int E, 
                        topk_idx, p.S, E, p.nTiles, p.nScan, cnt, rank, status, hdr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (p.nCnt <= kRedundantScanMax) {
+        EP_LAUNCH(layout_scanpos_kernel, dim3(p.nTiles), dim3(kBlock), 0, s,
+                  topk_idx, p.S, E, R, p.nTiles, cnt, rank, expert_counts, expert_offsets,
+                  rank_counts, rank_offsets, pos, slot_src, hdr);
+        return hipGetLastError();
+    }
     EP_LAUNCH(layout_scan_kernel, dim3(p.nScan), dim3(kBlock), 0, s,
                        cnt, p.nCnt, p.nTiles, E, base, expert_offsets, status, hdr,
                        kDefaultSpinLimit);

@@ -146,8 +146,9 @@ EDGE = [
     (1, 8, 1, 1, 1, 1),           # smallest everything
     (3, 16, 4, 2, 2, 2),
     (130, 7176, 64, 8, 6, 3),     # ragged rows (897 vectors) and T % 4 != 0
-    (8192, 64, 1024, 8, 4, 4),    # E = 1024: 8 tiles x 1024 experts -> 8 scan blocks
-    (50000, 24, 8, 4, 2, 5),      # 25 tiles, ragged last tile
+    (8192, 64, 1024, 8, 4, 4),    # E = 1024: 32 tiles x 1024 experts, bases in the positions launch
+    (16384, 16, 1024, 8, 4, 8),   # 65536 counters: separate scan launch, 32 look-back blocks
+    (50000, 24, 8, 4, 2, 5),      # 98 tiles, ragged last tile
     (257, 520, 33, 3, 5, 6),      # odd E, odd H/8 = 65
     (64, 4096, 128, 16, 64, 7),   # k = 64 (maximum)
 ]
