@@ -117,6 +117,7 @@ struct FusedPlan {
     LayoutPlan lay;
     size_t off_status64;  // u64 [nScan]  (epoch32 << 32 | flag << 30 | value)
     size_t off_fbase;     // u64 [nCnt]   (epoch32 << 32 | base) published bases
+    size_t off_sdone;     // u64 [ceil(T/2)] epoch of the call once a scatter item is done
     size_t bytes;
 };
 
@@ -126,6 +127,7 @@ inline FusedPlan fused_plan(int T, int k, int E) {
     size_t off = f.lay.bytes;
     f.off_status64 = off; off += align256(sizeof(uint64_t) * f.lay.nScan);
     f.off_fbase = off;    off += align256(sizeof(uint64_t) * f.lay.nCnt);
+    f.off_sdone = off;    off += align256(sizeof(uint64_t) * ((size_t(T) + 1) / 2));
     f.bytes = off;
     return f;
 }

@@ -29,10 +29,12 @@
 //             agent-coherent streaming stores; every wave waits for its
 //             stores to complete, and after a barrier wave 0 writes pos and
 //             {slot_src, 0} into the rows' trailers, then the 64-bit epoch.
-//   [combine] kCombTok tokens: wave 0 recomputes the positions, polls the
-//             item's trailers until they hold this call's epoch, issues one
-//             acquire fence; after a barrier each wave reduces one token's k
-//             rows with the same fp32 arithmetic as ep_combine.
+//   [combine] kCombTok tokens: wave 0 waits for the event words of the
+//             scatter items of its tokens (one epoch-tagged word per item),
+//             reads the positions those items wrote to pos, acquire-polls the
+//             rows' trailers until they hold this call's epoch; after a
+//             barrier each wave reduces one token's k rows with the same fp32
+//             arithmetic as ep_combine.
 // A row's trailer is its flag: on gfx950 a 64-bit aligned store is
 // single-copy atomic but a 14 KiB row is not, hence payload -> release ->
 // trailer, and trailer -> acquire -> payload on the reading side.  An
@@ -70,6 +72,7 @@ constexpr int kSegVec = kWave * kScatU;        // vectors per scatter row segmen
 constexpr int kMaxItemPicks = kCombTok * kMaxK;
 constexpr int kPickRounds = kMaxItemPicks / kWave;   // lanes cover the picks in <= 4 rounds
 static_assert(kScatTok * 2 == kWavesPerBlock, "two waves per scatter token");
+static_assert(kCombTok % kScatTok == 0, "a combine item covers whole scatter items");
 constexpr uint64_t kStFlagAggregate = uint64_t(1) << 30;
 constexpr uint64_t kStFlagInclusive = uint64_t(2) << 30;
 constexpr uint64_t kStValueMask = (uint64_t(1) << 30) - 1;
@@ -95,6 +98,7 @@ struct FusedArgs {
     int32_t* local_rank;
     uint64_t* status;
     uint64_t* fbase;
+    uint64_t* sdone;                      // per scatter item: the epoch once it is done
     uint32_t spin_limit;
 };
 
@@ -234,20 +238,23 @@ __device__ bool item_positions(const FusedArgs& a, int t0, int ntok, uint32_t ep
         e[r] = (q < npick && s < a.S) ? a.idx[s] : -1;
         word[r] = 0;
     }
-    // One word first: every lane reads the base word of pick 0, so a wave
-    // sends one request per polling round instead of one per pick (thousands
-    // of waves wait here while the layout runs, and their polls would slow
-    // it).  The scan publishes all bases within a short window, so the full
-    // poll below rarely needs a second round.
-    const int e0 = __builtin_amdgcn_readfirstlane(e[0]);
-    if (unsigned(e0) < unsigned(a.E)) {
-        const uint64_t* w0 = &a.fbase[int64_t(e0) * a.nTiles + s0 / kTileSlots];
-        Waiter wt0;
-        while (!published(ld_relaxed64(w0), ep32))
-            if (!wt0.tick(a.hdr, a.spin_limit)) return false;
-    }
+    // One full poll first (an item claimed after the layout is done finds
+    // every base published at once).  If it fails, wait on ONE word -- every
+    // lane reads the base word of pick 0, so a wave sends one request per
+    // polling round instead of one per pick while the layout runs (thousands
+    // of waves may wait here, and their polls would slow it) -- then poll
+    // all words again; the scan publishes them within a short window.
     Waiter wt;
-    while (true) {
+    for (int round = 0;; ++round) {
+        if (round == 1) {
+            const int e0 = __builtin_amdgcn_readfirstlane(e[0]);
+            if (unsigned(e0) < unsigned(a.E)) {
+                const uint64_t* w0 = &a.fbase[int64_t(e0) * a.nTiles + s0 / kTileSlots];
+                Waiter wt0;
+                while (!published(ld_relaxed64(w0), ep32))
+                    if (!wt0.tick(a.hdr, a.spin_limit)) return false;
+            }
+        }
         bool ready = true;
 #pragma unroll
         for (int r = 0; r < kPickRounds; ++r) {
@@ -365,16 +372,18 @@ __device__ void do_scatter(const FusedArgs& a, int item, uint64_t epoch, int* sh
             const int64_t s = s0 + q;
             if (s >= a.S) break;
             const int p = sh_pos[q];
-            a.pos[s] = p;
+            st_relaxed(reinterpret_cast<uint32_t*>(&a.pos[s]), uint32_t(p));
             if (p >= 0) st_relaxed64(trailer(a, p) + 1, uint64_t(uint32_t(s)));
         }
-        wait_own_stores();                 // trailer tails before the flags
+        wait_own_stores();                 // pos and trailer tails before the flags
         for (int q = lane; q < npick; q += kWave) {
             const int64_t s = s0 + q;
             if (s >= a.S) break;
             const int p = sh_pos[q];
             if (p >= 0) st_relaxed64(trailer(a, p), epoch);
         }
+        // the item's event word: its pos entries are final
+        if (lane == 0) st_relaxed64(&a.sdone[item], epoch);
     }
 }
 
@@ -435,25 +444,39 @@ __device__ void do_combine(const FusedArgs& a, int item, uint64_t epoch, int* sh
     const int lane = lane_id();
     const int t0 = item * kCombTok;
     if (wave == 0) {
-        int p[kPickRounds];
-        bool ok = item_positions(a, t0, kCombTok, uint32_t(epoch), sh_pos, p);
-        if (ok) {
-            // One trailer first, as for the bases: the first pick of token
-            // t0 + 2, whose scatter item was claimed after token t0's.
-            const int q = (kCombTok / 2) * a.k;
-            const int pr = q < kWave ? p[0] : q < 2 * kWave ? p[1] : q < 3 * kWave ? p[2] : p[3];
-            const int ps = __builtin_amdgcn_readlane(pr, q % kWave);
-            if (ps >= 0) {
-                Waiter wt0;
-                while (ld_relaxed64(trailer(a, ps)) != epoch)
-                    if (!wt0.tick(a.hdr, a.spin_limit)) {
-                        ok = false;
-                        break;
-                    }
+        // 1. the event words of the scatter items of these tokens: once they
+        //    hold this call's epoch, those items' pos entries are final (one
+        //    word per scatter item instead of recomputing every position from
+        //    the published bases and ranks -- fewer dependent load rounds,
+        //    which cost several microseconds each while HBM is saturated)
+        bool ok = true;
+        const int sfirst = t0 / kScatTok;
+        const int nsc = a.nScat - sfirst < kCombTok / kScatTok ? a.nScat - sfirst : kCombTok / kScatTok;
+        Waiter wt0;
+        while (true) {
+            const bool mine = lane < nsc ? ld_relaxed64(&a.sdone[sfirst + lane]) == epoch : true;
+            if (ballot(!mine) == 0) break;
+            if (!wt0.tick(a.hdr, a.spin_limit)) {
+                ok = false;
+                break;
             }
         }
+        int p[kPickRounds];
         if (ok) {
-            // then the item's trailers, all of them carrying this call's epoch
+            fence_acquire();               // the pos entries of those items
+            // 2. positions of the item's picks, from pos
+            const int npick = kCombTok * a.k;
+            const int64_t s0 = int64_t(t0) * a.k;
+#pragma unroll
+            for (int r = 0; r < kPickRounds; ++r) {
+                const int q = r * kWave + lane;
+                const int64_t s = s0 + q;
+                int pr = (q < npick && s < a.S) ? a.pos[s] : -1;
+                if (uint64_t(uint32_t(pr)) >= uint64_t(a.S)) pr = -1;   // never address outside the rows
+                p[r] = pr;
+                if (q < npick) sh_pos[q] = pr;
+            }
+            // 3. acquire-poll every row's trailer (the Data-as-Flag check)
             Waiter wt;
             while (true) {
                 bool ready = true;
@@ -636,6 +659,7 @@ hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float*
     a.local_rank = reinterpret_cast<int32_t*>(w + f.lay.off_rank);
     a.status = reinterpret_cast<uint64_t*>(w + f.off_status64);
     a.fbase = reinterpret_cast<uint64_t*>(w + f.off_fbase);
+    a.sdone = reinterpret_cast<uint64_t*>(w + f.off_sdone);
     a.spin_limit = spin_limit ? spin_limit : kDefaultSpinLimit;
 
     const void* kern = k == 8 ? reinterpret_cast<const void*>(&fused_kernel<8>)
