@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--no-isolated", action="store_true",
+                    help="skip the per-op timings after a cache-clearing overwrite")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -230,9 +232,14 @@ def main():
         "dispatch_combine_pct_of_peak": round(100 * dc_gbps / HBM_PEAK_GBPS, 2),
         "per_op_us": {n: round(v, 2) for n, v in mean_us.items()},
         "per_op_p10_p90_us": {n: [round(p10_us[n], 2), round(p90_us[n], 2)] for n in names},
+        # a timing is taken as stable when p90 / p10 <= 1.2 (RailWave's rule)
+        "per_op_p90_over_p10": {n: round(p90_us[n] / p10_us[n], 3) for n in names},
         "algorithmic_bytes": ab,
         "roofline": roofline,
     }
+
+    if not args.no_isolated:
+        result["isolated"] = bench_isolated(ep, torch, hip, ops, names, set_events, dev, stream)
 
     if not args.no_fused:
         result["fused"] = bench_fused(ep, torch, w, x, idx, wt, stream, K, args.warmup)
@@ -241,6 +248,40 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, inp, lay, args.cpu_seconds, step_bytes)
 
     print(json.dumps(result), flush=True)
+
+
+def bench_isolated(ep, torch, hip, ops, names, set_events, dev, stream, reps=30):
+    """Each op on its own, its inputs left in place by a previous step, after
+    READING a 1 GiB scratch buffer (larger than the 256 MB Infinity Cache plus
+    8 x 4 MB of L2), so the op's reads come from HBM.  A read, not a write:
+    overwriting the buffer would leave the caches full of dirty lines whose
+    write-back the op would then pay for.  Times are the op's own kernels
+    (start and stop events recorded by their dispatch packets)."""
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    sink = torch.empty((), dtype=torch.int64, device=dev)
+    for _ in range(2):
+        torch.sum(scratch, dim=0, dtype=torch.int64, out=sink)
+    starts = [[hip.create() for _ in ops] for _ in range(reps)]
+    stops = [[hip.create() for _ in ops] for _ in range(reps)]
+    for r in range(reps):
+        for i, op in enumerate(ops):
+            torch.sum(scratch, dim=0, dtype=torch.int64, out=sink)
+            set_events(starts[r][i], stops[r][i])
+            op()
+    torch.cuda.synchronize()
+    res = {}
+    for i, n in enumerate(names):
+        v = np.array([hip.elapsed_ms(starts[r][i], stops[r][i]) * 1e3 for r in range(reps)])
+        p10, p50, p90 = np.percentile(v, [10, 50, 90])
+        res[n] = {"median_us": round(float(p50), 2), "p10_us": round(float(p10), 2),
+                  "p90_us": round(float(p90), 2), "p90_over_p10": round(float(p90 / p10), 3)}
+    for row in starts + stops:
+        for e in row:
+            hip.destroy(e)
+    del scratch
+    res["note"] = (f"{reps} reps per op, each after reading a 1 GiB buffer; the op's own "
+                   "kernels from their dispatch packets")
+    return res
 
 
 def bench_fused(ep, torch, w, x, idx, wt, stream, K, W):
@@ -278,13 +319,21 @@ def cpu_baseline(w, inp, gpu_lay, seconds, step_bytes):
 
     reps, t_total = 0, 0.0
     idx = wt = lay = None
+    stage_s = {"route": [], "layout": [], "dispatch": [], "combine": []}
     while reps < 1 or (t_total < seconds and reps < 20):
         t0 = time.perf_counter()
         idx, wt = oracle.route_topk(inp["logits"], w.k, 1)
+        t1 = time.perf_counter()
         lay = oracle.dispatch_layout(idx, w.E, w.R)
+        t2 = time.perf_counter()
         send = oracle.dispatch(inp["x"], lay["pos"])
+        t3 = time.perf_counter()
         oracle.combine(send, lay["pos"], wt)
-        t_total += time.perf_counter() - t0
+        t4 = time.perf_counter()
+        for name, a, b in (("route", t0, t1), ("layout", t1, t2), ("dispatch", t2, t3),
+                           ("combine", t3, t4)):
+            stage_s[name].append(b - a)
+        t_total += t4 - t0
         reps += 1
     sec_per_step = t_total / reps
     agree = bool(np.array_equal(gpu_lay["pos"].cpu().numpy(), lay["pos"]))
@@ -292,8 +341,20 @@ def cpu_baseline(w, inp, gpu_lay, seconds, step_bytes):
             "cores": 1, "kind": "oracle",
             "sample": f"{reps} whole steps of {w.name} (route, layout, dispatch, combine), "
                       f"{sec_per_step:.3f} s per step, single thread; host has "
-                      f"{os.cpu_count()} cores",
+                      f"{os.cpu_count()} cores ({cpu_model()})",
+            "stage_median_ms": {n: round(1e3 * float(np.median(v)), 2) for n, v in stage_s.items()},
             "gpu_pos_matches_oracle": agree}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 if __name__ == "__main__":
