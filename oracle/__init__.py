@@ -41,9 +41,12 @@ def lib():
         L.ep_oracle_combine.argtypes = [P, P, P, i64, i32, i32, P]
         L.ep_oracle_combine_tokens.argtypes = [P, P, P, i64, i32, i32, P, i64, P]
         L.ep_oracle_fused_trailer.argtypes = [ctypes.c_uint64, P, i64, P]
+        L.ep_oracle_combine_grad.argtypes = [P, P, P, P, i64, i32, i32, P, P]
+        L.ep_oracle_dispatch_grad.argtypes = [P, P, i64, i32, i32, P]
         for f in ("ep_oracle_route_topk", "ep_oracle_dispatch_layout",
                   "ep_oracle_dispatch", "ep_oracle_combine",
-                  "ep_oracle_combine_tokens", "ep_oracle_fused_trailer"):
+                  "ep_oracle_combine_tokens", "ep_oracle_fused_trailer",
+                  "ep_oracle_combine_grad", "ep_oracle_dispatch_grad"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -138,6 +141,35 @@ def combine_tokens(y_bits, pos, topk_w, tokens):
                                           _p(tokens), len(tokens), _p(out)),
            "combine_tokens")
     return out
+
+
+def combine_grad(grad_out_bits, y_bits, pos, topk_w):
+    """Backward of combine: grad_out u16 [T][H], y u16 [T*k][H], pos i32
+    [T][k], w f32 [T][k] -> (grad_y u16 [T*k][H], grad_w f64 [T][k])."""
+    grad_out_bits = _c(grad_out_bits, np.uint16)
+    y_bits = _c(y_bits, np.uint16)
+    pos = _c(pos, np.int32)
+    topk_w = _c(topk_w, np.float32)
+    T, k = pos.shape
+    H = grad_out_bits.shape[1]
+    grad_y = np.zeros((T * k, H), np.uint16)
+    grad_w = np.zeros((T, k), np.float64)
+    _check(lib().ep_oracle_combine_grad(_p(grad_out_bits), _p(y_bits), _p(pos), _p(topk_w),
+                                        T, H, k, _p(grad_y), _p(grad_w)), "combine_grad")
+    return grad_y, grad_w
+
+
+def dispatch_grad(grad_send_bits, pos):
+    """Backward of dispatch: grad_send u16 [T*k][H], pos i32 [T][k] -> grad_x
+    u16 [T][H]."""
+    grad_send_bits = _c(grad_send_bits, np.uint16)
+    pos = _c(pos, np.int32)
+    T, k = pos.shape
+    H = grad_send_bits.shape[1]
+    grad_x = np.empty((T, H), np.uint16)
+    _check(lib().ep_oracle_dispatch_grad(_p(grad_send_bits), _p(pos), T, H, k, _p(grad_x)),
+           "dispatch_grad")
+    return grad_x
 
 
 def fused_trailers(epoch: int, slot_src):

@@ -278,3 +278,59 @@ int ep_oracle_fused_trailer(uint64_t epoch, const int32_t* slot_src, int64_t slo
     for (int i = 0; i < 4; ++i) trailer[12 + i] = 0;
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward pass [HPMOE sec. 2.2, Fig. 2(b)]: the backward Dispatch is the    */
+/* gradient of the forward Combine, the backward Combine returns the          */
+/* gradient of the input activations.                                         */
+/* ------------------------------------------------------------------------ */
+
+int ep_oracle_combine_grad(const uint16_t* grad_out, const uint16_t* y,
+                           const int32_t* pos, const float* topk_w,
+                           int64_t T, int32_t H, int32_t k,
+                           uint16_t* grad_y, double* grad_w)
+{
+    if (!grad_out || !y || !pos || !topk_w || !grad_y || !grad_w || T < 0 || H < 1 || k < 1)
+        return -1;
+    if (check_pos(pos, T, k) != 0) return -4;
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t* g = grad_out + t * (int64_t)H;
+        for (int32_t j = 0; j < k; ++j) {
+            const int64_t p = pos[t * k + j];
+            const double w = (double)topk_w[t * k + j];
+            const uint16_t* yr = y + p * (int64_t)H;
+            uint16_t* gy = grad_y + p * (int64_t)H;
+            double dot = 0.0;
+            for (int32_t h = 0; h < H; ++h) {
+                const double gh = ep_oracle_bf16_to_double(g[h]);
+                /* d out[t][h] / d y[p][h] = w: the exact product (24 x 8
+                 * significant bits fits a double), rounded once to bf16. */
+                gy[h] = ep_oracle_double_to_bf16(w * gh);
+                /* d out[t][h] / d w = y[p][h]; summed over h against g. */
+                dot = dot + gh * ep_oracle_bf16_to_double(yr[h]);
+            }
+            grad_w[t * k + j] = dot;
+        }
+    }
+    return 0;
+}
+
+int ep_oracle_dispatch_grad(const uint16_t* grad_send, const int32_t* pos,
+                            int64_t T, int32_t H, int32_t k, uint16_t* grad_x)
+{
+    if (!grad_send || !pos || !grad_x || T < 0 || H < 1 || k < 1) return -1;
+    if (check_pos(pos, T, k) != 0) return -4;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < H; ++h) {
+            /* x[t] was copied to every row pos[t][j]: its gradient is the sum
+             * of those rows' gradients, in double, rounded once. */
+            double acc = 0.0;
+            for (int32_t j = 0; j < k; ++j) {
+                const int64_t p = pos[t * k + j];
+                acc = acc + ep_oracle_bf16_to_double(grad_send[p * (int64_t)H + h]);
+            }
+            grad_x[t * (int64_t)H + h] = ep_oracle_double_to_bf16(acc);
+        }
+    }
+    return 0;
+}

@@ -23,7 +23,9 @@
  *   [HPMOE]  "HyperParallel-MoE: Multi-Core Interleaved Scheduling for Fast MoE
  *            Training on Ascend NPUs" -- sec. 2.2 (router picks top-k experts,
  *            outputs weighted by routing scores and combined), sec. 4.1
- *            (Combine accumulates the top-k contributions by routing score).
+ *            (Combine accumulates the top-k contributions by routing score),
+ *            Fig. 2(b) (backward graph: backward Dispatch is the gradient of
+ *            the forward Combine; backward Combine gives the input gradient).
  *
  * Readings of points the pages leave open (all listed in the design notes):
  *   - gating = softmax; selection on the raw fp32 logits; larger logit first,
@@ -36,6 +38,9 @@
  *   - one row per (token, pick): S = T*k rows.
  *   - combine value = sum_j w[t][j] * y[pos[t][j]] evaluated in double
  *     (each product w*y is exact in double), rounded once to bf16 RNE.
+ *   - backward: activation gradients are bf16 like the activations, each
+ *     element rounded once (RNE) from its exact or double value; the
+ *     routing-weight gradient is a double dot product over H.
  *
  * Conventions: bf16 values travel as uint16_t bit patterns.  Every function
  * returns 0 on success and a negative value on a rejected argument.
@@ -88,6 +93,27 @@ int ep_oracle_combine_tokens(const uint16_t* y, const int32_t* pos,
                              const float* topk_w, int64_t T, int32_t H, int32_t k,
                              const int64_t* tokens, int64_t n_tokens,
                              uint16_t* out_rows);
+
+/* Backward of combine [HPMOE sec. 2.2, Fig. 2(b): the backward Dispatch is
+ * the gradient of the forward Combine].  With out[t] = sum_j w[t][j] *
+ * y[pos[t][j]] (the forward combine above):
+ *   grad_y[pos[t][j]][h] = bf16( w[t][j] * grad_out[t][h] )   exact product,
+ *                                                           one RNE rounding;
+ *   grad_w[t][j]         = sum_h grad_out[t][h] * y[pos[t][j]][h]  in double.
+ * grad_out bf16 [T][H]; y bf16 [T*k][H] (send order); grad_y bf16 [T*k][H];
+ * grad_w double [T][k].  pos must be a permutation of [0, T*k). */
+int ep_oracle_combine_grad(const uint16_t* grad_out, const uint16_t* y,
+                           const int32_t* pos, const float* topk_w,
+                           int64_t T, int32_t H, int32_t k,
+                           uint16_t* grad_y, double* grad_w);
+
+/* Backward of dispatch [HPMOE sec. 2.2, Fig. 2(b): the backward Combine
+ * returns the gradient of the input activations].  send[pos[t][j]] = x[t]
+ * for every j, so
+ *   grad_x[t][h] = bf16( sum_j grad_send[pos[t][j]][h] )  in double, one RNE.
+ * grad_send bf16 [T*k][H]; grad_x bf16 [T][H]. */
+int ep_oracle_dispatch_grad(const uint16_t* grad_send, const int32_t* pos,
+                            int64_t T, int32_t H, int32_t k, uint16_t* grad_x);
 
 /* Readiness trailer of slot `slot` in the flag-in-payload (fused) mode
  * [UBEP sec. 3.4, Fig. 6, read as one trailer per row]: 16 bytes =

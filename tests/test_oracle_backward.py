@@ -1,0 +1,244 @@
+"""Pins of the oracle's backward pass.
+
+HyperParallel-MoE, sec. 2.2 and Fig. 2(b): the backward graph runs the
+backward Dispatch, which is the gradient of the forward Combine, and the
+backward Combine, which returns the gradient of the input activations.
+
+The oracle's gradients are pinned to the forward oracle (itself pinned in
+test_oracle_dispatch_combine.py) by the mathematics, not by retyping them:
+  - brute force: combine and dispatch are linear, so the derivative of
+    L = <forward(u), g> along a basis vector e is L(e) itself -- the forward
+    oracle run on every basis vector of a tiny case gives every gradient entry;
+  - exact finite differences: L is linear in each routing weight, so
+    L(w + e_tj) - L(w) is grad_w[t][j] exactly;
+  - adjointness <forward(u), g> == <u, backward(g)> on a larger case;
+all three on small integers and dyadic weights, where every bf16 rounding of
+the forward oracle is exact.  The rounding of the generic case is pinned to
+exact rational arithmetic (tests/exact_bf16.py), including products whose f32
+rounding lands on a bf16 tie, and the double dot product to math.fsum within
+the error bound of a recursive double sum.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from combine_ep_route_topk_amd import workloads as wl
+from exact_bf16 import bf16_exact, rne_bf16_exact
+
+ONE = 0x3F80  # bf16 1.0
+
+
+def layout(T, E, R, k, seed):
+    rng = np.random.default_rng(seed)
+    idx, w = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
+    return oracle.dispatch_layout(idx, E, R)["pos"], w
+
+
+def ints_bf16(rng, shape, lo, hi):
+    a = rng.integers(lo, hi + 1, size=shape)
+    return wl.f32_to_bf16_bits(a.astype(np.float32)), a.astype(np.float64)
+
+
+def dyadic_weights(rng, T, k, m=8):
+    """Weights i/m with |i| <= m: short enough that every product with a small
+    integer is exact in bf16."""
+    return (rng.integers(-m, m + 1, size=(T, k)) / m).astype(np.float32)
+
+
+def val(bits):
+    return wl.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def loss_combine(y_bits, pos, w, g):
+    """L = <combine(y), g> from the forward oracle, with its exactness checked."""
+    out = oracle.combine(y_bits, pos, w)
+    exact = np.zeros(out.shape)
+    for j in range(pos.shape[1]):
+        exact += w[:, j:j + 1].astype(np.float64) * val(y_bits)[pos[:, j]]
+    assert np.array_equal(val(out), exact), "forward combine not exact on this case"
+    return float(np.sum(val(out) * g))
+
+
+# ---------------------------------------------------------------- combine backward
+
+def test_grad_y_is_the_derivative_of_combine_brute_force():
+    T, H, E, R, k = 3, 4, 4, 2, 2
+    rng = np.random.default_rng(21)
+    pos, _ = layout(T, E, R, k, 22)
+    w = dyadic_weights(rng, T, k)
+    g_bits, g = ints_bf16(rng, (T, H), -4, 4)
+    y_any = wl.make_rows(T * k, H, 23)
+    grad_y, _ = oracle.combine_grad(g_bits, y_any, pos, w)
+    for s in range(T * k):
+        for h in range(H):
+            e = np.zeros((T * k, H), np.uint16)
+            e[s, h] = ONE
+            assert val(grad_y)[s, h] == loss_combine(e, pos, w, g), (s, h)
+
+
+def test_grad_w_is_the_exact_finite_difference():
+    T, H, E, R, k = 5, 6, 6, 3, 3
+    rng = np.random.default_rng(31)
+    pos, _ = layout(T, E, R, k, 32)
+    w = dyadic_weights(rng, T, k)
+    y_bits, _ = ints_bf16(rng, (T * k, H), -3, 3)
+    g_bits, g = ints_bf16(rng, (T, H), -3, 3)
+    _, grad_w = oracle.combine_grad(g_bits, y_bits, pos, w)
+    base = loss_combine(y_bits, pos, w, g)
+    for t in range(T):
+        for j in range(k):
+            w2 = w.copy()
+            w2[t, j] += np.float32(1.0)
+            assert grad_w[t, j] == loss_combine(y_bits, pos, w2, g) - base, (t, j)
+
+
+def test_combine_adjointness():
+    T, H, E, R, k = 64, 24, 16, 4, 4
+    rng = np.random.default_rng(41)
+    pos, _ = layout(T, E, R, k, 42)
+    w = dyadic_weights(rng, T, k, m=4)
+    y_bits, y = ints_bf16(rng, (T * k, H), -3, 3)
+    g_bits, g = ints_bf16(rng, (T, H), -3, 3)
+    grad_y, _ = oracle.combine_grad(g_bits, y_bits, pos, w)
+    assert loss_combine(y_bits, pos, w, g) == float(np.sum(y * val(grad_y)))
+
+
+def test_grad_y_rounding_vs_exact_rationals():
+    T, H, E, R, k = 16, 40, 32, 4, 8
+    pos, w = layout(T, E, R, k, 51)
+    g_bits = wl.make_rows(T, H, 52)
+    grad_y, _ = oracle.combine_grad(g_bits, wl.make_rows(T * k, H, 53), pos, w)
+    for t in range(T):
+        for j in range(k):
+            wq = Fraction(float(w[t, j]))
+            for h in range(H):
+                want = rne_bf16_exact(wq * bf16_exact(int(g_bits[t, h])))
+                assert grad_y[pos[t, j], h] == want, (t, j, h)
+
+
+def f32_tie_products(n, seed):
+    """(w f32, g bf16 bits) pairs whose exact product is NOT a bf16 tie but
+    whose f32 rounding IS one, on the side where ties-to-even goes the other
+    way: a product first rounded to f32 and then to bf16 comes out one bf16
+    step off on these."""
+    rng = np.random.default_rng(seed)
+    ws, gs = [], []
+    while len(ws) < n:
+        g_bits = int(wl.f32_to_bf16_bits(np.array([rng.uniform(1.0, 2.0)], np.float32))[0]) | 0x1
+        g = float(wl.bf16_bits_to_f32(np.array([g_bits], np.uint16))[0])
+        below = int(rng.integers(0x3F80, 0x4000))      # bf16 pattern in [1, 2)
+        target = float(np.array([(below << 16) | 0x8000], np.uint32).view(np.float32)[0])
+        w = np.float32(target / g)
+        exact = float(w) * g                           # exact: 24 x 8 bits
+        even_goes_down = below % 2 == 0
+        if float(np.float32(exact)) == target and (exact > target) == even_goes_down:
+            ws.append(w)
+            gs.append(g_bits)
+    return np.array(ws, np.float32), np.array(gs, np.uint16)
+
+
+def test_grad_y_rounds_the_exact_product_once():
+    w1, g1 = f32_tie_products(64, 61)
+    T, k, H = 64, 1, 8
+    pos = np.arange(T, dtype=np.int32).reshape(T, 1)
+    g_bits = np.tile(g1[:, None], (1, H))
+    grad_y, _ = oracle.combine_grad(g_bits, np.zeros((T, H), np.uint16), pos, w1[:, None])
+    for t in range(T):
+        want = rne_bf16_exact(Fraction(float(w1[t])) * bf16_exact(int(g1[t])))
+        assert grad_y[t, 0] == want
+        # and differs from the twice-rounded value
+        twice = int(wl.f32_to_bf16_bits(np.float32(float(w1[t]) * float(val(g1[t:t + 1])[0])))[0])
+        assert grad_y[t, 0] != twice
+
+
+def test_grad_w_vs_fsum_within_the_double_bound():
+    T, H, E, R, k = 8, 2048, 16, 4, 4
+    pos, w = layout(T, E, R, k, 71)
+    g_bits = wl.make_rows(T, H, 72)
+    y_bits = wl.make_rows(T * k, H, 73)
+    _, grad_w = oracle.combine_grad(g_bits, y_bits, pos, w)
+    g, y = val(g_bits), val(y_bits)
+    for t in range(T):
+        for j in range(k):
+            prods = g[t] * y[pos[t, j]]          # exact in double: 8 x 8 bits
+            ref = math.fsum(prods)
+            bound = H * 2.0 ** -53 * float(np.sum(np.abs(prods)))
+            assert abs(grad_w[t, j] - ref) <= bound, (t, j)
+
+
+def test_identity_experts_give_the_token_dot_product():
+    # y = dispatch(x): every pick of token t sees its own row, so all k
+    # weight gradients of the token are <g[t], x[t]>.
+    T, H, E, R, k = 32, 16, 8, 2, 4
+    rng = np.random.default_rng(81)
+    pos, w = layout(T, E, R, k, 82)
+    x_bits, x = ints_bf16(rng, (T, H), -5, 5)
+    g_bits, g = ints_bf16(rng, (T, H), -5, 5)
+    _, grad_w = oracle.combine_grad(g_bits, oracle.dispatch(x_bits, pos), pos, w)
+    np.testing.assert_array_equal(grad_w, np.repeat(np.sum(g * x, axis=1)[:, None], k, axis=1))
+
+
+def test_top1_unit_weight_grad_y_is_a_scatter_of_grad_out():
+    T, H, E, R = 20, 24, 4, 2
+    pos, _ = layout(T, E, R, 1, 91)
+    g_bits = wl.make_rows(T, H, 92)
+    grad_y, _ = oracle.combine_grad(g_bits, wl.make_rows(T, H, 93), pos,
+                                    np.ones((T, 1), np.float32))
+    np.testing.assert_array_equal(grad_y[pos[:, 0]], g_bits)
+
+
+# ---------------------------------------------------------------- dispatch backward
+
+def test_grad_x_is_the_derivative_of_dispatch_brute_force():
+    T, H, E, R, k = 3, 4, 4, 2, 2
+    rng = np.random.default_rng(101)
+    pos, _ = layout(T, E, R, k, 102)
+    G_bits, G = ints_bf16(rng, (T * k, H), -4, 4)
+    grad_x = oracle.dispatch_grad(G_bits, pos)
+    for t in range(T):
+        for h in range(H):
+            e = np.zeros((T, H), np.uint16)
+            e[t, h] = ONE
+            assert val(grad_x)[t, h] == float(np.sum(val(oracle.dispatch(e, pos)) * G))
+
+
+def test_dispatch_adjointness():
+    T, H, E, R, k = 64, 24, 16, 4, 6
+    rng = np.random.default_rng(111)
+    pos, _ = layout(T, E, R, k, 112)
+    x_bits, x = ints_bf16(rng, (T, H), -3, 3)
+    G_bits, G = ints_bf16(rng, (T * k, H), -3, 3)
+    lhs = float(np.sum(val(oracle.dispatch(x_bits, pos)) * G))
+    assert lhs == float(np.sum(x * val(oracle.dispatch_grad(G_bits, pos))))
+
+
+@pytest.mark.parametrize("k", [1, 2, 4, 8])
+def test_dispatch_grad_of_dispatch_is_k_times_x(k):
+    # k a power of two: k * x is exact in bf16 (an exponent shift)
+    T, H, E, R = 24, 32, 16, 4
+    pos, _ = layout(T, E, R, k, 120 + k)
+    x_bits = wl.make_rows(T, H, 130 + k)
+    got = oracle.dispatch_grad(oracle.dispatch(x_bits, pos), pos)
+    np.testing.assert_array_equal(val(got), k * val(x_bits))
+
+
+def test_dispatch_grad_is_a_unit_weight_combine():
+    # both round the same double sum once (generic values, k = 8)
+    T, H, E, R, k = 40, 56, 32, 8, 8
+    pos, _ = layout(T, E, R, k, 141)
+    G_bits = wl.make_rows(T * k, H, 142)
+    np.testing.assert_array_equal(oracle.dispatch_grad(G_bits, pos),
+                                  oracle.combine(G_bits, pos, np.ones((T, k), np.float32)))
+
+
+def test_backward_rejects_rows_outside_the_buffer():
+    pos = np.array([[0, 1], [2, 4]], np.int32)
+    rows = np.zeros((4, 8), np.uint16)
+    with pytest.raises(ValueError):
+        oracle.dispatch_grad(rows, pos)
+    with pytest.raises(ValueError):
+        oracle.combine_grad(np.zeros((2, 8), np.uint16), rows, pos,
+                            np.ones((2, 2), np.float32))
