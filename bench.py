@@ -5,7 +5,8 @@ is already resident in HBM: route (top-k gating) -> dispatch layout ->
 dispatch -> combine, on the DeepSeek-V3-like workload (T=4096 tokens,
 H=7168 bf16, E=256 experts over R=32 virtual ranks, top-8) -- one EP rank's
 share of the EP=32, 4096-token, H=7168, top-8 dispatch/combine benchmark.
-The fused flag-in-payload mode is timed beside it on the same inputs.
+The fused flag-in-payload mode and the backward pass (combine_grad ->
+dispatch_grad) are timed beside it on the same inputs.
 
 Prints ONE JSON line.  `value` = algorithmic HBM bytes of a whole step /
 step time (GB/s); tokens/s and the fraction of the 8 TB/s HBM peak ride along.
@@ -42,6 +43,7 @@ def parse():
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-isolated", action="store_true",
                     help="skip the per-op timings after a cache-clearing overwrite")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -140,13 +142,7 @@ def main():
            ep.bind_combine(send, lay["pos"], wt, out, stream)]
     set_events = ep.library().ep_set_timing_events
 
-    def step(stops=None, first_start=None):
-        # stops[i]: hipEvent_t recorded by op i's own last kernel (library
-        # timing hook); only the region's very first op also records a start.
-        for i, op in enumerate(ops):
-            if stops is not None:
-                set_events(first_start if i == 0 else None, stops[i])
-            op()
+    step = make_step(ops, set_events)
 
     # correctness gate before timing: the identity-expert round trip is exact
     step()
@@ -163,28 +159,8 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    stops = [[hip.create() for _ in range(4)] for _ in range(K)]
-    region_start = hip.create()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(stops[i], region_start if i == 0 else None)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # op i of step s spans from the end of the op before it (back-to-back
-    # kernels on one stream) to the end of its own last kernel
     names = ["route", "layout", "dispatch", "combine"]
-    per_op = {n: [] for n in names}
-    prev = region_start
-    for s_ev in stops:
-        for j, n in enumerate(names):
-            per_op[n].append(hip.elapsed_ms(prev, s_ev[j]) * 1e3)     # us
-            prev = s_ev[j]
-    for s_ev in stops:
-        for e in s_ev:
-            hip.destroy(e)
-    hip.destroy(region_start)
+    per_op, wall = time_steps(torch, hip, step, names, K)
     mean_us = {n: float(np.mean(v)) for n, v in per_op.items()}
     p10_us = {n: float(np.percentile(v, 10)) for n, v in per_op.items()}
     p90_us = {n: float(np.percentile(v, 90)) for n, v in per_op.items()}
@@ -244,10 +220,94 @@ def main():
     if not args.no_fused:
         result["fused"] = bench_fused(ep, torch, w, x, idx, wt, stream, K, args.warmup)
 
+    if not args.no_backward:
+        result["backward"] = bench_backward(ep, torch, hip, set_events, w, x, lay, wt, send,
+                                            dev, stream, K, args.warmup, not args.no_isolated)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, lay, args.cpu_seconds, step_bytes)
 
     print(json.dumps(result), flush=True)
+
+
+def make_step(ops, set_events):
+    def step(stops=None, first_start=None):
+        # stops[i]: hipEvent_t recorded by op i's own last kernel (library
+        # timing hook); only the region's very first op also records a start.
+        for i, op in enumerate(ops):
+            if stops is not None:
+                set_events(first_start if i == 0 else None, stops[i])
+            op()
+    return step
+
+
+def time_steps(torch, hip, step, names, K):
+    """K timed steps; returns (per-op durations in us, wall seconds).  Op i of
+    step s spans from the end of the op before it (back-to-back kernels on one
+    stream) to the end of its own last kernel."""
+    stops = [[hip.create() for _ in names] for _ in range(K)]
+    region_start = hip.create()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(stops[i], region_start if i == 0 else None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_op = {n: [] for n in names}
+    prev = region_start
+    for s_ev in stops:
+        for j, n in enumerate(names):
+            per_op[n].append(hip.elapsed_ms(prev, s_ev[j]) * 1e3)
+            prev = s_ev[j]
+    for s_ev in stops:
+        for e in s_ev:
+            hip.destroy(e)
+    hip.destroy(region_start)
+    return per_op, wall
+
+
+def bench_backward(ep, torch, hip, set_events, w, x, lay, wt, send, dev, stream, K, W,
+                   isolated):
+    """The backward pass (HyperParallel-MoE sec. 2.2, Fig. 2(b)) on the same
+    workload with identity experts: combine_grad(grad_out = x, y = send) then
+    dispatch_grad(grad_send = grad_y), back to back on one stream."""
+    from combine_ep_route_topk_amd import workloads as wl
+    T, H, k = w.T, w.H, w.k
+    grad_y = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    grad_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    grad_x = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ops = [ep.bind_combine_grad(x, send, lay["pos"], wt, grad_y, grad_w, stream),
+           ep.bind_dispatch_grad(grad_y, lay["pos"], grad_x, stream)]
+    names = ["combine_grad", "dispatch_grad"]
+    step = make_step(ops, set_events)
+    step()
+    torch.cuda.synchronize()
+    # gate: identity experts give every pick of a token the same <x_t, x_t>
+    if not torch.equal(grad_w, grad_w[:, :1].expand(T, k)):
+        return {"status": "parity gate failed: grad_w differs across the picks of a token"}
+    ref = x.float().pow(2).sum(dim=1)
+    if not torch.allclose(grad_w[:, 0], ref, rtol=1e-4, atol=0.0):
+        return {"status": "parity gate failed: grad_w != <x_t, x_t>"}
+    for _ in range(W):
+        step()
+    per_op, wall = time_steps(torch, hip, step, names, K)
+    ab = wl.algorithmic_bytes_backward(w)
+    res = {}
+    for n in names:
+        us = float(np.mean(per_op[n]))
+        p10, p90 = np.percentile(per_op[n], [10, 90])
+        res[n] = {"us": round(us, 2), "gbps": round(ab[n] / (us * 1e-6) / 1e9, 1),
+                  "pct_of_peak": round(100 * ab[n] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+                  "p90_over_p10": round(float(p90 / p10), 3),
+                  "algorithmic_bytes": ab[n]}
+    us_step = wall / K * 1e6
+    res["us_per_step"] = round(us_step, 2)
+    res["gbps_per_step"] = round(sum(ab.values()) / (us_step * 1e-6) / 1e9, 1)
+    if isolated:
+        res["isolated"] = bench_isolated(ep, torch, hip, ops, names, set_events, dev, stream)
+    res["what"] = "combine_grad -> dispatch_grad, identity experts, back to back"
+    del grad_y, grad_w, grad_x
+    return res
 
 
 def bench_isolated(ep, torch, hip, ops, names, set_events, dev, stream, reps=30):

@@ -198,6 +198,38 @@ ep_status ep_combine(const uint16_t* y, const int32_t* pos, const float* topk_w,
                     fn);
 }
 
+ep_status ep_combine_grad(const uint16_t* grad_out, const uint16_t* y, const int32_t* pos,
+                          const float* topk_w, int32_t T, int32_t H, int32_t k,
+                          uint16_t* grad_y, float* grad_w, void* stream)
+{
+    const char* fn = "ep_combine_grad";
+    TimingScope timing_scope;
+    EP_TRY(check_rows(fn, T, H, k));
+    EP_REQUIRE_PTR(fn, grad_out, 16);
+    EP_REQUIRE_PTR(fn, y, 16);
+    EP_REQUIRE_PTR(fn, pos, 4);
+    EP_REQUIRE_PTR(fn, topk_w, 4);
+    EP_REQUIRE_PTR(fn, grad_y, 16);
+    EP_REQUIRE_PTR(fn, grad_w, 4);
+    return launched(ep::launch_combine_grad(grad_out, y, pos, topk_w, T, H, k, grad_y, grad_w,
+                                            static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+ep_status ep_dispatch_grad(const uint16_t* grad_send, const int32_t* pos, int32_t T,
+                           int32_t H, int32_t k, uint16_t* grad_x, void* stream)
+{
+    const char* fn = "ep_dispatch_grad";
+    TimingScope timing_scope;
+    EP_TRY(check_rows(fn, T, H, k));
+    EP_REQUIRE_PTR(fn, grad_send, 16);
+    EP_REQUIRE_PTR(fn, pos, 4);
+    EP_REQUIRE_PTR(fn, grad_x, 16);
+    return launched(ep::launch_dispatch_grad(grad_send, pos, T, H, k, grad_x,
+                                             static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 size_t ep_fused_row_stride_bytes(int32_t H)
 {
     if (H < 8 || H % 8 != 0) return 0;

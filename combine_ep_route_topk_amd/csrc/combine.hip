@@ -19,6 +19,11 @@
 // dispatch 111 -> 95 us).  The output rows are stored streaming and
 // agent-coherent, through a descriptor over the token's row, so they do not
 // stay dirty in the L2 for the next kernel to flush.
+//
+// The same kernel with every weight 1 is the backward of dispatch
+// (HyperParallel-MoE sec. 2.2, Fig. 2(b): the backward Combine returns the
+// input activations' gradient): x[t] went to every row pos[t][j], so
+// grad_x[t] = bf16( sum_j grad_send[pos[t][j]] ), same order and rounding.
 #include "ep_combine_dev.h"
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -45,8 +50,9 @@ __device__ __forceinline__ void load_pick(u32x4 (&r)[U], const char* __restrict_
 
 // A (token, segment) item whose vectors all lie inside the row.  KC > 0: the
 // pick count is the compile-time KC, so all KC*U loads of a lane are issued
-// before the first FMA; KC == 0: runtime k, one pick at a time.
-template <int U, int KC>
+// before the first FMA; KC == 0: runtime k, one pick at a time.  UW: every
+// weight is 1 and wrow is not read.
+template <int U, int KC, bool UW>
 __device__ __forceinline__ void combine_whole(const char* __restrict__ y,
                                               const int32_t* __restrict__ prow,
                                               const float* __restrict__ wrow, int k,
@@ -59,23 +65,25 @@ __device__ __forceinline__ void combine_whole(const char* __restrict__ y,
 #pragma unroll
         for (int j = 0; j < KC; ++j) load_pick<U>(r[j], y, prow[j], S, row_bytes, lane_off);
 #pragma unroll
-        for (int j = 0; j < KC; ++j) accumulate<U>(acc, r[j], wrow[j], j == 0);
+        for (int j = 0; j < KC; ++j) accumulate<U>(acc, r[j], UW ? 1.0f : wrow[j], j == 0);
     } else {
         {
             u32x4 r[U];
             load_pick<U>(r, y, prow[0], S, row_bytes, lane_off);
-            accumulate<U>(acc, r, wrow[0], true);
+            accumulate<U>(acc, r, UW ? 1.0f : wrow[0], true);
         }
         for (int j = 1; j < k; ++j) {
             u32x4 r[U];
             load_pick<U>(r, y, prow[j], S, row_bytes, lane_off);
-            accumulate<U>(acc, r, wrow[j], false);
+            accumulate<U>(acc, r, UW ? 1.0f : wrow[j], false);
         }
     }
     store_acc_coherent<U>(buffer_rsrc(dst, row_bytes), lane_off, acc);
 }
 
-// The last, partial segment of a row: one vector at a time.
+// The last, partial segment of a row: one vector at a time.  UW: every
+// weight is 1 and wrow is not read.
+template <bool UW>
 __device__ __noinline__ void combine_tail(const char* __restrict__ y,
                                           const int32_t* __restrict__ prow,
                                           const float* __restrict__ wrow, int k, uint32_t S,
@@ -90,7 +98,7 @@ __device__ __noinline__ void combine_tail(const char* __restrict__ y,
         for (int j = 0; j < k; ++j) {
             u32x4 r[1];
             load_pick<1>(r, y, prow[j], S, row_bytes, off);
-            accumulate<1>(acc, r, wrow[j], j == 0);
+            accumulate<1>(acc, r, UW ? 1.0f : wrow[j], j == 0);
         }
         store_acc<1>(dst + off, acc);
     }
@@ -102,7 +110,7 @@ __device__ __noinline__ void combine_tail(const char* __restrict__ y,
 // (measured on MI355X at T=4096, H=7168, k=8: about 4 us less than
 // token-fastest order).  A 1-D grid strides over the items, so any T fits the
 // launch limits.
-template <int U, int KC>
+template <int U, int KC, bool UW>
 __global__ __launch_bounds__(kBlock) void combine_kernel(
     const uint16_t* __restrict__ y, const int32_t* __restrict__ pos,
     const float* __restrict__ w, int T, int nvec, int k,
@@ -118,17 +126,17 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(
         const int t = int(group) * kWavesPerBlock + wave;
         if (t >= T) continue;
         const int32_t* prow = pos + int64_t(t) * k;
-        const float* wrow = w + int64_t(t) * k;
+        const float* wrow = UW ? nullptr : w + int64_t(t) * k;
         char* dst = reinterpret_cast<char*>(out) + int64_t(t) * row_bytes;
         const int v0 = seg * kWave * U + lane_id();
         if ((seg + 1) * kWave * U <= nvec)
-            combine_whole<U, KC>(yb, prow, wrow, k, S, row_bytes, uint32_t(v0) * 16u, dst);
+            combine_whole<U, KC, UW>(yb, prow, wrow, k, S, row_bytes, uint32_t(v0) * 16u, dst);
         else
-            combine_tail(yb, prow, wrow, k, S, row_bytes, v0, U, nvec, dst);
+            combine_tail<UW>(yb, prow, wrow, k, S, row_bytes, v0, U, nvec, dst);
     }
 }
 
-template <int U>
+template <int U, bool UW>
 hipError_t launch_u(const uint16_t* y, const int32_t* pos, const float* w, int T,
                     int nvec, int k, uint16_t* out, hipStream_t s)
 {
@@ -136,10 +144,10 @@ hipError_t launch_u(const uint16_t* y, const int32_t* pos, const float* w, int T
     const uint32_t items = uint32_t((T + kWavesPerBlock - 1) / kWavesPerBlock) * segs;
     const uint32_t grid = items < kMaxGrid ? items : kMaxGrid;
     if (k == 8)
-        EP_LAUNCH((combine_kernel<U, 8>), dim3(grid), dim3(kBlock), 0, s,
+        EP_LAUNCH((combine_kernel<U, 8, UW>), dim3(grid), dim3(kBlock), 0, s,
                   y, pos, w, T, nvec, k, out, segs, items);
     else
-        EP_LAUNCH((combine_kernel<U, 0>), dim3(grid), dim3(kBlock), 0, s,
+        EP_LAUNCH((combine_kernel<U, 0, UW>), dim3(grid), dim3(kBlock), 0, s,
                   y, pos, w, T, nvec, k, out, segs, items);
     return hipGetLastError();
 }
@@ -151,7 +159,13 @@ hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w,
 {
     // One vector per lane and pick: more, smaller items keep more waves
     // resident than two (measured at H=7168: about 1 us faster).
-    return launch_u<1>(y, pos, w, T, H / 8, k, out, s);
+    return launch_u<1, false>(y, pos, w, T, H / 8, k, out, s);
+}
+
+hipError_t launch_dispatch_grad(const uint16_t* grad_send, const int32_t* pos, int T, int H,
+                                int k, uint16_t* grad_x, hipStream_t s)
+{
+    return launch_u<1, true>(grad_send, pos, nullptr, T, H / 8, k, grad_x, s);
 }
 
 }  // namespace ep

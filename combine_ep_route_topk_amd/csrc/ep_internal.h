@@ -156,6 +156,13 @@ hipError_t launch_dispatch(const uint16_t* x, int T, int H, int k, const int32_t
 hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w,
                           int T, int H, int k, uint16_t* out, hipStream_t s);
 
+hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* y,
+                               const int32_t* pos, const float* w, int T, int H, int k,
+                               uint16_t* grad_y, float* grad_w, hipStream_t s);
+
+hipError_t launch_dispatch_grad(const uint16_t* grad_send, const int32_t* pos, int T, int H,
+                                int k, uint16_t* grad_x, hipStream_t s);
+
 hipError_t launch_fused_init(void* ws, uint64_t first_epoch, hipStream_t s);
 
 hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float* topk_w,

@@ -41,6 +41,8 @@ _SIGS = {
                            ctypes.c_int),
     "ep_dispatch": ([_P, _i32, _i32, _i32, _P, _P, _P], ctypes.c_int),
     "ep_combine": ([_P, _P, _P, _i32, _i32, _i32, _P, _P], ctypes.c_int),
+    "ep_combine_grad": ([_P, _P, _P, _P, _i32, _i32, _i32, _P, _P, _P], ctypes.c_int),
+    "ep_dispatch_grad": ([_P, _P, _i32, _i32, _i32, _P, _P], ctypes.c_int),
     "ep_fused_row_stride_bytes": ([_i32], _sz),
     "ep_fused_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
     "ep_fused_workspace_init": ([_P, _sz, _P], ctypes.c_int),
@@ -204,6 +206,48 @@ def ep_combine(y: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor,
     return out
 
 
+# ------------------------------------------------------------------- backward
+def ep_combine_grad(grad_out: torch.Tensor, y: torch.Tensor, pos: torch.Tensor,
+                    topk_w: torch.Tensor, grad_y: torch.Tensor | None = None,
+                    grad_w: torch.Tensor | None = None, stream=None):
+    """grad_out bf16 [T][H], y bf16 [T*k][H], pos i32 [T][k], topk_w f32 [T][k]
+    -> (grad_y bf16 [T*k][H], grad_w f32 [T][k])."""
+    _need(pos, "pos", torch.int32)
+    T, k = pos.shape
+    _bits_ok(grad_out, "grad_out")
+    H = grad_out.shape[1]
+    if grad_out.shape[0] != T:
+        raise ValueError("grad_out must be [T][H]")
+    _bits_ok(y, "y", (T * k, H))
+    _need(topk_w, "topk_w", torch.float32, (T, k))
+    if grad_y is None:
+        grad_y = torch.empty((T * k, H), dtype=y.dtype, device=y.device)
+    if grad_w is None:
+        grad_w = torch.empty((T, k), dtype=torch.float32, device=y.device)
+    _bits_ok(grad_y, "grad_y", (T * k, H))
+    _need(grad_w, "grad_w", torch.float32, (T, k))
+    _check(_lib.ep_combine_grad(_ptr(grad_out), _ptr(y), _ptr(pos), _ptr(topk_w), T, H, k,
+                                _ptr(grad_y), _ptr(grad_w), _P(_stream(stream, y.device))))
+    return grad_y, grad_w
+
+
+def ep_dispatch_grad(grad_send: torch.Tensor, pos: torch.Tensor,
+                     grad_x: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """grad_send bf16 [T*k][H], pos i32 [T][k] -> grad_x bf16 [T][H]."""
+    _need(pos, "pos", torch.int32)
+    T, k = pos.shape
+    _bits_ok(grad_send, "grad_send")
+    H = grad_send.shape[1]
+    if grad_send.shape[0] != T * k:
+        raise ValueError("grad_send must have T*k rows")
+    if grad_x is None:
+        grad_x = torch.empty((T, H), dtype=grad_send.dtype, device=grad_send.device)
+    _bits_ok(grad_x, "grad_x", (T, H))
+    _check(_lib.ep_dispatch_grad(_ptr(grad_send), _ptr(pos), T, H, k, _ptr(grad_x),
+                                 _P(_stream(stream, grad_send.device))))
+    return grad_x
+
+
 # ------------------------------------------------------------------- fused
 def ep_fused_row_stride_bytes(H: int) -> int:
     return int(_lib.ep_fused_row_stride_bytes(H))
@@ -333,6 +377,37 @@ def bind_combine(y, pos, topk_w, out, stream) -> BoundCall:
                      (_ptr(y), _ptr(pos), _ptr(topk_w), T, H, k, _ptr(out),
                       _P(_stream(stream, y.device))),
                      (y, pos, topk_w, out, stream))
+
+
+def bind_combine_grad(grad_out, y, pos, topk_w, grad_y, grad_w, stream) -> BoundCall:
+    _need(pos, "pos", torch.int32)
+    T, k = pos.shape
+    _bits_ok(grad_out, "grad_out")
+    H = grad_out.shape[1]
+    if grad_out.shape[0] != T:
+        raise ValueError("grad_out must be [T][H]")
+    _bits_ok(y, "y", (T * k, H))
+    _need(topk_w, "topk_w", torch.float32, (T, k))
+    _bits_ok(grad_y, "grad_y", (T * k, H))
+    _need(grad_w, "grad_w", torch.float32, (T, k))
+    return BoundCall(_lib.ep_combine_grad,
+                     (_ptr(grad_out), _ptr(y), _ptr(pos), _ptr(topk_w), T, H, k, _ptr(grad_y),
+                      _ptr(grad_w), _P(_stream(stream, y.device))),
+                     (grad_out, y, pos, topk_w, grad_y, grad_w, stream))
+
+
+def bind_dispatch_grad(grad_send, pos, grad_x, stream) -> BoundCall:
+    _need(pos, "pos", torch.int32)
+    T, k = pos.shape
+    _bits_ok(grad_send, "grad_send")
+    H = grad_send.shape[1]
+    if grad_send.shape[0] != T * k:
+        raise ValueError("grad_send must have T*k rows")
+    _bits_ok(grad_x, "grad_x", (T, H))
+    return BoundCall(_lib.ep_dispatch_grad,
+                     (_ptr(grad_send), _ptr(pos), T, H, k, _ptr(grad_x),
+                      _P(_stream(stream, grad_send.device))),
+                     (grad_send, pos, grad_x, stream))
 
 
 def ep_set_timing_events(start_event, stop_event) -> None:

@@ -150,3 +150,17 @@ def algorithmic_bytes(w: Workload) -> dict:
         "layout": T * (12 * k) + 4 * (2 * E + 1) + 4 * (2 * R + 1),
     }
 
+
+
+def algorithmic_bytes_backward(w: Workload) -> dict:
+    """Bytes the backward pass must move per call, per op.
+
+    combine_grad : read grad_out (2H per token) + k rows of y (2Hk) + pos and
+                   weights (8k), write k gradient rows (2Hk) + grad_w (4k)
+    dispatch_grad: read k rows (2Hk) + pos (4k), write grad_x (2H)
+    """
+    T, H, k = w.T, w.H, w.k
+    return {
+        "combine_grad": T * (2 * H * (1 + 2 * k) + 12 * k),
+        "dispatch_grad": T * (2 * H * (k + 1) + 4 * k),
+    }

@@ -71,7 +71,7 @@ const char* ep_last_error(void);
  * RailWave's execution protocol times each run with GPU events around the
  * device work only).  After this call, the NEXT compute entry point called on
  * the same thread (ep_route_topk, ep_dispatch_layout, ep_dispatch, ep_combine,
- * ep_fused_dispatch_combine) records `start_event` when its first kernel
+ * ep_combine_grad, ep_dispatch_grad, ep_fused_dispatch_combine) records `start_event` when its first kernel
  * starts and `stop_event` when its last kernel ends, taken from the kernels'
  * own dispatch packets -- the same interval a kernel-trace profiler reports,
  * with no marker packet in between.  Either event may be NULL.  The hook then
@@ -156,6 +156,42 @@ ep_status ep_dispatch(const uint16_t* x, int32_t T, int32_t H, int32_t k,
  * ------------------------------------------------------------------------- */
 ep_status ep_combine(const uint16_t* y, const int32_t* pos, const float* topk_w,
                      int32_t T, int32_t H, int32_t k, uint16_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Backward of combine.  [HPMOE sec. 2.2, Fig. 2(b)] the backward graph's
+ * Dispatch is the gradient of the forward Combine.  For the forward
+ * out[t] = sum_j topk_w[t][j] * y[pos[t][j]] (ep_combine):
+ *   grad_out bf16 [T][H]    gradient of out.
+ *   y        bf16 [T*k][H]  the forward's expert outputs (send order).
+ *   pos      i32  [T][k]    rows from ep_dispatch_layout; a permutation of
+ *                           [0, T*k).
+ *   topk_w   f32  [T][k]    routing weights.
+ *   grad_y   bf16 [T*k][H]  out: grad_y[pos[t][j]] = bf16( topk_w[t][j] *
+ *                           grad_out[t] ), the exact product rounded once
+ *                           (nearest even) for products in the normal f32
+ *                           range.
+ *   grad_w   f32  [T][k]    out: sum_h grad_out[t][h] * y[pos[t][j]][h],
+ *                           accumulated in f32 in an order fixed by H alone
+ *                           (the same result on every call).
+ * A pos entry outside [0, T*k) gets grad_w = 0 and writes no grad_y row.
+ * ------------------------------------------------------------------------- */
+ep_status ep_combine_grad(const uint16_t* grad_out, const uint16_t* y, const int32_t* pos,
+                          const float* topk_w, int32_t T, int32_t H, int32_t k,
+                          uint16_t* grad_y, float* grad_w, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Backward of dispatch.  [HPMOE sec. 2.2, Fig. 2(b)] the backward graph's
+ * Combine returns the gradient of the input activations.  ep_dispatch copied
+ * x[t] to every row pos[t][j], so
+ *   grad_send bf16 [T*k][H]  gradient of the send buffer.
+ *   pos       i32  [T][k]    rows from ep_dispatch_layout.
+ *   grad_x    bf16 [T][H]    out: bf16( sum_j grad_send[pos[t][j]] ), summed
+ *                            in f32 in the order j = 0..k-1 and rounded once
+ *                            (nearest even) -- ep_combine with unit weights.
+ * pos entries outside [0, T*k) contribute nothing.
+ * ------------------------------------------------------------------------- */
+ep_status ep_dispatch_grad(const uint16_t* grad_send, const int32_t* pos, int32_t T,
+                           int32_t H, int32_t k, uint16_t* grad_x, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Fused flag-in-payload mode: layout + dispatch + combine with identity

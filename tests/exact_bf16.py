@@ -5,6 +5,10 @@ check that shares nothing with the oracle's own C rounding."""
 import math
 from fractions import Fraction
 
+import numpy as np
+
+from combine_ep_route_topk_amd import workloads as wl
+
 
 def bf16_exact(b):
     """Exact value of a finite bf16 pattern as a Fraction, from the format."""
@@ -43,3 +47,33 @@ def rne_bf16_exact(v: Fraction, negative_zero=False):
     e2 = e if r < Fraction(2) ** (e + 1) else e + 1
     frac = int((r / Fraction(2) ** e2 - 1) * 128)
     return sign | ((e2 + 127) << 7) | frac
+
+
+def f32_tie_products(n, seed):
+    """(w f32, g bf16 bits) pairs whose exact product is NOT a bf16 tie but
+    whose f32 rounding IS one, on the side where ties-to-even goes the other
+    way: a product first rounded to f32 and then to bf16 comes out one bf16
+    step off on these."""
+    rng = np.random.default_rng(seed)
+    ws, gs = [], []
+    while len(ws) < n:
+        g_bits = int(wl.f32_to_bf16_bits(np.array([rng.uniform(1.0, 2.0)], np.float32))[0]) | 0x1
+        g = float(wl.bf16_bits_to_f32(np.array([g_bits], np.uint16))[0])
+        below = int(rng.integers(0x3F80, 0x4000))      # bf16 pattern in [1, 2)
+        target = float(np.array([(below << 16) | 0x8000], np.uint32).view(np.float32)[0])
+        w = np.float32(target / g)
+        exact = float(w) * g                           # exact: 24 x 8 bits
+        even_goes_down = below % 2 == 0
+        if float(np.float32(exact)) == target and (exact > target) == even_goes_down:
+            ws.append(w)
+            gs.append(g_bits)
+    return np.array(ws, np.float32), np.array(gs, np.uint16)
+
+
+def plant_tie_products(w, g_bits, tokens, seed):
+    """Puts one f32_tie_products pair at pick 0, column 0 of each listed token:
+    w[t][0] and g[t][0] change in place."""
+    ws, gs = f32_tie_products(len(tokens), seed)
+    for i, t in enumerate(tokens):
+        w[t, 0] = ws[i]
+        g_bits[t, 0] = gs[i]

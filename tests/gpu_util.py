@@ -88,6 +88,33 @@ def check_combine(out_gpu_bits, ref_bits, y_bits, pos, w, chunk=256):
     return n_exact / out_gpu_bits.size
 
 
+# Weight gradient of the backward combine.  grad_w[t][j] is a dot product of
+# two bf16 rows over H: every product is exact in f32, so the error is that of
+# the f32 additions.  The kernel adds 8 products per 16-byte vector into a
+# per-lane sum over the lane's vectors (at most 8 * ceil(H / 2048) + 8 terms
+# for 4 waves of 64 lanes), then 6 butterfly steps and 3 cross-wave adds; any
+# summation tree of depth n has |err| <= g_n * sum_h |g_h y_h| with
+# g_n = n u / (1 - n u).  n = ceil(H / 64) + 24 bounds that depth for every H,
+# and the oracle's own double sum adds at most H * 2^-53 * sum|g y|.
+def check_grad_w(gw_gpu, gw_ref, g_bits, y_bits, pos, chunk=256):
+    T, k = pos.shape
+    H = g_bits.shape[1]
+    n = -(-H // 64) + 24
+    gam = n * 2.0 ** -24 / (1 - n * 2.0 ** -24) + H * 2.0 ** -53
+    worst = 0.0
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        G = np.abs(wl.bf16_bits_to_f32(g_bits[t0:t1]).astype(np.float64))
+        Y = np.abs(wl.bf16_bits_to_f32(y_bits[pos[t0:t1].reshape(-1)]).astype(np.float64))
+        mag = np.einsum("th,tkh->tk", G, Y.reshape(t1 - t0, k, H))
+        err = np.abs(gw_gpu[t0:t1].astype(np.float64) - gw_ref[t0:t1])
+        bad = err > gam * mag
+        assert not bad.any(), (f"{bad.sum()} weight gradients outside the derived bound; "
+                               f"worst {np.max(err / np.maximum(mag, 1e-300)):.3g} x sum|g y|")
+        worst = max(worst, float(np.max(err / np.maximum(mag, 1e-300))))
+    return worst
+
+
 # ----------------------------------------------------------------- oracle chain
 class Case:
     """Inputs of one workload plus the oracle's route / layout / dispatch."""

@@ -199,3 +199,40 @@ def test_emulated_bounded_waits_and_bad_ids(emu):
     assert st == 5 and m.flay["pos"][7, 1] == -1
     _, st = m.fused(x, o_idx, o_w)
     assert st == 0
+
+
+BACKWARD_SHAPES = [
+    # T, H, E, R, k, seed
+    (5, 16, 4, 2, 2, 21),
+    (40, 7176, 64, 8, 8, 22),     # ragged last segment, k = 8 path
+    (33, 520, 16, 4, 3, 23),      # runtime-k path
+    (7, 8, 4, 2, 1, 24),          # one vector per row
+]
+
+
+@pytest.mark.parametrize("T,H,E,R,k,seed", BACKWARD_SHAPES)
+def test_emulated_backward_matches_oracle(emu, T, H, E, R, k, seed):
+    """Backward of combine and of dispatch (HyperParallel-MoE sec. 2.2,
+    Fig. 2(b)) on the emulated kernels against the oracle."""
+    import gpu_util as gu
+    from exact_bf16 import plant_tie_products
+    rng = np.random.default_rng(seed)
+    o_idx, o_w = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
+    pos = oracle.dispatch_layout(o_idx, E, R)["pos"]
+    g = aligned(T * H * 2, 16).view(np.uint16).reshape(T, H)
+    g[:] = wl.make_rows(T, H, seed + 100)
+    plant_tie_products(o_w, g, range(0, T, 2), seed)   # f32 product on a bf16 tie
+    y = aligned(T * k * H * 2, 16).view(np.uint16).reshape(T * k, H)
+    y[:] = wl.make_rows(T * k, H, seed + 200)
+    gy = aligned(T * k * H * 2, 16).view(np.uint16).reshape(T * k, H)
+    gw = np.zeros((T, k), np.float32)
+    rc = emu.ep_combine_grad(p(g), p(y), p(pos), p(o_w), T, H, k, p(gy), p(gw), None)
+    assert rc == 0, emu.ep_last_error().decode()
+    r_gy, r_gw = oracle.combine_grad(g, y, pos, o_w)
+    assert np.array_equal(gy, r_gy), "grad_y"
+    gu.check_grad_w(gw, r_gw, g, y, pos)
+
+    gx = aligned(T * H * 2, 16).view(np.uint16).reshape(T, H)
+    rc = emu.ep_dispatch_grad(p(y), p(pos), T, H, k, p(gx), None)
+    assert rc == 0, emu.ep_last_error().decode()
+    gu.check_combine(gx, oracle.dispatch_grad(y, pos), y, pos, np.ones((T, k), np.float32))

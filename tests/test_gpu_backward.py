@@ -1,0 +1,151 @@
+"""GPU parity of the backward pass against the CPU oracle.
+
+HyperParallel-MoE sec. 2.2, Fig. 2(b): the backward Dispatch is the gradient
+of the forward Combine (ep_combine_grad: grad_y and grad_w), the backward
+Combine returns the input activations' gradient (ep_dispatch_grad).
+
+Bars: grad_y bit-exact (the exact product rounded once, also where the f32
+product sits on a bf16 tie -- planted in every other token); grad_w within the
+derived dot-product bound (gpu_util.check_grad_w) and the same bits on a second
+call; grad_x within the combine bound with unit weights.  Full workload sizes
+use the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_ep_route_topk_amd import workloads as wl
+from exact_bf16 import plant_tie_products
+
+from gpu_util import DEV, bits, check_combine, check_grad_w, poison_bits, say, to_dev_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def epm():
+    from combine_ep_route_topk_amd import ep as mod
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return mod
+
+
+def backward_inputs(T, H, E, R, k, seed, logits=None):
+    """pos and weights from the oracle's route + layout; grad_out, expert
+    outputs and send-buffer gradients ~ N(0, 1) in bf16; f32-tie products
+    planted at pick 0, column 0 of every other token."""
+    rng = np.random.default_rng(seed)
+    if logits is None:
+        logits = rng.standard_normal((T, E), dtype=np.float32)
+    idx, w = oracle.route_topk(logits, k, 1)
+    pos = oracle.dispatch_layout(idx, E, R)["pos"]
+    g = wl.make_rows(T, H, seed + 1)
+    plant_tie_products(w, g, range(0, T, 2), seed + 2)
+    y = wl.make_rows(T * k, H, seed + 3)
+    return pos, w, g, y
+
+
+def run_and_check(epm, pos, w, g, y, label):
+    T, k = pos.shape
+    H = g.shape[1]
+    say(f"combine_grad {label}")
+    d_pos = torch.from_numpy(pos).to(DEV)
+    d_w = torch.from_numpy(w).to(DEV)
+    d_g, d_y = to_dev_bits(g), to_dev_bits(y)
+    gy = poison_bits((T * k, H))
+    gw = torch.full((T, k), float("nan"), dtype=torch.float32, device=DEV)
+    epm.ep_combine_grad(d_g, d_y, d_pos, d_w, grad_y=gy, grad_w=gw)
+    torch.cuda.synchronize()
+    gw1 = gw.cpu().numpy().copy()
+    r_gy, r_gw = oracle.combine_grad(g, y, pos, w)
+    assert np.array_equal(bits(gy), r_gy), "grad_y differs from the exact product"
+    check_grad_w(gw1, r_gw, g, y, pos)
+    # a second call: the same bits (fixed summation order)
+    epm.ep_combine_grad(d_g, d_y, d_pos, d_w, grad_y=gy, grad_w=gw)
+    torch.cuda.synchronize()
+    assert np.array_equal(gw.cpu().numpy().view(np.uint32), gw1.view(np.uint32))
+    del gy, r_gy
+
+    say(f"dispatch_grad {label}")
+    gx = poison_bits((T, H))
+    epm.ep_dispatch_grad(d_y, d_pos, grad_x=gx)
+    torch.cuda.synchronize()
+    frac = check_combine(bits(gx), oracle.dispatch_grad(y, pos), y, pos,
+                         np.ones((T, k), np.float32))
+    assert frac > 0.99
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "glm45air", "dsv3"])
+def test_backward_workloads(epm, name):
+    wk = wl.WORKLOADS[name]
+    pos, w, g, y = backward_inputs(wk.T, wk.H, wk.E, wk.R, wk.k, wk.seed + 7,
+                                   logits=wl.make_logits(wk))
+    run_and_check(epm, pos, w, g, y, wk.describe())
+
+
+BACKWARD_EDGE = [
+    # T, H, E, R, k, seed
+    (1, 8, 1, 1, 1, 301),           # one token, one vector per row
+    (3, 16, 4, 2, 2, 302),
+    (130, 7176, 64, 8, 6, 303),     # ragged last segment, runtime-k path
+    (257, 520, 16, 4, 8, 304),      # k = 8 path, ragged segment, odd token count
+    (64, 4096, 64, 64, 64, 305),    # the largest k
+    (1000, 64, 256, 32, 8, 306),    # short rows, many tokens
+]
+
+
+@pytest.mark.parametrize("T,H,E,R,k,seed", BACKWARD_EDGE)
+def test_backward_edge_shapes(epm, T, H, E, R, k, seed):
+    pos, w, g, y = backward_inputs(T, H, E, R, k, seed)
+    run_and_check(epm, pos, w, g, y, f"T={T} H={H} E={E} R={R} k={k} seed={seed}")
+
+
+def test_backward_skips_rows_outside_the_buffer(epm):
+    """A pos entry outside [0, T*k): grad_w = 0, no grad_y row written, and no
+    contribution to grad_x."""
+    T, H, E, R, k = 48, 1024, 16, 4, 4
+    pos, w, g, y = backward_inputs(T, H, E, R, k, 311)
+    say(f"backward with invalid pos T={T} H={H} k={k}")
+    bad = [(3, 1), (17, 0), (40, 3)]
+    pos_bad = pos.copy()
+    lost = []
+    for t, j in bad:
+        lost.append(pos[t, j])
+        pos_bad[t, j] = -1 if t != 17 else T * k + 5
+    d_pos = torch.from_numpy(pos_bad).to(DEV)
+    gy = poison_bits((T * k, H))
+    gw = torch.zeros((T, k), dtype=torch.float32, device=DEV)
+    epm.ep_combine_grad(to_dev_bits(g), to_dev_bits(y), d_pos, torch.from_numpy(w).to(DEV),
+                        grad_y=gy, grad_w=gw)
+    gx = poison_bits((T, H))
+    epm.ep_dispatch_grad(to_dev_bits(y), d_pos, grad_x=gx)
+    torch.cuda.synchronize()
+    r_gy, r_gw = oracle.combine_grad(g, y, pos, w)
+    got = bits(gy)
+    keep = np.setdiff1d(np.arange(T * k), lost)
+    assert np.array_equal(got[keep], r_gy[keep])
+    assert np.all(got[lost] == 0xFFFF), "a row outside the buffer's picks was written"
+    gw_np = gw.cpu().numpy()
+    for t, j in bad:
+        assert gw_np[t, j] == 0.0
+    mask = np.ones((T, k), bool)
+    for t, j in bad:
+        mask[t, j] = False
+    check_grad_w(np.where(mask, gw_np, 0.0), np.where(mask, r_gw, 0.0), g, y, pos)
+    # expected grad_x: the lost picks' rows count as zero
+    y0 = y.copy()
+    y0[lost] = 0
+    check_combine(bits(gx), oracle.dispatch_grad(y0, pos), y0, pos, np.ones((T, k), np.float32))
+
+
+def test_backward_validation(epm):
+    T, H, k = 4, 16, 2
+    d = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device=DEV)
+    pos = torch.zeros((T, k), dtype=torch.int32, device=DEV)
+    w = torch.zeros((T, k), dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError):
+        epm.ep_combine_grad(d(T, H), d(T * k + 1, H), pos, w)
+    with pytest.raises(ValueError):
+        epm.ep_dispatch_grad(d(T * k - 1, H), pos)
+    with pytest.raises(epm.EpError):
+        epm.ep_dispatch_grad(d(T * k, 12), pos)         # H not a multiple of 8

@@ -26,7 +26,7 @@ import pytest
 
 import oracle
 from combine_ep_route_topk_amd import workloads as wl
-from exact_bf16 import bf16_exact, rne_bf16_exact
+from exact_bf16 import bf16_exact, f32_tie_products, rne_bf16_exact
 
 ONE = 0x3F80  # bf16 1.0
 
@@ -117,27 +117,6 @@ def test_grad_y_rounding_vs_exact_rationals():
             for h in range(H):
                 want = rne_bf16_exact(wq * bf16_exact(int(g_bits[t, h])))
                 assert grad_y[pos[t, j], h] == want, (t, j, h)
-
-
-def f32_tie_products(n, seed):
-    """(w f32, g bf16 bits) pairs whose exact product is NOT a bf16 tie but
-    whose f32 rounding IS one, on the side where ties-to-even goes the other
-    way: a product first rounded to f32 and then to bf16 comes out one bf16
-    step off on these."""
-    rng = np.random.default_rng(seed)
-    ws, gs = [], []
-    while len(ws) < n:
-        g_bits = int(wl.f32_to_bf16_bits(np.array([rng.uniform(1.0, 2.0)], np.float32))[0]) | 0x1
-        g = float(wl.bf16_bits_to_f32(np.array([g_bits], np.uint16))[0])
-        below = int(rng.integers(0x3F80, 0x4000))      # bf16 pattern in [1, 2)
-        target = float(np.array([(below << 16) | 0x8000], np.uint32).view(np.float32)[0])
-        w = np.float32(target / g)
-        exact = float(w) * g                           # exact: 24 x 8 bits
-        even_goes_down = below % 2 == 0
-        if float(np.float32(exact)) == target and (exact > target) == even_goes_down:
-            ws.append(w)
-            gs.append(g_bits)
-    return np.array(ws, np.float32), np.array(gs, np.uint16)
 
 
 def test_grad_y_rounds_the_exact_product_once():
