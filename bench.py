@@ -76,6 +76,8 @@ def copy_calibration(steps: int) -> None:
 KERNEL_SOURCES = {
     "dispatch": ["dispatch.hip", "ep_device.h", "ep_internal.h"],
     "combine": ["combine.hip", "ep_combine_dev.h", "ep_device.h", "ep_internal.h"],
+    "combine_grad": ["backward.hip", "ep_combine_dev.h", "ep_device.h", "ep_internal.h"],
+    "dispatch_grad": ["combine.hip", "ep_combine_dev.h", "ep_device.h", "ep_internal.h"],
 }
 
 
@@ -299,7 +301,7 @@ def bench_backward(ep, torch, hip, set_events, w, x, lay, wt, send, dev, stream,
         res[n] = {"us": round(us, 2), "gbps": round(ab[n] / (us * 1e-6) / 1e9, 1),
                   "pct_of_peak": round(100 * ab[n] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
                   "p90_over_p10": round(float(p90 / p10), 3),
-                  "algorithmic_bytes": ab[n]}
+                  "algorithmic_bytes": ab[n], "traffic": traffic_for(n, w.name)}
     us_step = wall / K * 1e6
     res["us_per_step"] = round(us_step, 2)
     res["gbps_per_step"] = round(sum(ab.values()) / (us_step * 1e-6) / 1e9, 1)

@@ -11,15 +11,18 @@
 //
 // HBM-bound: per token one grad_out row and k expert-output rows are read and
 // k gradient rows written, 2H(1 + 2k) bytes, plus 12k bytes of pos, weights
-// and weight gradients.  One workgroup (4 waves) per token: wave w walks the
-// row segments w, w + 4, ... of kWave 16-byte vectors.  Per segment a lane
-// loads its grad_out vector and the k expert-output vectors (all k loads in
-// flight at once for the common k = 8), writes the k scaled vectors, and adds
-// the 8 products g*y of each pick to that pick's running dot.  The dots then
-// go through a wave butterfly and a fixed-order sum over the 4 waves, so the
-// result does not depend on timing.  Products of two bf16 values are exact in
-// fp32; the dot's error is that of the additions only: per lane 8 per
-// segment, then 6 butterfly steps and 3 cross-wave adds.
+// and weight gradients.  Two launches, because one kernel that mixes the
+// gathered reads of y with the scattered writes of grad_y runs well below
+// either half on its own (measured on MI355X at T=4096, H=7168, k=8: one
+// kernel 197 us; its read half 80 us, its write half 98 us at the same grid):
+//   1. dots: one workgroup (4 waves) per token reads grad_out[t] and its k
+//      rows and writes grad_w -- reads only, a grid as large as the token count;
+//   2. scatter: grad_y[pos[t][j]] = w * grad_out[t], shaped like dispatch (a
+//      wave per (token, row segment) item, segment-fastest, a grid capped
+//      below the CU count: fewer concurrent streams of scattered row writes),
+//      reading grad_out again, from the Infinity Cache where it fits.
+// Measured at that shape: dots 79 us, scatter 91 us, 172 us for the pair.
+
 #include "ep_combine_dev.h"
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -64,15 +67,6 @@ __device__ __forceinline__ float dot8(const float (&g)[8], u32x4 y, float dot)
     return dot;
 }
 
-__device__ __forceinline__ u32x4 scaled(const float (&g)[8], float w)
-{
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        o[q] = pack_bf16x2(product_for_bf16(w, g[2 * q]), product_for_bf16(w, g[2 * q + 1]));
-    return o;
-}
-
 __device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8])
 {
 #pragma unroll
@@ -82,46 +76,62 @@ __device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8])
     }
 }
 
-// One token, the compile-time pick count KC: per segment all KC expert-output
-// loads are issued before the first product.
+// w * g[0..7] rounded to bf16 as the exact products would be.  Fast path: the
+// f32 products, and a check whether any lane's product sits on a bf16 tie
+// (low 16 bits 0x8000, about one product in 65536); only then does the wave
+// redo the vector with product_for_bf16.
+__device__ __forceinline__ u32x4 scaled(const float (&g)[8], float w)
+{
+    float p[8];
+    bool tie = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        p[e] = w * g[e];
+        tie |= uint16_t(__float_as_uint(p[e])) == 0x8000u;
+    }
+    if (ballot(tie) != 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = product_for_bf16(w, g[e]);
+    }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(p[2 * q], p[2 * q + 1]);
+    return o;
+}
+
+// ------------------------------------------------------------ 1. dots
+// One token, the compile-time pick count KC: per segment all KC loads of a
+// lane are issued before the first product.  Lanes past the row end and
+// picks outside the buffer read zeros.
 template <int KC>
-__device__ __forceinline__ void token_fixed_k(const char* __restrict__ g_row,
-                                              const char* __restrict__ yb,
-                                              char* __restrict__ gyb,
-                                              const int32_t* __restrict__ prow,
-                                              const float* __restrict__ wrow, uint32_t S,
-                                              int nvec, int64_t row_bytes, int wave,
-                                              float (*sh)[kMaxK])
+__device__ __forceinline__ void dots_fixed_k(const char* __restrict__ g_row,
+                                             const char* __restrict__ yb,
+                                             const int32_t* __restrict__ prow, uint32_t S,
+                                             int nvec, int64_t row_bytes, int wave,
+                                             float (*sh)[kMaxK])
 {
     int32_t p[KC];
-    float wv[KC];
     float dot[KC];
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
         p[j] = prow[j];
-        wv[j] = wrow[j];
         dot[j] = 0.0f;
     }
+    const u32x4 zero = {0, 0, 0, 0};
     const int segs = (nvec + kWave - 1) / kWave;
     for (int seg = wave; seg < segs; seg += kWavesPerBlock) {
         const int v = seg * kWave + lane_id();
         const bool lane_ok = v < nvec;
-        const uint32_t off = uint32_t(v) * 16u;
-        const u32x4 zero = {0, 0, 0, 0};
+        const int64_t off = int64_t(v) * 16;
         float g[8];
         unpack8(lane_ok ? load16(g_row + off) : zero, g);
         u32x4 r[KC];
 #pragma unroll
         for (int j = 0; j < KC; ++j)
-            r[j] = (lane_ok && uint32_t(p[j]) < S)
-                       ? load16_nt(yb + int64_t(p[j]) * row_bytes + off) : zero;
+            r[j] = (lane_ok && uint32_t(p[j]) < S) ? load16_nt(yb + int64_t(p[j]) * row_bytes + off)
+                                                   : zero;
 #pragma unroll
-        for (int j = 0; j < KC; ++j) {
-            dot[j] = dot8(g, r[j], dot[j]);
-            if (uint32_t(p[j]) < S && lane_ok)
-                store16_coherent(buffer_rsrc(gyb + int64_t(p[j]) * row_bytes, row_bytes),
-                                 int(off), scaled(g, wv[j]));
-        }
+        for (int j = 0; j < KC; ++j) dot[j] = dot8(g, r[j], dot[j]);
     }
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
@@ -132,29 +142,25 @@ __device__ __forceinline__ void token_fixed_k(const char* __restrict__ g_row,
 
 // One token, runtime k: pick by pick, each over all of the wave's segments
 // (the grad_out row is re-read from cache per pick).  Per lane the dot of a
-// pick sums the same products in the same order as token_fixed_k.
-__device__ __noinline__ void token_any_k(const char* __restrict__ g_row,
-                                         const char* __restrict__ yb, char* __restrict__ gyb,
-                                         const int32_t* __restrict__ prow,
-                                         const float* __restrict__ wrow, int k, uint32_t S,
-                                         int nvec, int64_t row_bytes, int wave,
-                                         float (*sh)[kMaxK])
+// pick sums the same products in the same order as dots_fixed_k.
+__device__ __noinline__ void dots_any_k(const char* __restrict__ g_row,
+                                        const char* __restrict__ yb,
+                                        const int32_t* __restrict__ prow, int k, uint32_t S,
+                                        int nvec, int64_t row_bytes, int wave,
+                                        float (*sh)[kMaxK])
 {
     const int segs = (nvec + kWave - 1) / kWave;
     for (int j = 0; j < k; ++j) {
         const int32_t p = prow[j];
-        const float w = wrow[j];
         const bool valid = uint32_t(p) < S;
         float dot = 0.0f;
         for (int seg = wave; seg < segs; seg += kWavesPerBlock) {
             const int v = seg * kWave + lane_id();
             if (v < nvec && valid) {
-                const uint32_t off = uint32_t(v) * 16u;
+                const int64_t off = int64_t(v) * 16;
                 float g[8];
                 unpack8(load16(g_row + off), g);
                 dot = dot8(g, load16_nt(yb + int64_t(p) * row_bytes + off), dot);
-                store16_coherent(buffer_rsrc(gyb + int64_t(p) * row_bytes, row_bytes),
-                                 int(off), scaled(g, w));
             }
         }
         dot = wave_sum_f(dot);
@@ -162,11 +168,12 @@ __device__ __noinline__ void token_any_k(const char* __restrict__ g_row,
     }
 }
 
+// A workgroup per token (grid-stride): the 4 waves' dots, summed in wave
+// order, so the result does not depend on timing.
 template <int KC>
-__global__ __launch_bounds__(kBlock) void combine_grad_kernel(
+__global__ __launch_bounds__(kBlock) void combine_grad_dot_kernel(
     const uint16_t* __restrict__ grad_out, const uint16_t* __restrict__ y,
-    const int32_t* __restrict__ pos, const float* __restrict__ w, int T, int nvec, int k,
-    uint16_t* __restrict__ grad_y, float* __restrict__ grad_w)
+    const int32_t* __restrict__ pos, int T, int nvec, int k, float* __restrict__ grad_w)
 {
     __shared__ float sh[kWavesPerBlock][kMaxK];
     const int tid = threadIdx.x;
@@ -174,15 +181,13 @@ __global__ __launch_bounds__(kBlock) void combine_grad_kernel(
     const uint32_t S = uint32_t(T) * uint32_t(k);
     const int64_t row_bytes = int64_t(nvec) * 16;
     const char* yb = reinterpret_cast<const char*>(y);
-    char* gyb = reinterpret_cast<char*>(grad_y);
     for (int t = blockIdx.x; t < T; t += gridDim.x) {
         const char* g_row = reinterpret_cast<const char*>(grad_out) + int64_t(t) * row_bytes;
         const int32_t* prow = pos + int64_t(t) * k;
-        const float* wrow = w + int64_t(t) * k;
         if constexpr (KC > 0)
-            token_fixed_k<KC>(g_row, yb, gyb, prow, wrow, S, nvec, row_bytes, wave, sh);
+            dots_fixed_k<KC>(g_row, yb, prow, S, nvec, row_bytes, wave, sh);
         else
-            token_any_k(g_row, yb, gyb, prow, wrow, k, S, nvec, row_bytes, wave, sh);
+            dots_any_k(g_row, yb, prow, k, S, nvec, row_bytes, wave, sh);
         __syncthreads();
         if (tid < k) {
             float s = sh[0][tid];
@@ -194,21 +199,120 @@ __global__ __launch_bounds__(kBlock) void combine_grad_kernel(
     }
 }
 
+// ------------------------------------------------------------ 2. scatter
+// One (token, segment) item whose vectors all lie inside the row: U loads
+// per lane, then per pick U scaled vectors stored through a descriptor over
+// the destination row (streaming, agent-coherent).
+template <int U>
+__device__ __forceinline__ void scatter_whole(const char* __restrict__ g_row,
+                                              char* __restrict__ gyb, int64_t row_bytes,
+                                              const int32_t* __restrict__ prow,
+                                              const float* __restrict__ wrow, int k,
+                                              uint32_t S, int v0)
+{
+    const uint32_t lane_off = uint32_t(v0) * 16u;
+    float g[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u) unpack8(load16(g_row + lane_off + u * kWave * 16), g[u]);
+    for (int j = 0; j < k; ++j) {
+        const int32_t p = prow[j];
+        if (uint32_t(p) >= S) continue;
+        const float w = wrow[j];
+        const __amdgpu_buffer_rsrc_t row = buffer_rsrc(gyb + int64_t(p) * row_bytes, row_bytes);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            store16_coherent(row, int(lane_off) + u * kWave * 16, scaled(g[u], w));
+    }
+}
+
+// The last, partial segment of a row: one vector at a time.
+__device__ __noinline__ void scatter_tail(const char* __restrict__ g_row,
+                                          char* __restrict__ gyb, int64_t row_bytes,
+                                          const int32_t* __restrict__ prow,
+                                          const float* __restrict__ wrow, int k, uint32_t S,
+                                          int v0, int U, int nvec)
+{
+    for (int u = 0; u < U; ++u) {
+        const int vi = v0 + u * kWave;
+        const bool lane_ok = vi < nvec;
+        if (ballot(lane_ok) == 0) break;
+        const u32x4 zero = {0, 0, 0, 0};
+        float g[8];
+        unpack8(lane_ok ? load16(g_row + int64_t(vi) * 16) : zero, g);
+        for (int j = 0; j < k; ++j) {
+            const int32_t p = prow[j];
+            if (uint32_t(p) >= S) continue;
+            const u32x4 o = scaled(g, wrow[j]);      // every lane: scaled() votes
+            if (lane_ok) store16_nt(gyb + int64_t(p) * row_bytes + int64_t(vi) * 16, o);
+        }
+    }
+}
+
+// Items are (group of 4 tokens, row segment of kWave*U vectors), one wave per
+// token, numbered segment-fastest, as in dispatch.
+template <int U>
+__global__ __launch_bounds__(kBlock) void combine_grad_scatter_kernel(
+    const uint16_t* __restrict__ grad_out, const int32_t* __restrict__ pos,
+    const float* __restrict__ w, int T, int nvec, int k, uint16_t* __restrict__ grad_y,
+    uint32_t segs, uint32_t items)
+{
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t S = uint32_t(T) * uint32_t(k);
+    const int64_t row_bytes = int64_t(nvec) * 16;
+    char* gyb = reinterpret_cast<char*>(grad_y);
+    for (uint32_t b = blockIdx.x; b < items; b += gridDim.x) {
+        const uint32_t group = b / segs;
+        const int seg = int(b - group * segs);
+        const int t = int(group) * kWavesPerBlock + wave;
+        if (t >= T) continue;
+        const char* g_row = reinterpret_cast<const char*>(grad_out) + int64_t(t) * row_bytes;
+        const int32_t* prow = pos + int64_t(t) * k;
+        const float* wrow = w + int64_t(t) * k;
+        const int v0 = seg * kWave * U + lane_id();
+        if ((seg + 1) * kWave * U <= nvec)
+            scatter_whole<U>(g_row, gyb, row_bytes, prow, wrow, k, S, v0);
+        else
+            scatter_tail(g_row, gyb, row_bytes, prow, wrow, k, S, v0, U, nvec);
+    }
+}
+
+template <int U>
+hipError_t launch_scatter(const uint16_t* grad_out, const int32_t* pos, const float* w, int T,
+                          int nvec, int k, uint16_t* grad_y, uint32_t cap, hipStream_t s)
+{
+    const uint32_t segs = uint32_t((nvec + kWave * U - 1) / (kWave * U));
+    const uint32_t items = uint32_t((T + kWavesPerBlock - 1) / kWavesPerBlock) * segs;
+    const uint32_t grid = items < cap ? items : cap;
+    EP_LAUNCH((combine_grad_scatter_kernel<U>), dim3(grid), dim3(kBlock), 0, s, grad_out, pos, w,
+              T, nvec, k, grad_y, segs, items);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* y,
                                const int32_t* pos, const float* w, int T, int H, int k,
                                uint16_t* grad_y, float* grad_w, hipStream_t s)
 {
-    const uint32_t grid = uint32_t(T) < kMaxGrid ? uint32_t(T) : kMaxGrid;
     const int nvec = H / 8;
+    const uint32_t grid = uint32_t(T) < kMaxGrid ? uint32_t(T) : kMaxGrid;
     if (k == 8)
-        EP_LAUNCH((combine_grad_kernel<8>), dim3(grid), dim3(kBlock), 0, s,
-                  grad_out, y, pos, w, T, nvec, k, grad_y, grad_w);
+        EP_LAUNCH((combine_grad_dot_kernel<8>), dim3(grid), dim3(kBlock), 0, s, grad_out, y,
+                  pos, T, nvec, k, grad_w);
     else
-        EP_LAUNCH((combine_grad_kernel<0>), dim3(grid), dim3(kBlock), 0, s,
-                  grad_out, y, pos, w, T, nvec, k, grad_y, grad_w);
-    return hipGetLastError();
+        EP_LAUNCH((combine_grad_dot_kernel<0>), dim3(grid), dim3(kBlock), 0, s, grad_out, y,
+                  pos, T, nvec, k, grad_w);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // Three quarters of the CU count: the per-element multiply and tie check
+    // need more waves than dispatch's plain copy to keep the write path busy
+    // (measured on MI355X at T=4096, H=7168, k=8: 119 us with 128 workgroups,
+    // 90.7 us with 192, 93-95 us with 256-1024).
+    const uint32_t cap = dispatch_grid_cap() * 3 / 2;
+    if (nvec % (kWave * 7) == 0) return launch_scatter<7>(grad_out, pos, w, T, nvec, k, grad_y, cap, s);
+    if (nvec >= kWave * 8) return launch_scatter<8>(grad_out, pos, w, T, nvec, k, grad_y, cap, s);
+    if (nvec >= kWave * 4) return launch_scatter<4>(grad_out, pos, w, T, nvec, k, grad_y, cap, s);
+    return launch_scatter<1>(grad_out, pos, w, T, nvec, k, grad_y, cap, s);
 }
 
 }  // namespace ep

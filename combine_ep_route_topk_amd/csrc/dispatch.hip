@@ -97,6 +97,21 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(
     }
 }
 
+template <int U>
+hipError_t launch_u(const uint16_t* x, int T, int nvec, int k, const int32_t* pos,
+                    uint16_t* send, hipStream_t s)
+{
+    const uint32_t segs = uint32_t((nvec + kWave * U - 1) / (kWave * U));
+    const uint32_t items = uint32_t((T + kWavesPerBlock - 1) / kWavesPerBlock) * segs;
+    const uint32_t cap = dispatch_grid_cap();
+    const uint32_t grid = items < cap ? items : cap;
+    EP_LAUNCH((dispatch_kernel<U>), dim3(grid), dim3(kBlock), 0, s, x, T, nvec, k, pos,
+              send, segs, items);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 // Half the CU count of the current device (cached per device).
 uint32_t dispatch_grid_cap() {
     static uint32_t cached[64] = {};
@@ -112,21 +127,6 @@ uint32_t dispatch_grid_cap() {
     }
     return cached[slot];
 }
-
-template <int U>
-hipError_t launch_u(const uint16_t* x, int T, int nvec, int k, const int32_t* pos,
-                    uint16_t* send, hipStream_t s)
-{
-    const uint32_t segs = uint32_t((nvec + kWave * U - 1) / (kWave * U));
-    const uint32_t items = uint32_t((T + kWavesPerBlock - 1) / kWavesPerBlock) * segs;
-    const uint32_t cap = dispatch_grid_cap();
-    const uint32_t grid = items < cap ? items : cap;
-    EP_LAUNCH((dispatch_kernel<U>), dim3(grid), dim3(kBlock), 0, s, x, T, nvec, k, pos,
-              send, segs, items);
-    return hipGetLastError();
-}
-
-}  // namespace
 
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int k, const int32_t* pos,
                            uint16_t* send, hipStream_t s)

@@ -141,6 +141,10 @@ inline size_t fused_row_stride(int H) {
 }
 
 // ----------------------------------------------------------------- launchers
+// Grid cap of the kernels that scatter whole rows (dispatch, the backward
+// combine's gradient scatter): half the CU count of the current device.
+uint32_t dispatch_grid_cap();
+
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int normalize,
                              int32_t* topk_idx, float* topk_w, hipStream_t s);
 
