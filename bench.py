@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--sync-sweep", action="store_true",
+                    help="instead of the step: the fused mode's synchronisation variants "
+                         "against three launches, over the row size (one JSON line)")
     ap.add_argument("--no-isolated", action="store_true",
                     help="skip the per-op timings after a cache-clearing overwrite")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -109,6 +112,9 @@ def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration(args.steps)
+        return
+    if args.sync_sweep and args.gpus == 1:
+        sync_sweep(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: the multi-GPU "
@@ -346,32 +352,103 @@ def bench_isolated(ep, torch, hip, ops, names, set_events, dev, stream, reps=30)
     return res
 
 
-def bench_fused(ep, torch, w, x, idx, wt, stream, K, W):
-    T, H, E, R, k = w.T, w.H, w.E, w.R, w.k
-    try:
-        fz = ep.fused_outputs(T, H, k, E, R, x.device)
-        ep.ep_fused_dispatch_combine(x, idx, wt, E, R, out=fz, stream=stream)
-    except ep.EpError as e:
-        return {"status": str(e)}
-    torch.cuda.synchronize()
-    if ep.ep_get_device_error(fz["workspace"]) != ep.EP_OK or \
-            not torch.equal(fz["out"].view(torch.int16), x.view(torch.int16)):
-        return {"status": "parity gate failed"}
+SYNC_MODES = {0: "item_events", 1: "row_flag", 2: "checksum", 3: "sentinel"}
+
+
+def time_fused(ep, torch, x, idx, wt, E, R, fz, stream, K, W, sync):
     for _ in range(W):
-        ep.ep_fused_dispatch_combine(x, idx, wt, E, R, out=fz, stream=stream)
+        ep.ep_fused_dispatch_combine(x, idx, wt, E, R, out=fz, stream=stream, sync=sync)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for _ in range(K):
-        ep.ep_fused_dispatch_combine(x, idx, wt, E, R, out=fz, stream=stream)
+        ep.ep_fused_dispatch_combine(x, idx, wt, E, R, out=fz, stream=stream, sync=sync)
     b.record(stream)
     torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / K
+    return a.elapsed_time(b) * 1e3 / K
+
+
+def bench_fused(ep, torch, w, x, idx, wt, stream, K, W):
+    """The fused flag-in-payload mode, every synchronisation variant, on the
+    step's inputs (each call after the previous on one stream)."""
+    T, H, E, R, k = w.T, w.H, w.E, w.R, w.k
     from combine_ep_route_topk_amd import workloads as wl
     ab = wl.algorithmic_bytes(w)
     byts = ab["layout"] + ab["dispatch"] + ab["combine"] + 16 * w.S
-    return {"us_per_call": round(us, 2), "gbps": round(byts / (us * 1e-6) / 1e9, 1),
-            "algorithmic_bytes": byts,
+    res = {}
+    fz = ep.fused_outputs(T, H, k, E, R, x.device)
+    for sync, name in SYNC_MODES.items():
+        try:
+            ep.ep_fused_dispatch_combine(x, idx, wt, E, R, out=fz, stream=stream, sync=sync)
+        except ep.EpError as e:
+            res[name] = {"status": str(e)}
+            continue
+        torch.cuda.synchronize()
+        if ep.ep_get_device_error(fz["workspace"]) != ep.EP_OK or \
+                not torch.equal(fz["out"].view(torch.int16), x.view(torch.int16)):
+            res[name] = {"status": "parity gate failed"}
+            continue
+        us = time_fused(ep, torch, x, idx, wt, E, R, fz, stream, K, W, sync)
+        res[name] = {"us_per_call": round(us, 2), "gbps": round(byts / (us * 1e-6) / 1e9, 1)}
+    d = res.get("item_events", {})
+    return {"us_per_call": d.get("us_per_call"), "gbps": d.get("gbps"),
+            "algorithmic_bytes": byts, "sync_modes": res,
             "what": "layout + dispatch + combine (identity experts) in one launch"}
+
+
+def sync_sweep(args):
+    """UBEP Fig. 10 on one GPU: latency of layout + dispatch + combine for the
+    three-launch path (kernel boundaries as the barriers: stop-and-wait) and
+    for the fused mode's synchronisation variants, over the bytes per row
+    (H), at the DeepSeek-V3-like T, E, R, k.  Prints one JSON line."""
+    import torch
+
+    from combine_ep_route_topk_amd import ep
+    from combine_ep_route_topk_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    base = wl.WORKLOADS[args.workload]
+    T, E, R, k = base.T, base.E, base.R, base.k
+    stream = torch.cuda.current_stream(dev)
+    set_events = ep.library().ep_set_timing_events
+    rows = []
+    for H in (64, 256, 1024, 2048, 4096, 7168):
+        w = wl.Workload(f"{base.name}_H{H}", T=T, H=H, E=E, R=R, k=k, seed=base.seed)
+        inp = wl.make_inputs(w)
+        x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+        idx, wt = ep.ep_route_topk(torch.from_numpy(inp["logits"]).to(dev), k, True)
+        lay = ep.layout_outputs(T, k, E, R, dev)
+        send = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        ops = [ep.bind_dispatch_layout(idx, E, R, lay, stream),
+               ep.bind_dispatch(x, lay["pos"], send, stream),
+               ep.bind_combine(send, lay["pos"], wt, out, stream)]
+        step = make_step(ops, set_events)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        row = {"H": H, "row_bytes": 2 * H,
+               "stop_and_wait_us": round(a.elapsed_time(b) * 1e3 / args.steps, 2)}
+        if not torch.equal(out.view(torch.int16), x.view(torch.int16)):
+            row["stop_and_wait_us"] = None
+        fz = ep.fused_outputs(T, H, k, E, R, dev)
+        for sync, name in SYNC_MODES.items():
+            ep.ep_fused_dispatch_combine(x, idx, wt, E, R, out=fz, stream=stream, sync=sync)
+            torch.cuda.synchronize()
+            ok = ep.ep_get_device_error(fz["workspace"]) == ep.EP_OK and \
+                torch.equal(fz["out"].view(torch.int16), x.view(torch.int16))
+            row[name + "_us"] = round(time_fused(ep, torch, x, idx, wt, E, R, fz, stream,
+                                                 args.steps, args.warmup, sync), 2) if ok else None
+        rows.append(row)
+        print(f"[sync-sweep] H={H} {row}", file=sys.stderr, flush=True)
+        del x, send, out, fz, lay
+    print(json.dumps({"sync_sweep": rows, "T": T, "E": E, "R": R, "k": k,
+                      "steps": args.steps, "warmup": args.warmup,
+                      "what": "layout + dispatch + combine latency (us) per call"}), flush=True)
 
 
 def cpu_baseline(w, inp, gpu_lay, seconds, step_bytes):

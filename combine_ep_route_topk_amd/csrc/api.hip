@@ -261,16 +261,20 @@ ep_status ep_fused_workspace_init(void* workspace, size_t workspace_bytes, void*
     return launched(ep::launch_fused_init(workspace, e, static_cast<hipStream_t>(stream)), fn);
 }
 
-ep_status ep_fused_dispatch_combine(const uint16_t* x, const int32_t* topk_idx,
-                                    const float* topk_w, int32_t T, int32_t H, int32_t k,
-                                    int32_t E, int32_t R, int32_t* expert_counts,
-                                    int32_t* expert_offsets, int32_t* rank_counts,
-                                    int32_t* rank_offsets, int32_t* pos, uint8_t* send_rows,
-                                    uint16_t* out, void* workspace, size_t workspace_bytes,
-                                    uint64_t* epoch_out, uint32_t spin_limit, void* stream)
+ep_status ep_fused_dispatch_combine_sync(const uint16_t* x, const int32_t* topk_idx,
+                                         const float* topk_w, int32_t T, int32_t H, int32_t k,
+                                         int32_t E, int32_t R, int32_t* expert_counts,
+                                         int32_t* expert_offsets, int32_t* rank_counts,
+                                         int32_t* rank_offsets, int32_t* pos,
+                                         uint8_t* send_rows, uint16_t* out, void* workspace,
+                                         size_t workspace_bytes, uint64_t* epoch_out,
+                                         uint32_t spin_limit, int32_t sync, void* stream)
 {
     const char* fn = "ep_fused_dispatch_combine";
     TimingScope timing_scope;
+    if (sync < 0 || sync >= ep::kNumFusedSync)
+        return fail(EP_ERR_INVALID_ARG, "%s: sync=%d is not one of the EP_FUSED_SYNC_* modes", fn,
+                    sync);
     EP_TRY(check_routing_sizes(fn, T, k, E));
     EP_TRY(check_rows(fn, T, H, k));
     if (R < 1 || E % R != 0)
@@ -306,8 +310,22 @@ ep_status ep_fused_dispatch_combine(const uint16_t* x, const int32_t* topk_idx,
     }
     return launched(ep::launch_fused(x, topk_idx, topk_w, T, H, k, E, R, expert_counts,
                                      expert_offsets, rank_counts, rank_offsets, pos, send_rows,
-                                     out, workspace, spin_limit, 0, s),
+                                     out, workspace, spin_limit, 0, sync, s),
                     fn);
+}
+
+ep_status ep_fused_dispatch_combine(const uint16_t* x, const int32_t* topk_idx,
+                                    const float* topk_w, int32_t T, int32_t H, int32_t k,
+                                    int32_t E, int32_t R, int32_t* expert_counts,
+                                    int32_t* expert_offsets, int32_t* rank_counts,
+                                    int32_t* rank_offsets, int32_t* pos, uint8_t* send_rows,
+                                    uint16_t* out, void* workspace, size_t workspace_bytes,
+                                    uint64_t* epoch_out, uint32_t spin_limit, void* stream)
+{
+    return ep_fused_dispatch_combine_sync(x, topk_idx, topk_w, T, H, k, E, R, expert_counts,
+                                          expert_offsets, rank_counts, rank_offsets, pos,
+                                          send_rows, out, workspace, workspace_bytes, epoch_out,
+                                          spin_limit, ep::kSyncItemEvents, stream);
 }
 
 ep_status ep_get_device_error(const void* workspace, void* stream)
@@ -326,6 +344,9 @@ ep_status ep_get_device_error(const void* workspace, void* stream)
     if (head[1] == ep::kDevOk) return ok();
     if (head[1] == ep::kDevTimeout)
         return fail(EP_ERR_TIMEOUT, "%s: a bounded device-side wait expired", fn);
+    if (head[1] == ep::kDevSentinel)
+        return fail(EP_ERR_DEVICE, "%s: a payload row began with the sentinel mode's reserved "
+                    "pattern", fn);
     return fail(EP_ERR_DEVICE, "%s: an expert id outside [0, E) was seen", fn);
 }
 

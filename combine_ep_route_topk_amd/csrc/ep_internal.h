@@ -48,7 +48,7 @@ constexpr int kMaxK = 64;
 constexpr uint32_t kMaxGrid = uint32_t(1) << 20;
 
 // Error codes stored in a workspace's error word (host maps them to ep_status).
-enum : uint32_t { kDevOk = 0, kDevBadExpert = 1, kDevTimeout = 2 };
+enum : uint32_t { kDevOk = 0, kDevBadExpert = 1, kDevTimeout = 2, kDevSentinel = 3 };
 
 // Magic words marking initialised workspaces.
 constexpr uint32_t kLayoutMagic = 0x45504C57u;   // "EPLW"
@@ -75,7 +75,8 @@ struct WsHeader {
     LineWord timeout;       // set by any expired bounded wait
     LineWord work_ticket;   // fused mode: next work item to claim
     LineWord hist_done;     // fused mode: histogram tiles finished
-    LineWord reserved[3];
+    LineWord collision;    // fused sentinel mode: a payload held the reserved pattern
+    LineWord reserved[2];
 };
 static_assert(sizeof(WsHeader) == 1024, "header is eight 128-byte lines");
 static_assert(offsetof(WsHeader, error) == 4, "the host reads magic and error as two words");
@@ -169,11 +170,23 @@ hipError_t launch_dispatch_grad(const uint16_t* grad_send, const int32_t* pos, i
 
 hipError_t launch_fused_init(void* ws, uint64_t first_epoch, hipStream_t s);
 
+// How a combine item of the fused mode learns that its rows are complete.
+enum FusedSync : int {
+    kSyncItemEvents = 0,   // event word per scatter item, then the rows' trailers
+    kSyncRowFlag = 1,      // the rows' trailers only (Token-Flag Fusion per row)
+    kSyncChecksum = 2,     // per scatter item a checksum of the rows' markers
+    kSyncSentinel = 3,     // each row's leading 16 bytes leave a reserved pattern
+};
+constexpr int kNumFusedSync = 4;
+// The sentinel mode's reserved pattern: every 32-bit word of a row's leading
+// 16 bytes holds two bf16 signalling NaNs 0x7FA5 until the row is written.
+constexpr uint32_t kSentinelWord = 0x7FA57FA5u;
+
 hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float* topk_w,
                         int T, int H, int k, int E, int R, int32_t* expert_counts,
                         int32_t* expert_offsets, int32_t* rank_counts,
                         int32_t* rank_offsets, int32_t* pos, uint8_t* send_rows,
-                        uint16_t* out, void* ws, uint32_t spin_limit, int grid,
+                        uint16_t* out, void* ws, uint32_t spin_limit, int grid, int sync,
                         hipStream_t s);
 
 }  // namespace ep

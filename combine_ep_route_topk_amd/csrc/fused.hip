@@ -98,8 +98,9 @@ struct FusedArgs {
     int32_t* local_rank;
     uint64_t* status;
     uint64_t* fbase;
-    uint64_t* sdone;                      // per scatter item: the epoch once it is done
+    uint64_t* sdone;                      // per scatter item: (epoch tag << 32) | value
     uint32_t spin_limit;
+    int sync;                             // FusedSync: how combine items wait for rows
 };
 
 // Bounded wait helper state: returns false once this wait has used up its
@@ -128,6 +129,24 @@ struct Waiter {
 
 __device__ __forceinline__ bool published(uint64_t word, uint32_t ep32) {
     return uint32_t(word >> 32) == ep32;
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+// The leading 16 bytes of send row p, read as two agent-scope 8-byte loads
+// (they see stores from any XCD once those have completed).
+__device__ __forceinline__ void lead_words(const FusedArgs& a, int p, uint32_t (&w)[4]) {
+    const uint64_t* d = reinterpret_cast<const uint64_t*>(a.send_rows + int64_t(p) * a.stride);
+    const uint64_t lo = ld_relaxed64(d);
+    const uint64_t hi = ld_relaxed64(d + 1);
+    w[0] = uint32_t(lo);
+    w[1] = uint32_t(lo >> 32);
+    w[2] = uint32_t(hi);
+    w[3] = uint32_t(hi >> 32);
 }
 
 // ---------------------------------------------------------------- hist item
@@ -291,7 +310,8 @@ __device__ __forceinline__ uint64_t* trailer(const FusedArgs& a, int p) {
 // One row segment of kSegVec vectors that lies inside the row: kScatU loads
 // per lane, then kScatU streaming stores per valid pick.
 __device__ __forceinline__ void scatter_whole(const char* __restrict__ src, const FusedArgs& a,
-                                              const int* prow, uint32_t lane_off)
+                                              const int* prow, uint32_t lane_off,
+                                              uint32_t skip_off)
 {
     u32x4 v[kScatU];
 #pragma unroll
@@ -303,7 +323,8 @@ __device__ __forceinline__ void scatter_whole(const char* __restrict__ src, cons
         const __amdgpu_buffer_rsrc_t row = buffer_rsrc(rows + int64_t(p) * a.stride, a.stride);
 #pragma unroll
         for (int u = 0; u < kScatU; ++u)
-            store16_coherent(row, int(lane_off) + u * kWave * 16, v[u]);
+            if (lane_off + u * kWave * 16 != skip_off)
+                store16_coherent(row, int(lane_off) + u * kWave * 16, v[u]);
     }
 }
 
@@ -312,11 +333,12 @@ __device__ __forceinline__ void scatter_whole(const char* __restrict__ src, cons
 // the whole struct into scratch memory.
 __device__ __noinline__ void scatter_tail(const char* __restrict__ src, char* __restrict__ rows,
                                           int64_t stride, const int* prow, int k, int nvec,
-                                          int v0)
+                                          int v0, bool skip_first)
 {
     for (int u = 0; u < kScatU; ++u) {
         const int vi = v0 + u * kWave;
         if (vi >= nvec) break;
+        if (skip_first && vi == 0) continue;
         const u32x4 v = load16(src + int64_t(vi) * 16);
         for (int j = 0; j < k; ++j) {
             const int p = prow[j];         // lanes may have left: no wave op here
@@ -347,11 +369,13 @@ __device__ void do_scatter(const FusedArgs& a, int item, uint64_t epoch, int* sh
         const int* prow = sh_pos + i * a.k;
         for (int seg = wave & 1; seg * kSegVec < a.nvec; seg += 2) {
             const int v0 = seg * kSegVec + lane;
+            // sentinel mode: the leading 16 bytes are written last, below
+            const bool sp = a.sync == kSyncSentinel;
             if ((seg + 1) * kSegVec <= a.nvec)
-                scatter_whole(src, a, prow, uint32_t(v0) * 16u);
+                scatter_whole(src, a, prow, uint32_t(v0) * 16u, sp ? 0u : ~0u);
             else
                 scatter_tail(src, reinterpret_cast<char*>(a.send_rows), a.stride, prow, a.k,
-                             a.nvec, v0);
+                             a.nvec, v0, sp);
         }
     }
     // Release without an L2 write-back: every payload store is agent-coherent
@@ -364,27 +388,72 @@ __device__ void do_scatter(const FusedArgs& a, int item, uint64_t epoch, int* sh
     wait_own_stores();
     __syncthreads();
 
-    // wave 0: pos, trailer tails (agent-coherent), then the epochs
-    if (wave == 0) {
-        const int npick = kScatTok * a.k;
-        const int64_t s0 = int64_t(t0) * a.k;
+    if (wave != 0) return;
+    const int npick = kScatTok * a.k;
+    const int64_t s0 = int64_t(t0) * a.k;
+    const uint64_t tag = uint64_t(uint32_t(epoch)) << 32;
+    if (a.sync == kSyncSentinel) {
+        // Sentinel Polling: each row's leading 16 bytes, written only now,
+        // are its readiness word; a payload that holds the reserved word
+        // there could never be told apart from an unwritten row, so it is
+        // reported, and every wait of the call gives up.
+        bool clash = false;
         for (int q = lane; q < npick; q += kWave) {
             const int64_t s = s0 + q;
             if (s >= a.S) break;
             const int p = sh_pos[q];
             st_relaxed(reinterpret_cast<uint32_t*>(&a.pos[s]), uint32_t(p));
-            if (p >= 0) st_relaxed64(trailer(a, p) + 1, uint64_t(uint32_t(s)));
+            if (p < 0) continue;
+            const int t = t0 + q / a.k;
+            const u32x4 lead = load16(reinterpret_cast<const char*>(a.x) + int64_t(t) * a.nvec * 16);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) clash = clash || lead[c] == kSentinelWord;
+            uint64_t* d = reinterpret_cast<uint64_t*>(a.send_rows + int64_t(p) * a.stride);
+            st_relaxed64(d, uint64_t(lead[0]) | (uint64_t(lead[1]) << 32));
+            st_relaxed64(d + 1, uint64_t(lead[2]) | (uint64_t(lead[3]) << 32));
         }
-        wait_own_stores();                 // pos and trailer tails before the flags
+        if (ballot(clash) != 0 && lane == 0) {
+            st_relaxed(&a.hdr->collision.v, 1u);
+            st_relaxed(&a.hdr->timeout.v, 1u);
+        }
+        return;
+    }
+    if (a.sync == kSyncChecksum) {
+        // Data for Checksum: no per-row flag; the item's word carries the sum
+        // of the 32-bit words of every row's leading 16 bytes (its marker).
+        uint32_t sum = 0;
         for (int q = lane; q < npick; q += kWave) {
             const int64_t s = s0 + q;
             if (s >= a.S) break;
             const int p = sh_pos[q];
-            if (p >= 0) st_relaxed64(trailer(a, p), epoch);
+            st_relaxed(reinterpret_cast<uint32_t*>(&a.pos[s]), uint32_t(p));
+            if (p < 0) continue;
+            const int t = t0 + q / a.k;
+            const u32x4 lead = load16(reinterpret_cast<const char*>(a.x) + int64_t(t) * a.nvec * 16);
+            sum += lead[0] + lead[1] + lead[2] + lead[3];
         }
-        // the item's event word: its pos entries are final
-        if (lane == 0) st_relaxed64(&a.sdone[item], epoch);
+        sum = wave_sum_u32(sum);
+        if (lane == 0) st_relaxed64(&a.sdone[item], tag | sum);
+        return;
     }
+    // item events / row flags: pos, trailer tails (agent-coherent), then the
+    // epochs
+    for (int q = lane; q < npick; q += kWave) {
+        const int64_t s = s0 + q;
+        if (s >= a.S) break;
+        const int p = sh_pos[q];
+        st_relaxed(reinterpret_cast<uint32_t*>(&a.pos[s]), uint32_t(p));
+        if (p >= 0) st_relaxed64(trailer(a, p) + 1, uint64_t(uint32_t(s)));
+    }
+    wait_own_stores();                     // pos and trailer tails before the flags
+    for (int q = lane; q < npick; q += kWave) {
+        const int64_t s = s0 + q;
+        if (s >= a.S) break;
+        const int p = sh_pos[q];
+        if (p >= 0) st_relaxed64(trailer(a, p), epoch);
+    }
+    // the item's event word: its pos entries are final
+    if (a.sync == kSyncItemEvents && lane == 0) st_relaxed64(&a.sdone[item], tag);
 }
 
 // ---------------------------------------------------------------- combine item
@@ -436,6 +505,74 @@ __device__ __noinline__ void combine_tail(const char* __restrict__ rows, int64_t
     store_acc<1>(dst + off, acc);
 }
 
+// Waits, in one wave, until the rows p[] of a combine item are complete by
+// the Data-as-Flag check of a.sync (row flag, checksum or sentinel).  The
+// positions came from the published bases, not from the scatter items.
+__device__ bool rows_ready(const FusedArgs& a, int t0, const int (&p)[kPickRounds],
+                           uint64_t epoch)
+{
+    const int lane = lane_id();
+    Waiter wt;
+    if (a.sync == kSyncRowFlag) {
+        while (true) {
+            bool ready = true;
+#pragma unroll
+            for (int r = 0; r < kPickRounds; ++r)
+                if (p[r] >= 0) ready = ready && ld_relaxed64(trailer(a, p[r])) == epoch;
+            if (ballot(!ready) == 0) return true;
+            if (!wt.tick(a.hdr, a.spin_limit)) return false;
+        }
+    }
+    if (a.sync == kSyncSentinel) {
+        while (true) {
+            bool ready = true;
+#pragma unroll
+            for (int r = 0; r < kPickRounds; ++r) {
+                if (p[r] < 0) continue;
+                uint32_t w[4];
+                lead_words(a, p[r], w);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) ready = ready && w[c] != kSentinelWord;
+            }
+            if (ballot(!ready) == 0) return true;
+            if (!wt.tick(a.hdr, a.spin_limit)) return false;
+        }
+    }
+    // kSyncChecksum: the scatter items' words, then the rows' markers summed
+    // per item must match them
+    const uint32_t ep32 = uint32_t(epoch);
+    const int sfirst = t0 / kScatTok;
+    const int nsc = a.nScat - sfirst < kCombTok / kScatTok ? a.nScat - sfirst : kCombTok / kScatTok;
+    uint64_t word = 0;
+    while (true) {
+        if (lane < nsc) word = ld_relaxed64(&a.sdone[sfirst + lane]);
+        const bool mine = lane < nsc ? published(word, ep32) : true;
+        if (ballot(!mine) == 0) break;
+        if (!wt.tick(a.hdr, a.spin_limit)) return false;
+    }
+    fence_acquire();
+    static_assert(kCombTok / kScatTok == 2, "two scatter items per combine item");
+    const uint32_t want0 = uint32_t(__shfl(word, 0, kWave));
+    const uint32_t want1 = uint32_t(__shfl(word, 1, kWave));
+    const int per_item = kScatTok * a.k;
+    while (true) {
+        uint32_t sum0 = 0, sum1 = 0;
+#pragma unroll
+        for (int r = 0; r < kPickRounds; ++r) {
+            if (p[r] < 0) continue;
+            uint32_t w[4];
+            lead_words(a, p[r], w);
+            const uint32_t v = w[0] + w[1] + w[2] + w[3];
+            if ((r * kWave + lane) / per_item == 0) sum0 += v;
+            else sum1 += v;
+        }
+        sum0 = wave_sum_u32(sum0);
+        sum1 = wave_sum_u32(sum1);
+        if (sum0 == want0 && (nsc < 2 || sum1 == want1)) return true;
+        if (!wt.tick(a.hdr, a.spin_limit)) return false;
+    }
+}
+
 template <int KC>
 __device__ void do_combine(const FusedArgs& a, int item, uint64_t epoch, int* sh_pos,
                            int* sh_word)
@@ -443,7 +580,13 @@ __device__ void do_combine(const FusedArgs& a, int item, uint64_t epoch, int* sh
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = lane_id();
     const int t0 = item * kCombTok;
-    if (wave == 0) {
+    if (wave == 0 && a.sync != kSyncItemEvents) {
+        int p[kPickRounds];
+        bool ok = item_positions(a, t0, kCombTok, uint32_t(epoch), sh_pos, p);
+        if (ok) ok = rows_ready(a, t0, p, epoch);
+        if (ok) fence_acquire();           // the rows' payloads
+        if (lane == 0) sh_word[0] = ok;
+    } else if (wave == 0) {
         // 1. the event words of the scatter items of these tokens: once they
         //    hold this call's epoch, those items' pos entries are final (one
         //    word per scatter item instead of recomputing every position from
@@ -454,7 +597,8 @@ __device__ void do_combine(const FusedArgs& a, int item, uint64_t epoch, int* sh
         const int nsc = a.nScat - sfirst < kCombTok / kScatTok ? a.nScat - sfirst : kCombTok / kScatTok;
         Waiter wt0;
         while (true) {
-            const bool mine = lane < nsc ? ld_relaxed64(&a.sdone[sfirst + lane]) == epoch : true;
+            const uint64_t tag = uint64_t(uint32_t(epoch)) << 32;
+            const bool mine = lane < nsc ? ld_relaxed64(&a.sdone[sfirst + lane]) == tag : true;
             if (ballot(!mine) == 0) break;
             if (!wt0.tick(a.hdr, a.spin_limit)) {
                 ok = false;
@@ -568,9 +712,11 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs a) {
     if (tid == 0) {
         WsHeader* h = a.hdr;
         uint32_t err = kDevOk;
-        if (ld_relaxed(&h->timeout.v)) err = kDevTimeout;
+        if (ld_relaxed(&h->collision.v)) err = kDevSentinel;
+        else if (ld_relaxed(&h->timeout.v)) err = kDevTimeout;
         else if (a.expert_offsets[a.E] != a.S) err = kDevBadExpert;
         h->error = err;
+        h->collision.v = 0;
         h->timeout.v = 0;
         h->work_ticket.v = 0;
         h->hist_done.v = 0;
@@ -587,11 +733,24 @@ __global__ void fused_init_kernel(WsHeader* hdr, uint64_t first_epoch) {
         hdr->error = kDevOk;
         hdr->scan_ticket.v = 0;
         hdr->timeout.v = 0;
+        hdr->collision.v = 0;
         hdr->work_ticket.v = 0;
         hdr->hist_done.v = 0;
         hdr->epoch = first_epoch;
         hdr->last_epoch = 0;
     }
+}
+
+// Sentinel mode, before each call: every row's leading 16 bytes get the
+// reserved pattern again (the reset pass that sentinel polling needs after
+// the rows of the previous call were consumed).
+__global__ __launch_bounds__(kBlock) void sentinel_reset_kernel(uint8_t* rows, int64_t stride,
+                                                                int64_t S)
+{
+    const u32x4 v = {kSentinelWord, kSentinelWord, kSentinelWord, kSentinelWord};
+    for (int64_t s = int64_t(blockIdx.x) * kBlock + threadIdx.x; s < S;
+         s += int64_t(gridDim.x) * kBlock)
+        store16(rows + s * stride, v);
 }
 
 int resident_grid(const void* kernel) {
@@ -625,7 +784,7 @@ hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float*
                         int T, int H, int k, int E, int R, int32_t* expert_counts,
                         int32_t* expert_offsets, int32_t* rank_counts,
                         int32_t* rank_offsets, int32_t* pos, uint8_t* send_rows,
-                        uint16_t* out, void* ws, uint32_t spin_limit, int grid,
+                        uint16_t* out, void* ws, uint32_t spin_limit, int grid, int sync,
                         hipStream_t s)
 {
     const FusedPlan f = fused_plan(T, k, E);
@@ -661,6 +820,15 @@ hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float*
     a.fbase = reinterpret_cast<uint64_t*>(w + f.off_fbase);
     a.sdone = reinterpret_cast<uint64_t*>(w + f.off_sdone);
     a.spin_limit = spin_limit ? spin_limit : kDefaultSpinLimit;
+    a.sync = sync;
+
+    if (sync == kSyncSentinel) {
+        const int64_t blocks = (a.S + kBlock - 1) / kBlock;
+        const uint32_t rg = blocks < 1024 ? uint32_t(blocks) : 1024u;
+        EP_LAUNCH(sentinel_reset_kernel, dim3(rg), dim3(kBlock), 0, s, send_rows, a.stride, a.S);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
 
     const void* kern = k == 8 ? reinterpret_cast<const void*>(&fused_kernel<8>)
                               : reinterpret_cast<const void*>(&fused_kernel<0>);

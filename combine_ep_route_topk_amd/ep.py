@@ -49,6 +49,10 @@ _SIGS = {
     "ep_fused_dispatch_combine": ([_P, _P, _P, _i32, _i32, _i32, _i32, _i32, _P, _P, _P, _P,
                                    _P, _P, _P, _P, _sz, ctypes.POINTER(ctypes.c_uint64), _u32,
                                    _P], ctypes.c_int),
+    "ep_fused_dispatch_combine_sync": ([_P, _P, _P, _i32, _i32, _i32, _i32, _i32, _P, _P, _P,
+                                        _P, _P, _P, _P, _P, _sz,
+                                        ctypes.POINTER(ctypes.c_uint64), _u32, _i32, _P],
+                                       ctypes.c_int),
     "ep_get_device_error": ([_P, _P], ctypes.c_int),
     "ep_set_timing_events": ([_P, _P], ctypes.c_int),
 }
@@ -59,6 +63,9 @@ for _name, (_args, _res) in _SIGS.items():
 
 EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_WORKSPACE = 0, 1, 2, 3
 EP_ERR_LAUNCH, EP_ERR_DEVICE, EP_ERR_TIMEOUT = 4, 5, 6
+# How the fused mode's combine waits for the rows (ep_fused_sync in the header)
+EP_FUSED_SYNC_ITEM_EVENTS, EP_FUSED_SYNC_ROW_FLAG = 0, 1
+EP_FUSED_SYNC_CHECKSUM, EP_FUSED_SYNC_SENTINEL = 2, 3
 
 
 class EpError(RuntimeError):
@@ -281,10 +288,12 @@ def fused_outputs(T: int, H: int, k: int, E: int, R: int, device) -> dict:
 
 def ep_fused_dispatch_combine(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
                               E: int, R: int, out: dict | None = None, spin_limit: int = 0,
-                              want_epoch: bool = False, stream=None) -> dict:
+                              want_epoch: bool = False, stream=None,
+                              sync: int = EP_FUSED_SYNC_ITEM_EVENTS) -> dict:
     """Layout + dispatch + combine (identity experts) in one persistent launch.
     Returns the dict of outputs; with want_epoch the call also reads back the
-    epoch written into the trailers (key 'epoch')."""
+    epoch written into the trailers (key 'epoch').  `sync` picks how combine
+    waits for the rows (EP_FUSED_SYNC_*)."""
     _bits_ok(x, "x")
     T, H = x.shape
     _need(topk_idx, "topk_idx", torch.int32)
@@ -293,12 +302,12 @@ def ep_fused_dispatch_combine(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: t
     if out is None:
         out = fused_outputs(T, H, k, E, R, x.device)
     ep = ctypes.c_uint64(0)
-    _check(_lib.ep_fused_dispatch_combine(
+    _check(_lib.ep_fused_dispatch_combine_sync(
         _ptr(x), _ptr(topk_idx), _ptr(topk_w), T, H, k, E, R, _ptr(out["expert_counts"]),
         _ptr(out["expert_offsets"]), _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]),
         _ptr(out["pos"]), _ptr(out["send_rows"]), _ptr(out["out"]), _ptr(out["workspace"]),
         out["workspace"].numel(), ctypes.byref(ep) if want_epoch else None, int(spin_limit),
-        _P(_stream(stream, x.device))))
+        int(sync), _P(_stream(stream, x.device))))
     if want_epoch:
         out["epoch"] = int(ep.value)
     return out

@@ -71,7 +71,7 @@ const char* ep_last_error(void);
  * RailWave's execution protocol times each run with GPU events around the
  * device work only).  After this call, the NEXT compute entry point called on
  * the same thread (ep_route_topk, ep_dispatch_layout, ep_dispatch, ep_combine,
- * ep_combine_grad, ep_dispatch_grad, ep_fused_dispatch_combine) records `start_event` when its first kernel
+ * ep_combine_grad, ep_dispatch_grad, ep_fused_dispatch_combine[_sync]) records `start_event` when its first kernel
  * starts and `stop_event` when its last kernel ends, taken from the kernels'
  * own dispatch packets -- the same interval a kernel-trace profiler reports,
  * with no marker packet in between.  Either event may be NULL.  The hook then
@@ -231,6 +231,58 @@ ep_status ep_fused_dispatch_combine(const uint16_t* x, const int32_t* topk_idx,
                                     void* workspace, size_t workspace_bytes,
                                     uint64_t* epoch_out, uint32_t spin_limit,
                                     void* stream);
+
+/* ---------------------------------------------------------------------------
+ * The fused mode with a choice of how each combine item learns that its send
+ * rows are complete.  [UBEP sec. 3.4, Fig. 6] three Data-as-Flag variants:
+ * Token-Flag Fusion (a flag travels with each block of data), Data for
+ * Checksum (a per-batch checksum of marker bytes confirms arrival) and
+ * Sentinel Polling (the receive buffer starts at a reserved value that the
+ * data overwrites; it must be reset after use, and data equal to that value
+ * cannot be told from none); [UBEP sec. 5.4, Fig. 10] compares them with
+ * stop-and-wait.  [HPMOE sec. 4.3-4.4] event counters per task.  On this GPU a
+ * 16-byte store is the largest whose visibility the readers rely on, so in
+ * every mode the data is made visible before its readiness word (stores with
+ * the agent-coherence bit, then a wait for their completion).
+ *   sync = EP_FUSED_SYNC_ITEM_EVENTS (0): ep_fused_dispatch_combine's mode.
+ *          Combine waits for the event words of the scatter items of its
+ *          tokens, reads pos, then checks each row's trailer.
+ *   sync = EP_FUSED_SYNC_ROW_FLAG (1): combine derives its positions from
+ *          the published bases and polls each row's 16-byte trailer
+ *          {epoch, slot_src} (Token-Flag Fusion at row granularity).
+ *   sync = EP_FUSED_SYNC_CHECKSUM (2): no trailers are written.  Each scatter
+ *          item (2 tokens) publishes one word: the call's epoch tag and the
+ *          32-bit sum of the 32-bit words of its rows' leading 16 bytes;
+ *          combine waits for the words of its items, then re-reads those
+ *          bytes from the rows until the sums match.
+ *   sync = EP_FUSED_SYNC_SENTINEL (3): no trailers are written.  Before the
+ *          fused kernel, a reset launch stores the reserved pattern -- bf16
+ *          0x7FA5 (a signalling NaN) in all eight positions -- into every
+ *          row's leading 16 bytes; scatter writes those 16 bytes last;
+ *          combine polls them until none of their four 32-bit words is
+ *          0x7FA57FA5.  A token whose leading 16 bytes contain that 32-bit
+ *          word cannot be sent this way: the call then ends its waits early
+ *          and ep_get_device_error() returns EP_ERR_DEVICE (the other modes
+ *          accept any data).
+ * In modes 2 and 3 the trailer bytes of send_rows are left as they were.
+ * Layout outputs, payload and out are the same in every mode.  Any other
+ * sync value is EP_ERR_INVALID_ARG.
+ * ------------------------------------------------------------------------- */
+typedef enum {
+    EP_FUSED_SYNC_ITEM_EVENTS = 0,
+    EP_FUSED_SYNC_ROW_FLAG = 1,
+    EP_FUSED_SYNC_CHECKSUM = 2,
+    EP_FUSED_SYNC_SENTINEL = 3
+} ep_fused_sync;
+
+ep_status ep_fused_dispatch_combine_sync(const uint16_t* x, const int32_t* topk_idx,
+                                         const float* topk_w, int32_t T, int32_t H, int32_t k,
+                                         int32_t E, int32_t R, int32_t* expert_counts,
+                                         int32_t* expert_offsets, int32_t* rank_counts,
+                                         int32_t* rank_offsets, int32_t* pos,
+                                         uint8_t* send_rows, uint16_t* out, void* workspace,
+                                         size_t workspace_bytes, uint64_t* epoch_out,
+                                         uint32_t spin_limit, int32_t sync, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Reads a layout or fused workspace's error word: synchronises `stream` first,

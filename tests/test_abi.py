@@ -26,7 +26,8 @@ def ep():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("ep_route_topk", "ep_dispatch_layout", "ep_dispatch", "ep_combine",
-                     "ep_fused_dispatch_combine", "ep_get_device_error"):
+                     "ep_fused_dispatch_combine", "ep_fused_dispatch_combine_sync",
+                     "ep_combine_grad", "ep_dispatch_grad", "ep_get_device_error"):
         assert required in names
 
 
@@ -135,6 +136,24 @@ def test_fused_validation(ep):
     assert rc == ep.EP_ERR_WORKSPACE
     rc, _ = call(lib, "ep_fused_workspace_init", f, 16, None)
     assert rc == ep.EP_ERR_WORKSPACE
+    for bad in (-1, 4):
+        rc, msg = call(lib, "ep_fused_dispatch_combine_sync", f, f, f, 64, 16, 2, 8, 2, f, f, f,
+                       f, f, f, f, f, need, None, 0, bad, None)
+        assert rc == ep.EP_ERR_INVALID_ARG and "sync" in msg
+
+
+def test_backward_validation(ep):
+    lib = ep.library()
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    rc, msg = call(lib, "ep_combine_grad", f, f, f, f, 16, 12, 2, f, f, None)
+    assert rc == ep.EP_ERR_INVALID_ARG and "H=12" in msg
+    rc, _ = call(lib, "ep_combine_grad", f, f, f, f, 16, 16, 2, f, P(FAKE + 2), None)
+    assert rc == ep.EP_ERR_INVALID_ARG            # grad_w not 4-byte aligned
+    rc, _ = call(lib, "ep_dispatch_grad", f, f, 16, 16, 0, f, None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+    rc, msg = call(lib, "ep_dispatch_grad", f, f, 1 << 21, 1 << 19, 1, f, None)
+    assert rc == ep.EP_ERR_UNSUPPORTED and "T*H" in msg
 
 
 def test_binding_refuses_cpu_tensors(ep):

@@ -91,18 +91,18 @@ class Emu:
         self.flay = self.layout_arrays()
         self.out = aligned(self.T * self.H * 2, 16).view(np.uint16).reshape(self.T, self.H)
 
-    def fused(self, x, idx, wt, spin_limit=1 << 26):
+    def fused(self, x, idx, wt, spin_limit=1 << 26, sync=0):
         L = self.L
         xa = aligned(x.nbytes, 16).view(np.uint16).reshape(x.shape)
         xa[:] = x
         e = ctypes.c_uint64(0)
         lay = self.flay
-        rc = L.ep_fused_dispatch_combine(
+        rc = L.ep_fused_dispatch_combine_sync(
             p(xa), p(np.ascontiguousarray(idx)), p(np.ascontiguousarray(wt)), self.T, self.H,
             self.k, self.E, self.R, p(lay["expert_counts"]), p(lay["expert_offsets"]),
             p(lay["rank_counts"]), p(lay["rank_offsets"]), p(lay["pos"]), p(self.rows),
             p(self.out), p(self.ws), ctypes.c_size_t(self.ws.size), ctypes.byref(e),
-            ctypes.c_uint32(spin_limit), None)
+            ctypes.c_uint32(spin_limit), ctypes.c_int32(sync), None)
         self.check(rc)
         return e.value, L.ep_get_device_error(p(self.ws), None)
 
@@ -236,3 +236,63 @@ def test_emulated_backward_matches_oracle(emu, T, H, E, R, k, seed):
     rc = emu.ep_dispatch_grad(p(y), p(pos), T, H, k, p(gx), None)
     assert rc == 0, emu.ep_last_error().decode()
     gu.check_combine(gx, oracle.dispatch_grad(y, pos), y, pos, np.ones((T, k), np.float32))
+
+
+SYNC_NAMES = {0: "item events", 1: "row flags", 2: "checksum", 3: "sentinel"}
+
+
+@pytest.mark.parametrize("sync", [1, 2, 3])
+@pytest.mark.parametrize("T,H,E,R,k,seed", [(128, 256, 8, 2, 2, 41), (130, 7176, 64, 8, 6, 42),
+                                             (600, 64, 256, 32, 8, 43), (5, 16, 4, 2, 2, 44)])
+def test_emulated_fused_sync_modes(emu, sync, T, H, E, R, k, seed):
+    """The Data-as-Flag variants of the fused mode (UBEP sec. 3.4, Fig. 6):
+    row flags, a per-batch checksum, sentinel polling.  Layout, payload and
+    combined output match the oracle on two calls in a row, then the default
+    mode runs on the same workspace."""
+    rng = np.random.default_rng(seed)
+    o_idx, o_w = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
+    o_lay = oracle.dispatch_layout(o_idx, E, R)
+    x = wl.make_rows(T, H, seed + 1)
+    x2 = wl.make_rows(T, H, seed + 2)
+    o_send = oracle.dispatch(x, o_lay["pos"])
+    m = Emu(emu, T, H, E, R, k)
+    m.fused_setup()
+    for xi in (x2, x):
+        _, st = m.fused(xi, o_idx, o_w, sync=sync)
+        assert st == 0, SYNC_NAMES[sync]
+        assert np.array_equal(m.out, oracle.combine(oracle.dispatch(xi, o_lay["pos"]),
+                                                    o_lay["pos"], o_w)), SYNC_NAMES[sync]
+    for key in m.flay:
+        np.testing.assert_array_equal(m.flay[key], o_lay[key], err_msg=key)
+    payload = m.rows[:, :2 * H].copy().view(np.uint16)
+    assert np.array_equal(payload, o_send), "payload"
+    _, st = m.fused(x2, o_idx, o_w, sync=0)
+    assert st == 0
+    assert np.array_equal(m.out, oracle.combine(oracle.dispatch(x2, o_lay["pos"]), o_lay["pos"], o_w))
+
+
+def test_emulated_sentinel_collision_is_reported(emu):
+    """A token whose leading 16 bytes hold the reserved pattern cannot be told
+    from an unwritten row: the call reports it (EP_ERR_DEVICE) instead of
+    waiting, and the workspace works again on the next call."""
+    T, H, E, R, k = 64, 32, 8, 2, 2
+    rng = np.random.default_rng(51)
+    o_idx, o_w = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
+    x = wl.make_rows(T, H, 52)
+    bad = x.copy()
+    bad[9, 2:4] = 0x7FA5                  # one 32-bit word of the reserved pattern
+    m = Emu(emu, T, H, E, R, k)
+    m.fused_setup()
+    _, st = m.fused(bad, o_idx, o_w, sync=3)
+    assert st == 5
+    assert b"sentinel" in emu.ep_last_error()
+    _, st = m.fused(x, o_idx, o_w, sync=3)
+    assert st == 0
+    o_lay = oracle.dispatch_layout(o_idx, E, R)
+    assert np.array_equal(m.out, oracle.combine(oracle.dispatch(x, o_lay["pos"]),
+                                                o_lay["pos"], o_w))
+    # the same rows through the other modes are fine: the pattern is reserved
+    # only in the sentinel mode
+    for sync in (0, 1, 2):
+        _, st = m.fused(bad, o_idx, o_w, sync=sync)
+        assert st == 0
