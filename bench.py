@@ -352,7 +352,7 @@ def bench_isolated(ep, torch, hip, ops, names, set_events, dev, stream, reps=30)
     return res
 
 
-SYNC_MODES = {0: "item_events", 1: "row_flag", 2: "checksum", 3: "sentinel"}
+SYNC_MODES = {0: "item_events", 1: "row_flag", 2: "checksum", 3: "sentinel", 4: "chunk_flag"}
 
 
 def time_fused(ep, torch, x, idx, wt, E, R, fz, stream, K, W, sync):

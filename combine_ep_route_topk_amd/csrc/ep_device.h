@@ -61,6 +61,13 @@ constexpr int kCpolNtSc1 = 2 | 16;
 __device__ __forceinline__ void store16_coherent(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolNtSc1);
 }
+// 16-byte load with the same bits: served at agent scope (it sees every
+// store from any XCD that has completed) and not kept in this XCD's L2, so
+// no L2 invalidate (acquire fence) is needed before it.  The descriptor's
+// base must be wave-uniform.
+__device__ __forceinline__ u32x4 load16_coherent(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolNtSc1));
+}
 // Wait until every store this wave issued has completed (s_waitcnt vmcnt(0)
 // on gfx9-family ISAs, where stores count in vmcnt); the compiler may move
 // no memory access across it.

@@ -137,8 +137,14 @@ inline FusedPlan fused_plan(int T, int k, int E) {
 // agent-scope load plus a short sleep, roughly a microsecond).
 constexpr uint32_t kDefaultSpinLimit = uint32_t(1) << 20;
 
+// Bytes per 16-byte-vector chunk that carries its own readiness word in the
+// fused mode's sub-row flag variant (one wave-wide row segment).
+constexpr int kChunkBytes = 1024;
+// A fused send row: payload (2H bytes), the 16-byte trailer, then one 8-byte
+// flag per kChunkBytes chunk of the payload, padded to 128 bytes.
 inline size_t fused_row_stride(int H) {
-    return (size_t(2) * H + 16 + 127) / 128 * 128;
+    const size_t chunks = (size_t(2) * H + kChunkBytes - 1) / kChunkBytes;
+    return (size_t(2) * H + 16 + 8 * chunks + 127) / 128 * 128;
 }
 
 // ----------------------------------------------------------------- launchers
@@ -176,8 +182,9 @@ enum FusedSync : int {
     kSyncRowFlag = 1,      // the rows' trailers only (Token-Flag Fusion per row)
     kSyncChecksum = 2,     // per scatter item a checksum of the rows' markers
     kSyncSentinel = 3,     // each row's leading 16 bytes leave a reserved pattern
+    kSyncChunkFlag = 4,    // a flag per 1 KiB chunk of each row (sub-row TFF)
 };
-constexpr int kNumFusedSync = 4;
+constexpr int kNumFusedSync = 5;
 // The sentinel mode's reserved pattern: every 32-bit word of a row's leading
 // 16 bytes holds two bf16 signalling NaNs 0x7FA5 until the row is written.
 constexpr uint32_t kSentinelWord = 0x7FA57FA5u;

@@ -306,6 +306,34 @@ __device__ __forceinline__ uint64_t* trailer(const FusedArgs& a, int p) {
     return reinterpret_cast<uint64_t*>(a.send_rows + int64_t(p) * a.stride + a.trailer_off);
 }
 
+// The flag of 1 KiB chunk c (kWave 16-byte vectors) of row p, after the
+// trailer (sub-row flag mode).
+__device__ __forceinline__ uint64_t* chunk_flag(const FusedArgs& a, int p, int c) {
+    return trailer(a, p) + 2 + c;
+}
+
+// Sub-row flag mode, one wave: waits until chunk c of every row in prow[0..k)
+// holds this call's flag.  No acquire fence: in this mode the chunk's data is
+// read with agent-coherent loads (load16_coherent), issued only after the
+// flags were seen -- an L2 invalidate per chunk and wave would cost more than
+// the copy.  False on timeout.
+__device__ bool chunk_ready(const FusedArgs& a, const int* prow, int k, int c, uint64_t epoch)
+{
+    const int lane = lane_id();
+    Waiter wt;
+    while (true) {
+        bool ready = true;
+        for (int j = lane; j < k; j += kWave) {
+            const int p = prow[j];
+            if (p >= 0) ready = ready && ld_relaxed64(chunk_flag(a, p, c)) == epoch;
+        }
+        if (ballot(!ready) == 0) break;
+        if (!wt.tick(a.hdr, a.spin_limit)) return false;
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // no load moves above the flags
+    return true;
+}
+
 // ---------------------------------------------------------------- scatter item
 // One row segment of kSegVec vectors that lies inside the row: kScatU loads
 // per lane, then kScatU streaming stores per valid pick.
@@ -376,6 +404,18 @@ __device__ void do_scatter(const FusedArgs& a, int item, uint64_t epoch, int* sh
             else
                 scatter_tail(src, reinterpret_cast<char*>(a.send_rows), a.stride, prow, a.k,
                              a.nvec, v0, sp);
+            if (a.sync == kSyncChunkFlag) {
+                // sub-row flags: this wave's chunks of the k rows, as soon as
+                // its own stores of them have completed
+                wait_own_stores();
+                const int nchunk = (a.nvec + kWave - 1) / kWave;
+                const int c0 = seg * kScatU;
+                const int nc = nchunk - c0 < kScatU ? nchunk - c0 : kScatU;
+                for (int q = lane; q < a.k * nc; q += kWave) {
+                    const int p = prow[q / nc];
+                    if (p >= 0) st_relaxed64(chunk_flag(a, p, c0 + q % nc), epoch);
+                }
+            }
         }
     }
     // Release without an L2 write-back: every payload store is agent-coherent
@@ -415,6 +455,14 @@ __device__ void do_scatter(const FusedArgs& a, int item, uint64_t epoch, int* sh
         if (ballot(clash) != 0 && lane == 0) {
             st_relaxed(&a.hdr->collision.v, 1u);
             st_relaxed(&a.hdr->timeout.v, 1u);
+        }
+        return;
+    }
+    if (a.sync == kSyncChunkFlag) {        // the flags are out already
+        for (int q = lane; q < npick; q += kWave) {
+            const int64_t s = s0 + q;
+            if (s >= a.S) break;
+            st_relaxed(reinterpret_cast<uint32_t*>(&a.pos[s]), uint32_t(sh_pos[q]));
         }
         return;
     }
@@ -459,28 +507,33 @@ __device__ void do_scatter(const FusedArgs& a, int item, uint64_t epoch, int* sh
 // ---------------------------------------------------------------- combine item
 // One 64-vector segment that lies inside the row: all picks' loads first (KC
 // unrolled), then the fixed-order reduction.
-template <int KC>
+// COH: the rows are read with agent-coherent loads (sub-row flag mode).
+template <bool COH>
+__device__ __forceinline__ u32x4 row_load(const FusedArgs& a, int p, uint32_t off) {
+    char* row = reinterpret_cast<char*>(a.send_rows) + int64_t(p) * a.stride;
+    if constexpr (COH) return load16_coherent(buffer_rsrc(row, a.stride), int(off));
+    else return load16_nt(row + off);
+}
+
+template <int KC, bool COH>
 __device__ __forceinline__ void combine_whole(const FusedArgs& a, const int (&pj)[KC > 0 ? KC : 1],
                                               const int* prow, const float* wrow,
                                               uint32_t off, char* dst)
 {
     const uint32_t S = uint32_t(a.S);
-    const char* rows = reinterpret_cast<const char*>(a.send_rows);
     float acc[1][8];
     if constexpr (KC > 0) {
         u32x4 r[KC][1];
 #pragma unroll
         for (int j = 0; j < KC; ++j)
-            r[j][0] = uint32_t(pj[j]) < S ? load16_nt(rows + int64_t(pj[j]) * a.stride + off)
-                                          : u32x4{0, 0, 0, 0};
+            r[j][0] = uint32_t(pj[j]) < S ? row_load<COH>(a, pj[j], off) : u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < KC; ++j) accumulate<1>(acc, r[j], wrow[j], j == 0);
     } else {
         for (int j = 0; j < a.k; ++j) {
             const int p = __builtin_amdgcn_readfirstlane(prow[j]);
             u32x4 r[1];
-            r[0] = uint32_t(p) < S ? load16_nt(rows + int64_t(p) * a.stride + off)
-                                   : u32x4{0, 0, 0, 0};
+            r[0] = uint32_t(p) < S ? row_load<COH>(a, p, off) : u32x4{0, 0, 0, 0};
             accumulate<1>(acc, r, wrow[j], j == 0);
         }
     }
@@ -490,16 +543,24 @@ __device__ __forceinline__ void combine_whole(const FusedArgs& a, const int (&pj
 // The last, partial segment of a row (scalar arguments, as scatter_tail).
 __device__ __noinline__ void combine_tail(const char* __restrict__ rows, int64_t stride,
                                           uint32_t S, const int* prow, const float* wrow,
-                                          int k, int nvec, int v0, char* dst)
+                                          int k, int nvec, int v0, char* dst, bool coherent)
 {
     if (v0 >= nvec) return;
     const uint32_t off = uint32_t(v0) * 16u;
     float acc[1][8];
     for (int j = 0; j < k; ++j) {
         const int p = prow[j];             // lanes may have left: no wave op here
-        u32x4 r[1];
-        r[0] = uint32_t(p) < S ? load16_nt(rows + int64_t(p) * stride + off)
-                               : u32x4{0, 0, 0, 0};
+        u32x4 r[1] = {u32x4{0, 0, 0, 0}};
+        if (uint32_t(p) < S) {
+            const char* src = rows + int64_t(p) * stride + off;
+            if (coherent) {                // two agent-scope 8-byte loads
+                const uint64_t lo = ld_relaxed64(reinterpret_cast<const uint64_t*>(src));
+                const uint64_t hi = ld_relaxed64(reinterpret_cast<const uint64_t*>(src) + 1);
+                r[0] = u32x4{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32)};
+            } else {
+                r[0] = load16_nt(src);
+            }
+        }
         accumulate<1>(acc, r, wrow[j], j == 0);
     }
     store_acc<1>(dst + off, acc);
@@ -583,7 +644,8 @@ __device__ void do_combine(const FusedArgs& a, int item, uint64_t epoch, int* sh
     if (wave == 0 && a.sync != kSyncItemEvents) {
         int p[kPickRounds];
         bool ok = item_positions(a, t0, kCombTok, uint32_t(epoch), sh_pos, p);
-        if (ok) ok = rows_ready(a, t0, p, epoch);
+        // sub-row flags: each wave waits per chunk below
+        if (ok && a.sync != kSyncChunkFlag) ok = rows_ready(a, t0, p, epoch);
         if (ok) fence_acquire();           // the rows' payloads
         if (lane == 0) sh_word[0] = ok;
     } else if (wave == 0) {
@@ -654,11 +716,16 @@ __device__ void do_combine(const FusedArgs& a, int item, uint64_t epoch, int* sh
     for (int j = 0; j < (KC > 0 ? KC : 1); ++j)
         pj[j] = KC > 0 ? __builtin_amdgcn_readfirstlane(prow[j]) : 0;
     for (int v0 = (wave % kWpt) * kWave + lane; v0 - lane < a.nvec; v0 += kWpt * kWave) {
-        if (v0 - lane + kWave <= a.nvec)
-            combine_whole<KC>(a, pj, prow, wrow, uint32_t(v0) * 16u, dst);
-        else
+        if (a.sync == kSyncChunkFlag && !chunk_ready(a, prow, k, (v0 - lane) / kWave, epoch))
+            return;
+        const bool coh = a.sync == kSyncChunkFlag;
+        if (v0 - lane + kWave <= a.nvec) {
+            if (coh) combine_whole<KC, true>(a, pj, prow, wrow, uint32_t(v0) * 16u, dst);
+            else combine_whole<KC, false>(a, pj, prow, wrow, uint32_t(v0) * 16u, dst);
+        } else {
             combine_tail(reinterpret_cast<const char*>(a.send_rows), a.stride, uint32_t(a.S),
-                         prow, wrow, a.k, a.nvec, v0, dst);
+                         prow, wrow, a.k, a.nvec, v0, dst, coh);
+        }
     }
 }
 

@@ -65,7 +65,7 @@ EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_WORKSPACE = 0, 1, 2, 3
 EP_ERR_LAUNCH, EP_ERR_DEVICE, EP_ERR_TIMEOUT = 4, 5, 6
 # How the fused mode's combine waits for the rows (ep_fused_sync in the header)
 EP_FUSED_SYNC_ITEM_EVENTS, EP_FUSED_SYNC_ROW_FLAG = 0, 1
-EP_FUSED_SYNC_CHECKSUM, EP_FUSED_SYNC_SENTINEL = 2, 3
+EP_FUSED_SYNC_CHECKSUM, EP_FUSED_SYNC_SENTINEL, EP_FUSED_SYNC_CHUNK_FLAG = 2, 3, 4
 
 
 class EpError(RuntimeError):

@@ -201,7 +201,9 @@ ep_status ep_dispatch_grad(const uint16_t* grad_send, const int32_t* pos, int32_
  * [UBEP sec. 6, Table 5] without large atomic writes, fences are needed;
  * [HPMOE sec. 4.3-4.4] one launch whose workers wait on event counters.
  * Each send row is the bf16 payload followed by a 16-byte trailer
- * { u64 epoch, u32 slot_src, u32 0 }, padded to ep_fused_row_stride_bytes(H).
+ * { u64 epoch, u32 slot_src, u32 0 }, then one u64 flag per 1 KiB chunk of
+ * the payload (used by EP_FUSED_SYNC_CHUNK_FLAG only), padded to
+ * ep_fused_row_stride_bytes(H) = roundup(2H + 16 + 8*ceil(2H/1024), 128).
  *   send_rows  u8 [T*k][stride]  out: payload = x[token of the slot]; trailer
  *                                as above with this call's epoch.
  *   out        bf16 [T][H]       out: combine of the payload rows, identical
@@ -264,7 +266,14 @@ ep_status ep_fused_dispatch_combine(const uint16_t* x, const int32_t* topk_idx,
  *          word cannot be sent this way: the call then ends its waits early
  *          and ep_get_device_error() returns EP_ERR_DEVICE (the other modes
  *          accept any data).
- * In modes 2 and 3 the trailer bytes of send_rows are left as they were.
+ *   sync = EP_FUSED_SYNC_CHUNK_FLAG (4): Token-Flag Fusion at sub-row
+ *          granularity.  Every 1 KiB chunk c of a row has its own u64 flag
+ *          at byte 2H + 16 + 8c of the row; each scatter wave sets the flags
+ *          of the chunks it wrote (the call's epoch) once its stores have
+ *          completed, and each combine wave waits, chunk by chunk, only for
+ *          the chunks it reduces next.  No trailers are written.
+ * In modes 2, 3 and 4 the trailer bytes of send_rows are left as they were;
+ * the chunk flags are written in mode 4 only.
  * Layout outputs, payload and out are the same in every mode.  Any other
  * sync value is EP_ERR_INVALID_ARG.
  * ------------------------------------------------------------------------- */
@@ -272,7 +281,8 @@ typedef enum {
     EP_FUSED_SYNC_ITEM_EVENTS = 0,
     EP_FUSED_SYNC_ROW_FLAG = 1,
     EP_FUSED_SYNC_CHECKSUM = 2,
-    EP_FUSED_SYNC_SENTINEL = 3
+    EP_FUSED_SYNC_SENTINEL = 3,
+    EP_FUSED_SYNC_CHUNK_FLAG = 4
 } ep_fused_sync;
 
 ep_status ep_fused_dispatch_combine_sync(const uint16_t* x, const int32_t* topk_idx,

@@ -150,7 +150,18 @@ template <class V> inline void emu_buffer_store(V v, emu_buffer_rsrc r, int off)
     }
     std::memcpy(r.base + off, &v, sizeof(V));
 }
+struct emu_v4u32 { uint32_t v[4]; };
+inline emu_v4u32 emu_buffer_load_b128(emu_buffer_rsrc r, int off) {
+    if (off < 0 || uint64_t(uint32_t(off)) + 16 > r.n) {
+        std::fprintf(stderr, "[emu] buffer load at %d outside a %u-byte range\n", off, r.n);
+        std::abort();
+    }
+    emu_v4u32 v;
+    std::memcpy(&v, r.base + off, 16);
+    return v;
+}
 #define __builtin_amdgcn_make_buffer_rsrc(p, s, n, f) emu_make_buffer_rsrc((void*)(p), (s), (n), (f))
+#define __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, aux) emu_buffer_load_b128((r), (off))
 #define __builtin_amdgcn_raw_buffer_store_b128(v, r, off, soff, aux) emu_buffer_store((v), (r), (off))
 #define __builtin_amdgcn_s_waitcnt(x) ((void)0)
 

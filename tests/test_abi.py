@@ -56,7 +56,8 @@ def test_workspace_and_stride_queries(ep):
     assert lib.ep_fused_workspace_bytes(16384, 8, 256, 64) > big
     # payload + 16-byte trailer, rounded up to 128-byte lines
     for H in (8, 256, 4096, 7168, 7176):
-        assert lib.ep_fused_row_stride_bytes(H) == -(-(2 * H + 16) // 128) * 128
+        chunks = -(-2 * H // 1024)
+        assert lib.ep_fused_row_stride_bytes(H) == -(-(2 * H + 16 + 8 * chunks) // 128) * 128
     assert lib.ep_fused_row_stride_bytes(7) == 0
 
 
@@ -136,7 +137,7 @@ def test_fused_validation(ep):
     assert rc == ep.EP_ERR_WORKSPACE
     rc, _ = call(lib, "ep_fused_workspace_init", f, 16, None)
     assert rc == ep.EP_ERR_WORKSPACE
-    for bad in (-1, 4):
+    for bad in (-1, 5):
         rc, msg = call(lib, "ep_fused_dispatch_combine_sync", f, f, f, 64, 16, 2, 8, 2, f, f, f,
                        f, f, f, f, f, need, None, 0, bad, None)
         assert rc == ep.EP_ERR_INVALID_ARG and "sync" in msg

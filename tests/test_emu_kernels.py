@@ -238,10 +238,10 @@ def test_emulated_backward_matches_oracle(emu, T, H, E, R, k, seed):
     gu.check_combine(gx, oracle.dispatch_grad(y, pos), y, pos, np.ones((T, k), np.float32))
 
 
-SYNC_NAMES = {0: "item events", 1: "row flags", 2: "checksum", 3: "sentinel"}
+SYNC_NAMES = {0: "item events", 1: "row flags", 2: "checksum", 3: "sentinel", 4: "chunk flags"}
 
 
-@pytest.mark.parametrize("sync", [1, 2, 3])
+@pytest.mark.parametrize("sync", [1, 2, 3, 4])
 @pytest.mark.parametrize("T,H,E,R,k,seed", [(128, 256, 8, 2, 2, 41), (130, 7176, 64, 8, 6, 42),
                                              (600, 64, 256, 32, 8, 43), (5, 16, 4, 2, 2, 44)])
 def test_emulated_fused_sync_modes(emu, sync, T, H, E, R, k, seed):
@@ -293,6 +293,6 @@ def test_emulated_sentinel_collision_is_reported(emu):
                                                 o_lay["pos"], o_w))
     # the same rows through the other modes are fine: the pattern is reserved
     # only in the sentinel mode
-    for sync in (0, 1, 2):
+    for sync in (0, 1, 2, 4):
         _, st = m.fused(bad, o_idx, o_w, sync=sync)
         assert st == 0

@@ -15,7 +15,7 @@ from gpu_util import DEV, Case, bits, say, to_dev_bits
 pytestmark = pytest.mark.gpu
 
 LAYOUT_KEYS = ("expert_counts", "expert_offsets", "rank_counts", "rank_offsets", "pos")
-MODES = {1: "row flags", 2: "checksum", 3: "sentinel"}
+MODES = {1: "row flags", 2: "checksum", 3: "sentinel", 4: "chunk flags"}
 SENTINEL_WORD_HALF = 0x7FA5          # bf16; the reserved 32-bit word is two of them
 
 
@@ -36,6 +36,10 @@ def check(fz, x_bits, idx, wt, E, R, H, sync, epoch=None):
     if sync == 1 and epoch is not None:
         assert np.array_equal(rows[:, 2 * H:2 * H + 16],
                               oracle.fused_trailers(epoch, o_lay["slot_src"])), "trailers"
+    if sync == 4 and epoch is not None:
+        nchunk = -(-2 * H // 1024)
+        flags = rows[:, 2 * H + 16:2 * H + 16 + 8 * nchunk].copy().view(np.uint64)
+        assert np.all(flags == np.uint64(epoch)), "chunk flags"
     got, ref = bits(fz["out"]), oracle.combine(o_send, o_lay["pos"], wt)
     nan = (ref & 0x7F80) == 0x7F80
     nan &= (ref & 0x007F) != 0
@@ -94,7 +98,7 @@ def test_modes_alternate_on_one_workspace(epm):
     idx = torch.from_numpy(c.idx).to(DEV)
     wt = torch.from_numpy(c.wt).to(DEV)
     fz = epm.fused_outputs(w.T, w.H, w.k, w.E, w.R, DEV)
-    for i, sync in enumerate([0, 1, 2, 3, 0, 3, 2, 1, 3, 3, 2, 2]):
+    for i, sync in enumerate([0, 1, 2, 3, 4, 0, 4, 3, 2, 1, 3, 4, 4, 2, 2]):
         x_bits = wl.make_rows(w.T, w.H, seed=700 + i)
         say(f"alternating call {i} sync={sync}")
         epm.ep_fused_dispatch_combine(to_dev_bits(x_bits), idx, wt, w.E, w.R, out=fz, sync=sync)
@@ -103,7 +107,7 @@ def test_modes_alternate_on_one_workspace(epm):
         assert np.array_equal(bits(fz["out"]), x_bits), f"call {i} sync={sync}"
 
 
-@pytest.mark.parametrize("sync", [2, 3])
+@pytest.mark.parametrize("sync", [2, 3, 4])
 def test_sync_modes_back_to_back_without_host_sync(epm, sync):
     w = wl.WORKLOADS["dsv3"]
     c = Case(w)
@@ -144,7 +148,7 @@ def test_sentinel_collision_is_reported(epm):
     assert epm.ep_get_device_error(fz["workspace"]) == epm.EP_OK
     check(fz, x, o_idx, o_w, E, R, H, 3)
     # the reserved word is two bf16 signalling NaNs: combine passes NaNs on
-    for sync in (0, 1, 2):
+    for sync in (0, 1, 2, 4):
         say(f"reserved word through sync={sync}")
         epm.ep_fused_dispatch_combine(to_dev_bits(bad), idx, wt, E, R, out=fz, sync=sync,
                                       want_epoch=True)
@@ -178,6 +182,6 @@ def test_invalid_sync_is_rejected(epm):
     x = torch.zeros((T, H), dtype=torch.bfloat16, device=DEV)
     idx = torch.zeros((T, k), dtype=torch.int32, device=DEV)
     wt = torch.zeros((T, k), dtype=torch.float32, device=DEV)
-    for bad in (-1, 4):
+    for bad in (-1, 5):
         with pytest.raises(epm.EpError):
             epm.ep_fused_dispatch_combine(x, idx, wt, E, R, out=fz, sync=bad)
