@@ -43,10 +43,13 @@ def lib():
         L.ep_oracle_fused_trailer.argtypes = [ctypes.c_uint64, P, i64, P]
         L.ep_oracle_combine_grad.argtypes = [P, P, P, P, i64, i32, i32, P, P]
         L.ep_oracle_dispatch_grad.argtypes = [P, P, i64, i32, i32, P]
+        L.ep_oracle_slices.argtypes = [P, i32, i32, P, P, P]
+        L.ep_oracle_lpt.argtypes = [P, P, i32, P, i32, i32, P, P, P]
         for f in ("ep_oracle_route_topk", "ep_oracle_dispatch_layout",
                   "ep_oracle_dispatch", "ep_oracle_combine",
                   "ep_oracle_combine_tokens", "ep_oracle_fused_trailer",
-                  "ep_oracle_combine_grad", "ep_oracle_dispatch_grad"):
+                  "ep_oracle_combine_grad", "ep_oracle_dispatch_grad", "ep_oracle_slices",
+                  "ep_oracle_lpt"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -170,6 +173,32 @@ def dispatch_grad(grad_send_bits, pos):
     _check(lib().ep_oracle_dispatch_grad(_p(grad_send_bits), _p(pos), T, H, k, _p(grad_x)),
            "dispatch_grad")
     return grad_x
+
+
+def slices(expert_offsets, P: int):
+    """Equal slot slices for P workers -> (start i64 [P+1], expert i32 [P],
+    offset i64 [P])."""
+    eo = _c(expert_offsets, np.int32)
+    E = eo.shape[0] - 1
+    start = np.empty(P + 1, np.int64)
+    expert = np.empty(P, np.int32)
+    offset = np.empty(P, np.int64)
+    _check(lib().ep_oracle_slices(_p(eo), E, P, _p(start), _p(expert), _p(offset)), "slices")
+    return start, expert, offset
+
+
+def lpt(cost, peer, cap_of_peer, C: int):
+    """LPT list schedule -> (core i32 [U], stripe i32 [U], load f64 [C])."""
+    cost = _c(cost, np.float64)
+    peer = _c(peer, np.int32)
+    cap = _c(cap_of_peer, np.int32)
+    U = cost.shape[0]
+    core = np.empty(max(U, 1), np.int32)
+    stripe = np.empty(max(U, 1), np.int32)
+    load = np.empty(C, np.float64)
+    _check(lib().ep_oracle_lpt(_p(cost), _p(peer), U, _p(cap), cap.shape[0], C, _p(core),
+                               _p(stripe), _p(load)), "lpt")
+    return core[:U], stripe[:U], load
 
 
 def fused_trailers(epoch: int, slot_src):

@@ -334,3 +334,98 @@ int ep_oracle_dispatch_grad(const uint16_t* grad_send, const int32_t* pos,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Skew-balanced work partition.                                             */
+/* ------------------------------------------------------------------------ */
+
+int ep_oracle_slices(const int32_t* expert_offsets, int32_t E, int32_t P,
+                     int64_t* start, int32_t* expert, int64_t* offset)
+{
+    if (!expert_offsets || !start || !expert || !offset || E < 1 || P < 1) return -1;
+    const int64_t S = expert_offsets[E];
+    for (int32_t e = 0; e < E; ++e)
+        if (expert_offsets[e + 1] < expert_offsets[e]) return -2;
+    for (int32_t p = 0; p <= P; ++p) {
+        /* [UBEP sec. 3.3, token-level load partition] equal contiguous slices:
+         * slice p is [floor(p*S/P), floor((p+1)*S/P)), sizes differ by <= 1. */
+        start[p] = (p * S) / P;
+        if (p == P) break;
+        /* the expert whose cumulative range [offsets[e], offsets[e+1])
+         * covers the slice start, and the start's offset inside it; a start
+         * at S (an empty last slice) maps to expert E, offset 0 */
+        expert[p] = E;
+        offset[p] = 0;
+        for (int32_t e = 0; e < E; ++e) {
+            if (expert_offsets[e] <= start[p] && start[p] < expert_offsets[e + 1]) {
+                expert[p] = e;
+                offset[p] = start[p] - expert_offsets[e];
+                break;
+            }
+        }
+    }
+    return 0;
+}
+
+int ep_oracle_lpt(const double* cost, const int32_t* peer, int32_t U,
+                  const int32_t* cap_of_peer, int32_t npeer, int32_t C,
+                  int32_t* core, int32_t* stripe, double* load)
+{
+    if (!cost || !peer || !cap_of_peer || !core || !stripe || !load || U < 0 || C < 1 ||
+        npeer < 1)
+        return -1;
+    for (int32_t p = 0; p < npeer; ++p)
+        if (cap_of_peer[p] < 1) return -2;
+    for (int32_t j = 0; j < U; ++j)
+        if (peer[j] < 0 || peer[j] >= npeer) return -3;
+    /* [StrataCL sec. 6.2, App. B] LPT-style list scheduling: units in order
+     * of decreasing estimated cost (equal costs: lower index first), each to
+     * the least-loaded core (ties: lower index) whose next stripe still has
+     * room for the unit's peer under the fan-out cap.  A core issues at most
+     * one unit per stripe, so its next stripe is its count of stripes so far.
+     * When no core has room, the least-loaded core skips stripes (idle) until
+     * its next stripe has room. */
+    int32_t* order = (int32_t*)malloc(sizeof(int32_t) * (size_t)(U > 0 ? U : 1));
+    int32_t* next = (int32_t*)calloc((size_t)C, sizeof(int32_t));
+    /* fan-out counts per (stripe, peer).  A core's next stripe grows by one
+     * per unit it takes plus one per stripe it skips; a skipped stripe is full
+     * for some peer, and there are at most U such stripes, so 2U + 2 rows
+     * bound the table. */
+    const int64_t maxk = 2 * (int64_t)U + 2;
+    int32_t* fan = (int32_t*)calloc((size_t)(maxk * npeer), sizeof(int32_t));
+    if (!order || !next || !fan) { free(order); free(next); free(fan); return -4; }
+    for (int32_t j = 0; j < U; ++j) order[j] = j;
+    for (int32_t a = 1; a < U; ++a) {          /* insertion sort: stable */
+        const int32_t v = order[a];
+        int32_t b = a - 1;
+        while (b >= 0 && cost[order[b]] < cost[v]) { order[b + 1] = order[b]; --b; }
+        order[b + 1] = v;
+    }
+    for (int32_t c = 0; c < C; ++c) load[c] = 0.0;
+    int rc = 0;
+    for (int32_t i = 0; i < U; ++i) {
+        const int32_t j = order[i];
+        const int32_t p = peer[j];
+        int32_t best = -1;
+        for (int32_t c = 0; c < C; ++c) {
+            if (fan[(int64_t)next[c] * npeer + p] >= cap_of_peer[p]) continue;
+            if (best < 0 || load[c] < load[best]) best = c;
+        }
+        if (best < 0) {
+            for (int32_t c = 0; c < C; ++c)
+                if (best < 0 || load[c] < load[best]) best = c;
+            while (next[best] < maxk && fan[(int64_t)next[best] * npeer + p] >= cap_of_peer[p])
+                ++next[best];
+        }
+        if (next[best] >= maxk) { rc = -5; break; }
+        core[j] = best;
+        stripe[j] = next[best];
+        fan[(int64_t)next[best] * npeer + p] += 1;
+        next[best] += 1;
+        load[best] += cost[j];
+    }
+    free(order);
+    free(next);
+    free(fan);
+    return rc;
+}
