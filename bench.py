@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--partition-sweep", action="store_true",
+                    help="instead of the step: the window-copy consumer under per-peer, "
+                         "equal-slice and LPT schedules (one JSON line)")
     ap.add_argument("--sync-sweep", action="store_true",
                     help="instead of the step: the fused mode's synchronisation variants "
                          "against three launches, over the row size (one JSON line)")
@@ -115,6 +118,9 @@ def main():
         return
     if args.sync_sweep and args.gpus == 1:
         sync_sweep(args)
+        return
+    if args.partition_sweep and args.gpus == 1:
+        partition_sweep(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: the multi-GPU "
@@ -449,6 +455,105 @@ def sync_sweep(args):
     print(json.dumps({"sync_sweep": rows, "T": T, "E": E, "R": R, "k": k,
                       "steps": args.steps, "warmup": args.warmup,
                       "what": "layout + dispatch + combine latency (us) per call"}), flush=True)
+
+
+def partition_sweep(args):
+    """UBEP sec. 3.3 / StrataCL sec. 6.2 on one GPU: C persistent "cores"
+    copy the send buffer's peer windows (ep_window_copy) following (a) one core
+    per peer window, (b) equal slot slices from the GPU search
+    (ep_expert_slices), (c) StrataCL's LPT task lists (ep_lpt_partition);
+    reports the copy time and the per-core completion-time gap
+    (slowest - fastest) / slowest.  Prints one JSON line."""
+    import torch
+
+    from combine_ep_route_topk_amd import ep
+    from combine_ep_route_topk_amd import workloads as wl
+    import oracle
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    hip = ep.HipEvents()
+    set_events = ep.library().ep_set_timing_events
+    res = []
+    for name in ("dsv3", "glm45air", "incast"):
+        w = wl.WORKLOADS[name]
+        inp = wl.make_inputs(w, with_x=False)
+        idx, _ = oracle.route_topk(inp["logits"], w.k, 1)
+        lay = oracle.dispatch_layout(idx, w.E, w.R)
+        row_bytes = 2 * w.H
+        src = torch.randint(-30000, 30000, (w.S, w.H), dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        ro = lay["rank_offsets"]
+        eo_dev = torch.from_numpy(lay["expert_offsets"]).to(dev)
+        clock = torch.zeros(2 * 4096, dtype=torch.int64, device=dev)
+        bad = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def timed(C, **kw):
+            def call():
+                ep.ep_window_copy(src, dst, row_bytes, w.S, C, core_clock=clock[:2 * C], bad=bad,
+                                  stream=stream, **kw)
+            for _ in range(args.warmup):
+                call()
+            st, sp = hip.create(), hip.create()
+            times = []
+            for _ in range(args.steps):
+                set_events(st, sp)
+                call()
+                torch.cuda.synchronize()
+                times.append(hip.elapsed_ms(st, sp) * 1e3)
+            hip.destroy(st)
+            hip.destroy(sp)
+            ok = int(bad.item()) == 0 and torch.equal(dst, src)
+            c = clock[:2 * C].cpu().numpy().astype(np.float64)
+            t0 = c[0::2].min()
+            ends = c[1::2] - t0
+            gap = float((ends.max() - ends.min()) / ends.max()) if ends.max() > 0 else 0.0
+            return {"us": round(float(np.median(times)), 2), "core_gap": round(gap, 3),
+                    "gbps": round(2 * w.S * row_bytes / (np.median(times) * 1e-6) / 1e9, 1),
+                    "parity": ok}
+
+        row = {"workload": w.describe(), "rank_rows_min_max": [int(np.diff(ro).min()),
+                                                               int(np.diff(ro).max())]}
+        # (a) one core per peer window
+        tasks = np.zeros(w.R, ep.TASK_DTYPE)
+        tasks["peer"] = np.arange(w.R)
+        tasks["first_row"] = ro[:-1]
+        tasks["rows"] = np.diff(ro)
+        row["per_peer_C=R"] = timed(w.R, tasks=ep.tasks_to_device(tasks, dev),
+                                    core_begin=torch.arange(w.R + 1, dtype=torch.int64, device=dev))
+        for C in (w.R, 256):
+            # (b) equal slices: the search itself, then the copy
+            sl = ep.ep_expert_slices(eo_dev, C, stream=stream)
+            st, sp = hip.create(), hip.create()
+            set_events(st, sp)
+            ep.ep_expert_slices(eo_dev, C, out=sl, stream=stream)
+            torch.cuda.synchronize()
+            search_us = hip.elapsed_ms(st, sp) * 1e3
+            hip.destroy(st)
+            hip.destroy(sp)
+            r = timed(C, slice_start=sl["start"])
+            r["search_us"] = round(search_us, 2)
+            row[f"slices_C={C}"] = r
+            # (c) LPT task lists, units of 64 rows, cap C/8 units per peer and stripe
+            t0 = time.perf_counter()
+            tasks, core_begin, _ = ep.ep_lpt_partition(ro, row_bytes, 64, C, alpha=[2000.0],
+                                                       beta=[100.0], cap=[max(1, C // 8)])
+            host_us = (time.perf_counter() - t0) * 1e6
+            r = timed(C, tasks=ep.tasks_to_device(tasks, dev),
+                      core_begin=torch.from_numpy(core_begin).to(dev))
+            r["schedule_host_us"] = round(host_us, 1)
+            r["units"] = int(len(tasks))
+            row[f"lpt_C={C}"] = r
+            # (d) the same without a binding fan-out cap (C units of a peer per stripe)
+            tasks, core_begin, _ = ep.ep_lpt_partition(ro, row_bytes, 64, C, alpha=[2000.0],
+                                                       beta=[100.0], cap=[C])
+            row[f"lpt_nocap_C={C}"] = timed(C, tasks=ep.tasks_to_device(tasks, dev),
+                                            core_begin=torch.from_numpy(core_begin).to(dev))
+        res.append(row)
+        print(f"[partition] {json.dumps(row)}", file=sys.stderr, flush=True)
+        del src, dst
+    print(json.dumps({"partition_sweep": res, "steps": args.steps, "warmup": args.warmup,
+                      "what": "ep_window_copy of the send buffer (read + write S rows) per schedule"}),
+          flush=True)
 
 
 def cpu_baseline(w, inp, gpu_lay, seconds, step_bytes):

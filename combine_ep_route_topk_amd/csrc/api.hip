@@ -328,6 +328,90 @@ ep_status ep_fused_dispatch_combine(const uint16_t* x, const int32_t* topk_idx,
                                           spin_limit, ep::kSyncItemEvents, stream);
 }
 
+ep_status ep_expert_slices(const int32_t* expert_offsets, int32_t E, int32_t P, int64_t* start,
+                           int32_t* expert, int64_t* offset, void* stream)
+{
+    const char* fn = "ep_expert_slices";
+    TimingScope timing_scope;
+    if (E < 1 || E > (1 << 20)) return fail(EP_ERR_INVALID_ARG, "%s: E=%d must be in [1, 2^20]", fn, E);
+    if (P < 1 || P >= (1 << 24)) return fail(EP_ERR_INVALID_ARG, "%s: P=%d must be in [1, 2^24)", fn, P);
+    EP_REQUIRE_PTR(fn, expert_offsets, 4);
+    EP_REQUIRE_PTR(fn, start, 8);
+    EP_REQUIRE_PTR(fn, expert, 4);
+    EP_REQUIRE_PTR(fn, offset, 8);
+    return launched(ep::launch_slices(expert_offsets, E, P, start, expert, offset,
+                                      static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int64_t ep_lpt_task_count(const int32_t* rank_offsets, int32_t R, int64_t unit_rows)
+{
+    if (!rank_offsets || R < 1 || unit_rows < 1) return -1;
+    return ep::lpt_unit_count(rank_offsets, R, unit_rows);
+}
+
+ep_status ep_lpt_partition(const int32_t* rank_offsets, int32_t R, int64_t row_bytes,
+                           int64_t unit_rows, const int32_t* tier_of_peer, const double* alpha,
+                           const double* beta, const int32_t* cap, int32_t ntier, int32_t C,
+                           ep_task* tasks, int64_t max_tasks, int64_t* core_begin,
+                           double* core_load)
+{
+    const char* fn = "ep_lpt_partition";
+    if (!rank_offsets || !alpha || !beta || !cap || !core_begin || (!tasks && max_tasks > 0))
+        return fail(EP_ERR_INVALID_ARG, "%s: a required pointer is NULL", fn);
+    if (R < 1 || ntier < 1 || C < 1 || unit_rows < 1 || row_bytes < 1)
+        return fail(EP_ERR_INVALID_ARG, "%s: R=%d ntier=%d C=%d unit_rows=%lld row_bytes=%lld "
+                    "must all be >= 1", fn, R, ntier, C, (long long)unit_rows, (long long)row_bytes);
+    for (int32_t p = 0; p < R; ++p) {
+        if (rank_offsets[p + 1] < rank_offsets[p] || rank_offsets[p] < 0)
+            return fail(EP_ERR_INVALID_ARG, "%s: rank_offsets must be non-decreasing and >= 0", fn);
+        if (tier_of_peer && (tier_of_peer[p] < 0 || tier_of_peer[p] >= ntier))
+            return fail(EP_ERR_INVALID_ARG, "%s: tier_of_peer[%d]=%d outside [0, %d)", fn, p,
+                        tier_of_peer[p], ntier);
+    }
+    for (int32_t t = 0; t < ntier; ++t)
+        if (!(beta[t] > 0.0) || cap[t] < 1)
+            return fail(EP_ERR_INVALID_ARG, "%s: tier %d needs beta > 0 and cap >= 1", fn, t);
+    const int64_t need = ep::lpt_unit_count(rank_offsets, R, unit_rows);
+    if (max_tasks < need)
+        return fail(EP_ERR_INVALID_ARG, "%s: max_tasks=%lld, %lld units are needed", fn,
+                    (long long)max_tasks, (long long)need);
+    ep::lpt_partition(rank_offsets, R, row_bytes, unit_rows, tier_of_peer, alpha, beta, cap, C,
+                      tasks, max_tasks, core_begin, core_load);
+    return ok();
+}
+
+ep_status ep_window_copy(const void* src, void* dst, int64_t row_bytes, int64_t S,
+                         const ep_task* tasks, const int64_t* core_begin,
+                         const int64_t* slice_start, int32_t C, uint64_t* core_clock,
+                         uint32_t* bad, void* stream)
+{
+    const char* fn = "ep_window_copy";
+    TimingScope timing_scope;
+    if (row_bytes < 16 || row_bytes % 16 != 0)
+        return fail(EP_ERR_INVALID_ARG, "%s: row_bytes=%lld must be a positive multiple of 16", fn,
+                    (long long)row_bytes);
+    if (S < 0 || C < 1 || uint32_t(C) > ep::kMaxGrid)
+        return fail(EP_ERR_INVALID_ARG, "%s: S=%lld must be >= 0 and C=%d in [1, 2^20]", fn,
+                    (long long)S, C);
+    if (!tasks == !slice_start)
+        return fail(EP_ERR_INVALID_ARG, "%s: give either tasks (with core_begin) or slice_start", fn);
+    if (tasks) {
+        EP_REQUIRE_PTR(fn, tasks, 8);
+        EP_REQUIRE_PTR(fn, core_begin, 8);
+    } else {
+        EP_REQUIRE_PTR(fn, slice_start, 8);
+    }
+    EP_REQUIRE_PTR(fn, src, 16);
+    EP_REQUIRE_PTR(fn, dst, 16);
+    if (core_clock && !aligned(core_clock, 8))
+        return fail(EP_ERR_INVALID_ARG, "%s: core_clock is not 8-byte aligned", fn);
+    if (bad && !aligned(bad, 4)) return fail(EP_ERR_INVALID_ARG, "%s: bad is not 4-byte aligned", fn);
+    return launched(ep::launch_window_copy(src, dst, row_bytes, S, tasks, core_begin, slice_start,
+                                           C, core_clock, bad, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 ep_status ep_get_device_error(const void* workspace, void* stream)
 {
     const char* fn = "ep_get_device_error";

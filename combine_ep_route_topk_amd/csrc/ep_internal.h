@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/ep_route_topk.h"
+
 namespace ep {
 
 // One-shot measurement hook (ep_set_timing_events): when set, the next
@@ -195,5 +197,20 @@ hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float*
                         int32_t* rank_offsets, int32_t* pos, uint8_t* send_rows,
                         uint16_t* out, void* ws, uint32_t spin_limit, int grid, int sync,
                         hipStream_t s);
+
+hipError_t launch_slices(const int32_t* eo, int E, int P, int64_t* start, int32_t* expert,
+                         int64_t* offset, hipStream_t s);
+
+hipError_t launch_window_copy(const void* src, void* dst, int64_t row_bytes, int64_t S,
+                              const ep_task* tasks, const int64_t* core_begin,
+                              const int64_t* slice_start, int C, uint64_t* core_clock,
+                              uint32_t* bad, hipStream_t s);
+
+int64_t lpt_unit_count(const int32_t* rank_offsets, int R, int64_t unit_rows);
+
+int64_t lpt_partition(const int32_t* rank_offsets, int R, int64_t row_bytes, int64_t unit_rows,
+                      const int32_t* tier_of_peer, const double* alpha, const double* beta,
+                      const int32_t* cap, int C, ep_task* tasks, int64_t max_tasks,
+                      int64_t* core_begin, double* core_load);
 
 }  // namespace ep

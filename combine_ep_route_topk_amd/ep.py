@@ -14,6 +14,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as _np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +54,12 @@ _SIGS = {
                                         _P, _P, _P, _P, _P, _sz,
                                         ctypes.POINTER(ctypes.c_uint64), _u32, _i32, _P],
                                        ctypes.c_int),
+    "ep_expert_slices": ([_P, _i32, _i32, _P, _P, _P, _P], ctypes.c_int),
+    "ep_lpt_task_count": ([_P, _i32, ctypes.c_int64], ctypes.c_int64),
+    "ep_lpt_partition": ([_P, _i32, ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P, _i32, _i32,
+                          _P, ctypes.c_int64, _P, _P], ctypes.c_int),
+    "ep_window_copy": ([_P, _P, ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _i32, _P, _P, _P],
+                       ctypes.c_int),
     "ep_get_device_error": ([_P, _P], ctypes.c_int),
     "ep_set_timing_events": ([_P, _P], ctypes.c_int),
 }
@@ -311,6 +318,87 @@ def ep_fused_dispatch_combine(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: t
     if want_epoch:
         out["epoch"] = int(ep.value)
     return out
+
+
+# ------------------------------------------------------------------- partition
+# ep_task as a numpy record (host) / raw bytes (device): 32 bytes per task
+TASK_DTYPE = _np.dtype([("peer", "<i4"), ("stripe", "<i4"), ("first_row", "<i8"),
+                        ("rows", "<i8"), ("cost", "<f8")])
+
+
+def ep_expert_slices(expert_offsets: torch.Tensor, P: int, out: dict | None = None,
+                     stream=None) -> dict:
+    """expert_offsets i32 [E+1] (device) -> dict(start i64 [P+1], expert i32 [P],
+    offset i64 [P]): P equal contiguous slot slices and their covering experts."""
+    _need(expert_offsets, "expert_offsets", torch.int32)
+    E = expert_offsets.numel() - 1
+    dev = expert_offsets.device
+    if out is None:
+        out = dict(start=torch.empty(P + 1, dtype=torch.int64, device=dev),
+                   expert=torch.empty(P, dtype=torch.int32, device=dev),
+                   offset=torch.empty(P, dtype=torch.int64, device=dev))
+    _need(out["start"], "start", torch.int64, (P + 1,))
+    _need(out["expert"], "expert", torch.int32, (P,))
+    _need(out["offset"], "offset", torch.int64, (P,))
+    _check(_lib.ep_expert_slices(_ptr(expert_offsets), E, P, _ptr(out["start"]),
+                                 _ptr(out["expert"]), _ptr(out["offset"]), _P(_stream(stream, dev))))
+    return out
+
+
+def ep_lpt_partition(rank_offsets, row_bytes: int, unit_rows: int, C: int, alpha=(0.0,),
+                     beta=(1.0,), cap=(1,), tier_of_peer=None):
+    """HOST scheduler.  rank_offsets: host int32 [R+1] (numpy or CPU tensor).
+    Returns (tasks: numpy TASK_DTYPE [U] grouped by core in stripe order,
+    core_begin: int64 [C+1], core_load: float64 [C])."""
+    ro = _np.ascontiguousarray(_np.asarray(rank_offsets, dtype=_np.int32))
+    R = ro.size - 1
+    alpha = _np.ascontiguousarray(alpha, dtype=_np.float64)
+    beta = _np.ascontiguousarray(beta, dtype=_np.float64)
+    cap = _np.ascontiguousarray(cap, dtype=_np.int32)
+    tier = None if tier_of_peer is None else _np.ascontiguousarray(tier_of_peer, dtype=_np.int32)
+    n = int(_lib.ep_lpt_task_count(_P(ro.ctypes.data), R, unit_rows))
+    if n < 0:
+        raise ValueError("bad rank_offsets or unit_rows")
+    tasks = _np.zeros(max(n, 1), TASK_DTYPE)
+    core_begin = _np.zeros(C + 1, _np.int64)
+    load = _np.zeros(C, _np.float64)
+    _check(_lib.ep_lpt_partition(
+        _P(ro.ctypes.data), R, row_bytes, unit_rows,
+        _P(tier.ctypes.data) if tier is not None else None, _P(alpha.ctypes.data),
+        _P(beta.ctypes.data), _P(cap.ctypes.data), alpha.size, C, _P(tasks.ctypes.data), n,
+        _P(core_begin.ctypes.data), _P(load.ctypes.data)))
+    return tasks[:n], core_begin, load
+
+
+def tasks_to_device(tasks, device) -> torch.Tensor:
+    """A TASK_DTYPE array as raw bytes on the device (the ep_task layout)."""
+    raw = _np.ascontiguousarray(tasks).view(_np.uint8)
+    return torch.from_numpy(raw.copy()).to(device)
+
+
+def ep_window_copy(src: torch.Tensor, dst: torch.Tensor, row_bytes: int, S: int, C: int,
+                   tasks: torch.Tensor | None = None, core_begin: torch.Tensor | None = None,
+                   slice_start: torch.Tensor | None = None, core_clock: torch.Tensor | None = None,
+                   bad: torch.Tensor | None = None, stream=None) -> None:
+    """C persistent cores copy src -> dst rows following task lists (tasks as
+    raw ep_task bytes + core_begin i64 [C+1]) or slices (slice_start i64 [C+1])."""
+    for t, name in ((src, "src"), (dst, "dst")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+        if t.numel() * t.element_size() < S * row_bytes:
+            raise ValueError(f"{name} holds fewer than S rows")
+    if tasks is not None:
+        _need(tasks, "tasks", torch.uint8)
+        _need(core_begin, "core_begin", torch.int64, (C + 1,))
+    if slice_start is not None:
+        _need(slice_start, "slice_start", torch.int64, (C + 1,))
+    if core_clock is not None:
+        _need(core_clock, "core_clock", torch.int64, (2 * C,))
+    if bad is not None:
+        _need(bad, "bad", torch.int32, (1,))
+    _check(_lib.ep_window_copy(_ptr(src), _ptr(dst), row_bytes, S, _ptr(tasks), _ptr(core_begin),
+                               _ptr(slice_start), C, _ptr(core_clock), _ptr(bad),
+                               _P(_stream(stream, src.device))))
 
 
 # ------------------------------------------------------------------- bound calls

@@ -194,6 +194,82 @@ ep_status ep_dispatch_grad(const uint16_t* grad_send, const int32_t* pos, int32_
                            int32_t H, int32_t k, uint16_t* grad_x, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Skew-balanced work partition for consumers of the send buffer.
+ *
+ * ep_expert_slices  [UBEP sec. 3.3, "Token-level Load Partition" and
+ * Algorithm 1] cuts the S = expert_offsets[E] slots into P equal contiguous
+ * slices -- slice p is [floor(p*S/P), floor((p+1)*S/P)), so sizes differ by at
+ * most one slot however skewed the experts are -- and maps each slice start
+ * to the expert whose cumulative range covers it.
+ *   expert_offsets i32 [E+1]  device, non-decreasing (ep_dispatch_layout's).
+ *   start          i64 [P+1]  out: slice starts; start[P] = S.
+ *   expert         i32 [P]    out: e with expert_offsets[e] <= start[p] <
+ *                             expert_offsets[e+1]; E when start[p] = S.
+ *   offset         i64 [P]    out: start[p] - expert_offsets[expert[p]] (0 for E).
+ * Sizes: 1 <= E <= 2^20, 1 <= P < 2^24.
+ * ------------------------------------------------------------------------- */
+ep_status ep_expert_slices(const int32_t* expert_offsets, int32_t E, int32_t P, int64_t* start,
+                           int32_t* expert, int64_t* offset, void* stream);
+
+/* One transfer unit of a per-core task list: rows [first_row, first_row +
+ * rows) of the send buffer, destined to virtual rank `peer`, issued by its
+ * core in issue stripe `stripe`, with estimated cost `cost`. */
+typedef struct {
+    int32_t peer;
+    int32_t stripe;
+    int64_t first_row;
+    int64_t rows;
+    double cost;
+} ep_task;
+
+/* Number of transfer units ep_lpt_partition makes: sum over the R peers of
+ * ceil(window rows / unit_rows).  rank_offsets is a HOST array [R+1]. */
+int64_t ep_lpt_task_count(const int32_t* rank_offsets, int32_t R, int64_t unit_rows);
+
+/* ---------------------------------------------------------------------------
+ * ep_lpt_partition  [StrataCL sec. 6.2 and App. B] -- HOST function, all
+ * pointers are host memory.  Peer p's window [rank_offsets[p],
+ * rank_offsets[p+1]) is cut into units of unit_rows rows (the last may be
+ * shorter); a unit of n rows for a peer of tier t costs
+ * alpha[t] + n * row_bytes / beta[t].  Units are assigned longest first
+ * (equal costs: peer-major, then row order) to the least-loaded core (ties:
+ * lower core index) whose next issue stripe has fewer than cap[t] units for
+ * that peer; a core issues one unit per stripe, and when no core has room the
+ * least-loaded one skips stripes until one has.
+ *   tier_of_peer  i32 [R] in [0, ntier), or NULL: every peer is tier 0.
+ *   alpha, beta   f64 [ntier], beta > 0;  cap  i32 [ntier], >= 1.
+ *   tasks         out [max_tasks]: grouped by core, each core's in stripe
+ *                 order; core c owns tasks[core_begin[c] .. core_begin[c+1]).
+ *   core_begin    i64 [C+1] out;  core_load  f64 [C] out (may be NULL).
+ * max_tasks below ep_lpt_task_count() is EP_ERR_INVALID_ARG.
+ * ------------------------------------------------------------------------- */
+ep_status ep_lpt_partition(const int32_t* rank_offsets, int32_t R, int64_t row_bytes,
+                           int64_t unit_rows, const int32_t* tier_of_peer, const double* alpha,
+                           const double* beta, const int32_t* cap, int32_t ntier, int32_t C,
+                           ep_task* tasks, int64_t max_tasks, int64_t* core_begin,
+                           double* core_load);
+
+/* ---------------------------------------------------------------------------
+ * ep_window_copy -- a consumer that follows a partition: C persistent
+ * workgroups ("cores"); core c copies, from src to dst (two buffers of S rows
+ * of row_bytes bytes, the same layout), either the rows of its tasks
+ * tasks[core_begin[c] .. core_begin[c+1]) in order, or -- when tasks is
+ * NULL -- its slice [slice_start[c], slice_start[c+1]) (ep_expert_slices with
+ * P = C).  The one-GPU stand-in for the per-peer transfers that the
+ * partitions schedule [StrataCL sec. 6.2; UBEP sec. 3.3].
+ *   tasks, core_begin, slice_start  device arrays.
+ *   core_clock  u64 [2C] device, may be NULL: each core's start and end time
+ *               on the GPU's constant-rate wall clock (wall_clock64).
+ *   bad         u32 device counter, may be NULL: incremented for every task
+ *               or slice that lies outside [0, S) rows (it is skipped).
+ * row_bytes: a positive multiple of 16; buffers 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+ep_status ep_window_copy(const void* src, void* dst, int64_t row_bytes, int64_t S,
+                         const ep_task* tasks, const int64_t* core_begin,
+                         const int64_t* slice_start, int32_t C, uint64_t* core_clock,
+                         uint32_t* bad, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Fused flag-in-payload mode: layout + dispatch + combine with identity
  * experts in ONE persistent launch, no kernel-boundary barrier.  [UBEP sec.
  * 3.2] tasks wait on published data instead of global barriers; [UBEP sec.

@@ -123,6 +123,13 @@ inline void __syncthreads() { emu::yield_op(emu::OP_SYNC, 0, 0); }
 inline int __popcll(unsigned long long x) { return __builtin_popcountll(x); }
 inline int __ffsll(unsigned long long x) { return __builtin_ffsll((long long)x); }
 inline int __clz(int x) { return x == 0 ? 32 : __builtin_clz((unsigned)x); }
+inline int __clzll(long long x) { return x == 0 ? 64 : __builtin_clzll((unsigned long long)x); }
+// The GPU's constant-rate wall clock: here the host's steady clock in 10 ns ticks.
+#include <chrono>
+inline long long wall_clock64() {
+    return std::chrono::duration_cast<std::chrono::nanoseconds>(
+               std::chrono::steady_clock::now().time_since_epoch()).count() / 10;
+}
 inline float __uint_as_float(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
 #define __HIP_MEMORY_SCOPE_AGENT 3
 template <class T> inline T emu_atomic_load(const T* p) {

@@ -296,3 +296,51 @@ def test_emulated_sentinel_collision_is_reported(emu):
     for sync in (0, 1, 2, 4):
         _, st = m.fused(bad, o_idx, o_w, sync=sync)
         assert st == 0
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_emulated_slices_and_window_copy(emu, seed):
+    """UBEP sec. 3.3 slices from the emulated search kernel equal the oracle's;
+    the window-copy consumer copies every row once, following slices or task
+    lists, and skips (and counts) a task outside the buffer."""
+    rng = np.random.default_rng(900 + seed)
+    E = int(rng.integers(1, 700))
+    counts = rng.integers(0, 9, size=E)
+    counts[rng.random(E) < 0.4] = 0
+    eo = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    S = int(eo[-1])
+    for P in (1, 5, 64, 130, S + 3):
+        start = np.zeros(P + 1, np.int64)
+        expert = np.zeros(P, np.int32)
+        offset = np.zeros(P, np.int64)
+        rc = emu.ep_expert_slices(p(eo), E, P, p(start), p(expert), p(offset), None)
+        assert rc == 0, emu.ep_last_error().decode()
+        o_start, o_expert, o_offset = oracle.slices(eo, P)
+        assert np.array_equal(start, o_start) and np.array_equal(expert, o_expert)
+        assert np.array_equal(offset, o_offset)
+    # the consumer, on S rows of 48 bytes
+    row_bytes = 48
+    src = aligned(S * row_bytes + 16, 16)[:max(S * row_bytes, 16)]
+    src[:] = rng.integers(0, 256, size=src.size, dtype=np.uint8)
+    C = 6
+    start, _, _ = oracle.slices(eo, C)
+    dst = aligned(src.size, 16)
+    bad = np.zeros(1, np.uint32)
+    rc = emu.ep_window_copy(p(src), p(dst), ctypes.c_int64(row_bytes), ctypes.c_int64(S), None,
+                            None, p(start), C, None, p(bad), None)
+    assert rc == 0 and bad[0] == 0
+    assert np.array_equal(dst[:S * row_bytes], src[:S * row_bytes])
+    # task lists: rows in pieces of 5 over 3 cores, plus one task past the end
+    rows = [(r, min(5, S - r)) for r in range(0, S, 5)] + [(S, 2)]
+    tasks = np.zeros(len(rows), dtype=[("peer", "<i4"), ("stripe", "<i4"), ("first_row", "<i8"),
+                                       ("rows", "<i8"), ("cost", "<f8")])
+    tasks["first_row"] = [r for r, _ in rows]
+    tasks["rows"] = [n for _, n in rows]
+    core_begin = np.array([0, len(rows) // 3, 2 * len(rows) // 3, len(rows)], np.int64)
+    dst[:] = 0
+    clock = np.zeros(6, np.uint64)
+    rc = emu.ep_window_copy(p(src), p(dst), ctypes.c_int64(row_bytes), ctypes.c_int64(S),
+                            p(tasks), p(core_begin), None, 3, p(clock), p(bad), None)
+    assert rc == 0 and bad[0] == 1
+    assert np.array_equal(dst[:S * row_bytes], src[:S * row_bytes])
+    assert np.all(clock[1::2] >= clock[0::2])

@@ -1,0 +1,107 @@
+"""GPU parity of the skew-balanced partition (UBEP sec. 3.3, Algorithm 1) and
+of the window-copy consumer that follows either partition (StrataCL sec. 6.2):
+slices bit-exact against the oracle on every workload's layout and on
+random, empty-expert and more-workers-than-slots cases; every row copied
+exactly once under slices, LPT task lists and a per-peer schedule; a task
+outside the buffer skipped and counted."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from combine_ep_route_topk_amd import workloads as wl
+
+from gpu_util import DEV, Case, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def epm():
+    from combine_ep_route_topk_amd import ep as mod
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return mod
+
+
+def check_slices(epm, eo, P):
+    out = epm.ep_expert_slices(torch.from_numpy(eo).to(DEV), P)
+    torch.cuda.synchronize()
+    o_start, o_expert, o_offset = oracle.slices(eo, P)
+    assert np.array_equal(out["start"].cpu().numpy(), o_start)
+    assert np.array_equal(out["expert"].cpu().numpy(), o_expert)
+    assert np.array_equal(out["offset"].cpu().numpy(), o_offset)
+
+
+@pytest.mark.parametrize("name", wl.ORDER)
+def test_slices_on_workload_layouts(epm, name):
+    c = Case(wl.WORKLOADS[name])
+    say(f"slices {c.w.describe()}")
+    for P in (1, 7, 64, 256, 1000):
+        check_slices(epm, c.lay["expert_offsets"], P)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_slices_random_and_degenerate(epm, seed):
+    rng = np.random.default_rng(1200 + seed)
+    E = int(rng.integers(1, 1025))
+    counts = rng.integers(0, 50, size=E)
+    counts[rng.random(E) < 0.5] = 0
+    eo = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    S = int(eo[-1])
+    say(f"slices random E={E} S={S}")
+    for P in (1, 3, 64, 65, 4097, S + 5):
+        check_slices(epm, eo, P)
+    check_slices(epm, np.zeros(E + 1, np.int32), 9)          # no slots at all
+
+
+def run_copy(epm, src, S, row_bytes, C, **kw):
+    dst = torch.zeros_like(src)
+    clock = torch.zeros(2 * C, dtype=torch.int64, device=DEV)
+    bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+    epm.ep_window_copy(src, dst, row_bytes, S, C, core_clock=clock, bad=bad, **kw)
+    torch.cuda.synchronize()
+    return dst, clock.cpu().numpy(), int(bad.item())
+
+
+@pytest.mark.parametrize("name", ["glm45air", "incast"])
+def test_window_copy_follows_every_schedule(epm, name):
+    c = Case(wl.WORKLOADS[name])
+    w = c.w
+    row_bytes = 2 * w.H
+    say(f"window copy {w.describe()}")
+    send = torch.from_numpy(c.send.view(np.int16)).to(DEV)
+    ref = send.clone()
+    ro = c.lay["rank_offsets"]
+    for C in (w.R, 256):
+        # slices from the GPU search
+        sl = epm.ep_expert_slices(torch.from_numpy(c.lay["expert_offsets"]).to(DEV), C)
+        dst, clock, bad = run_copy(epm, send, w.S, row_bytes, C, slice_start=sl["start"])
+        assert bad == 0 and torch.equal(dst, ref)
+        assert np.all(clock[1::2] >= clock[0::2])
+        # LPT task lists
+        tasks, core_begin, load = epm.ep_lpt_partition(ro, row_bytes, 256, C, alpha=[2000.0],
+                                                       beta=[100.0], cap=[max(1, C // 8)])
+        dst, _, bad = run_copy(epm, send, w.S, row_bytes, C,
+                               tasks=epm.tasks_to_device(tasks, DEV),
+                               core_begin=torch.from_numpy(core_begin).to(DEV))
+        assert bad == 0 and torch.equal(dst, ref)
+    # one core per peer window
+    tasks = np.zeros(w.R, epm.TASK_DTYPE)
+    tasks["peer"] = np.arange(w.R)
+    tasks["first_row"] = ro[:-1]
+    tasks["rows"] = np.diff(ro)
+    dst, _, bad = run_copy(epm, send, w.S, row_bytes, w.R, tasks=epm.tasks_to_device(tasks, DEV),
+                           core_begin=torch.arange(w.R + 1, dtype=torch.int64, device=DEV))
+    assert bad == 0 and torch.equal(dst, ref)
+
+
+def test_window_copy_skips_tasks_outside_the_buffer(epm):
+    S, row_bytes, C = 1000, 64, 4
+    src = torch.randint(-128, 127, (S * row_bytes,), dtype=torch.int8, device=DEV)
+    tasks = np.zeros(6, epm.TASK_DTYPE)
+    tasks["first_row"] = [0, 250, 500, 750, 990, -3]
+    tasks["rows"] = [250, 250, 250, 250, 20, 5]              # the last two leave [0, S)
+    say("window copy with tasks outside the buffer")
+    dst, _, bad = run_copy(epm, src, S, row_bytes, C, tasks=epm.tasks_to_device(tasks, DEV),
+                           core_begin=torch.tensor([0, 1, 2, 3, 6], dtype=torch.int64, device=DEV))
+    assert bad == 2 and torch.equal(dst, src)
