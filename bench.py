@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-pipelined", action="store_true")
     ap.add_argument("--partition-sweep", action="store_true",
                     help="instead of the step: the window-copy consumer under per-peer, "
                          "equal-slice and LPT schedules (one JSON line)")
@@ -231,6 +232,17 @@ def main():
     if not args.no_isolated:
         result["isolated"] = bench_isolated(ep, torch, hip, ops, names, set_events, dev, stream)
 
+    if not args.no_pipelined:
+        ms_p, ok_p, enq_p = bench_pipelined(ep, torch, w, logits, x, dev, K, args.warmup)
+        result["pipelined"] = {
+            "ms_per_step": round(ms_p, 4),
+            "host_enqueue_ms_per_step": round(enq_p, 4),
+            "value": round(step_bytes / (ms_p * 1e-3) / 1e9, 1) if ok_p else None,
+            "tokens_per_s": round(T / (ms_p * 1e-3), 1) if ok_p else None,
+            "parity": ok_p,
+            "what": "route + layout of the next batch on a second stream during this batch's "
+                    "dispatch and combine; every step still runs all four ops"}
+
     if not args.no_fused:
         result["fused"] = bench_fused(ep, torch, w, x, idx, wt, stream, K, args.warmup)
 
@@ -242,6 +254,67 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, inp, lay, args.cpu_seconds, step_bytes)
 
     print(json.dumps(result), flush=True)
+
+
+def bench_pipelined(ep, torch, w, logits, x, dev, K, W):
+    """Steps whose preprocessing is pipelined (UBEP sec. 5.2: the
+    preprocessing steps are pipelined with the transfers): route and layout of
+    batch i+1 run on a second stream while batch i's dispatch runs -- dispatch
+    fills only half the CUs -- and its combine.  Every step still runs all four
+    ops on its own batch; routing and layout outputs are double-buffered, and
+    stream events order each buffer's reuse.  Returns the wall time per step
+    and the parity of every step's output."""
+    T, H, E, R, k = w.T, w.H, w.E, w.R, w.k
+    s0 = torch.cuda.current_stream(dev)
+    s1 = torch.cuda.Stream(device=dev)             # default priority
+    buf = []
+    for _ in range(2):
+        b = {"idx": torch.empty((T, k), dtype=torch.int32, device=dev),
+             "wt": torch.empty((T, k), dtype=torch.float32, device=dev),
+             "lay": ep.layout_outputs(T, k, E, R, dev, slot_src=True)}
+        buf.append(b)
+    send = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    pre = [[ep.bind_route_topk(logits, k, True, b["idx"], b["wt"], s1),
+            ep.bind_dispatch_layout(b["idx"], E, R, b["lay"], s1)] for b in buf]
+    post = [[ep.bind_dispatch(x, b["lay"]["pos"], send, s0),
+             ep.bind_combine(send, b["lay"]["pos"], b["wt"], out, s0)] for b in buf]
+
+    def run(n):
+        lay_done = [torch.cuda.Event(), torch.cuda.Event()]
+        comb_done = [torch.cuda.Event(), torch.cuda.Event()]
+        s1.wait_stream(s0)
+        for op in pre[0]:
+            op()
+        lay_done[0].record(s1)
+        for i in range(n):
+            b = i % 2
+            s0.wait_event(lay_done[b])
+            for op in post[b]:
+                op()
+            comb_done[b].record(s0)
+            if i + 1 < n:
+                nb = (i + 1) % 2
+                if i >= 1:
+                    s1.wait_event(comb_done[nb])     # batch i-1 no longer reads buffer nb
+                for op in pre[nb]:
+                    op()
+                lay_done[nb].record(s1)
+        s0.wait_stream(s1)
+
+    run(W if W > 1 else 2)
+    torch.cuda.synchronize()
+    ok = torch.equal(out.view(torch.int16), x.view(torch.int16))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(K)
+    t_enq = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ok = ok and torch.equal(out.view(torch.int16), x.view(torch.int16))
+    for b in buf:
+        ok = ok and ep.ep_get_device_error(b["lay"]["workspace"]) == ep.EP_OK
+    return wall / K * 1e3, ok, t_enq / K * 1e3
 
 
 def make_step(ops, set_events):
