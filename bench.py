@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-pipelined", action="store_true")
+    ap.add_argument("--fused-modes", default="0,1,2,3,4",
+                    help="comma-separated fused synchronisation modes to time")
     ap.add_argument("--partition-sweep", action="store_true",
                     help="instead of the step: the window-copy consumer under per-peer, "
                          "equal-slice and LPT schedules (one JSON line)")
@@ -244,7 +246,8 @@ def main():
                     "dispatch and combine; every step still runs all four ops"}
 
     if not args.no_fused:
-        result["fused"] = bench_fused(ep, torch, w, x, idx, wt, stream, K, args.warmup)
+        result["fused"] = bench_fused(ep, torch, w, x, idx, wt, stream, K, args.warmup,
+                                      tuple(int(m) for m in args.fused_modes.split(",") if m))
 
     if not args.no_backward:
         result["backward"] = bench_backward(ep, torch, hip, set_events, w, x, lay, wt, send,
@@ -446,9 +449,9 @@ def time_fused(ep, torch, x, idx, wt, E, R, fz, stream, K, W, sync):
     return a.elapsed_time(b) * 1e3 / K
 
 
-def bench_fused(ep, torch, w, x, idx, wt, stream, K, W):
-    """The fused flag-in-payload mode, every synchronisation variant, on the
-    step's inputs (each call after the previous on one stream)."""
+def bench_fused(ep, torch, w, x, idx, wt, stream, K, W, modes=tuple(SYNC_MODES)):
+    """The fused flag-in-payload mode, the chosen synchronisation variants, on
+    the step's inputs (each call after the previous on one stream)."""
     T, H, E, R, k = w.T, w.H, w.E, w.R, w.k
     from combine_ep_route_topk_amd import workloads as wl
     ab = wl.algorithmic_bytes(w)
@@ -456,6 +459,8 @@ def bench_fused(ep, torch, w, x, idx, wt, stream, K, W):
     res = {}
     fz = ep.fused_outputs(T, H, k, E, R, x.device)
     for sync, name in SYNC_MODES.items():
+        if sync not in modes:
+            continue
         try:
             ep.ep_fused_dispatch_combine(x, idx, wt, E, R, out=fz, stream=stream, sync=sync)
         except ep.EpError as e:
