@@ -71,7 +71,8 @@ const char* ep_last_error(void);
  * RailWave's execution protocol times each run with GPU events around the
  * device work only).  After this call, the NEXT compute entry point called on
  * the same thread (ep_route_topk, ep_dispatch_layout, ep_dispatch, ep_combine,
- * ep_combine_grad, ep_dispatch_grad, ep_fused_dispatch_combine[_sync]) records `start_event` when its first kernel
+ * ep_combine_grad, ep_dispatch_grad, ep_fused_dispatch_combine[_sync],
+ * ep_expert_slices, ep_window_copy) records `start_event` when its first kernel
  * starts and `stop_event` when its last kernel ends, taken from the kernels'
  * own dispatch packets -- the same interval a kernel-trace profiler reports,
  * with no marker packet in between.  Either event may be NULL.  The hook then

@@ -116,8 +116,8 @@ SHAPES = [
     (600, 64, 256, 32, 8, 5),       # five layout tiles
     (1, 8, 1, 1, 1, 6),
     (3000, 24, 33, 3, 5, 7),        # fifteen tiles, odd E
-    (8192, 16, 1024, 8, 4, 8),      # 32768 counters: bases in the positions launch; fused: four scan items
-    (16384, 8, 1024, 8, 4, 9),      # 65536 counters: separate scan launch with look-back
+    (2560, 16, 1024, 8, 8, 8),      # 20480 counters: bases in the positions launch; fused: three scan items
+    (4608, 8, 1024, 8, 8, 9),       # 36864 counters: separate scan launch with look-back; fused: five
 ]
 
 
