@@ -126,7 +126,7 @@ def main():
         partition_sweep(args)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the multi-GPU "
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the multi-GPU "
                                    "exchange is not part of it; run with --gpus 1"}))
         sys.exit(2)
 
