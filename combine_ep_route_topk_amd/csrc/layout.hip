@@ -34,6 +34,7 @@
 //   offset = exclusive scan over e of sum_t cnt[e][t],
 // which costs each workgroup a 32 KiB read at T=4096, k=8, E=256 and saves a
 // launch and the look-back (measured on MI355X: layout 14.3 -> ~10 us).
+// A layout of a single tile runs all of it in one workgroup and one launch.
 #include "ep_device.h"
 #include "ep_internal.h"
 #include "ep_layout_dev.h"
@@ -167,13 +168,13 @@ __global__ __launch_bounds__(kBlock) void layout_pos_kernel(
     }
 }
 
-// Scan + positions in one launch, one workgroup per tile (see the header).
-// Experts are split contiguously, kExpPerThread per thread, so the scan over
-// experts is a thread-local run plus one block-wide scan.
+// Scan + positions of one tile by one workgroup (see the header).  Experts
+// are split contiguously, kExpPerThread per thread, so the scan over experts
+// is a thread-local run plus one block-wide scan.
 constexpr int kExpPerThread = kMaxE / kBlock;    // 4
 static_assert(kExpPerThread * kBlock == kMaxE, "expert split");
-__global__ __launch_bounds__(kBlock) void layout_scanpos_kernel(
-    const int32_t* __restrict__ topk_idx, int64_t S, int E, int R, int nTiles,
+__device__ __forceinline__ void scanpos_tile(
+    int tile, const int32_t* __restrict__ topk_idx, int64_t S, int E, int R, int nTiles,
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ local_rank,
     int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
@@ -185,7 +186,6 @@ __global__ __launch_bounds__(kBlock) void layout_scanpos_kernel(
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = lane_id();
-    const int tile = blockIdx.x;
 
     // per expert: its total over all tiles and its count before this tile.
     // Each round issues all its loads (kExpPerThread experts x 4 vectors of 4
@@ -292,6 +292,36 @@ __global__ __launch_bounds__(kBlock) void layout_scanpos_kernel(
     }
 }
 
+__global__ __launch_bounds__(kBlock) void layout_scanpos_kernel(
+    const int32_t* __restrict__ topk_idx, int64_t S, int E, int R, int nTiles,
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ local_rank,
+    int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
+    int32_t* __restrict__ pos, int32_t* __restrict__ slot_src, WsHeader* __restrict__ hdr)
+{
+    scanpos_tile(blockIdx.x, topk_idx, S, E, R, nTiles, cnt, local_rank, expert_counts,
+                 expert_offsets, rank_counts, rank_offsets, pos, slot_src, hdr);
+}
+
+// A layout of one tile (T*k <= kTileSlots, e.g. a decode batch): histogram,
+// scan and positions in ONE workgroup and one launch -- nothing crosses
+// workgroups, so the kernel boundary between hist and scan+positions is not
+// needed.  The workgroup's own stores of cnt and local_rank are visible to
+// its other threads after the barrier.
+__global__ __launch_bounds__(kBlock) void layout_single_kernel(
+    const int32_t* __restrict__ topk_idx, int64_t S, int E, int R,
+    int32_t* __restrict__ cnt, int32_t* __restrict__ local_rank,
+    int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
+    int32_t* __restrict__ pos, int32_t* __restrict__ slot_src, WsHeader* __restrict__ hdr)
+{
+    __shared__ int32_t hist[kWavesPerBlock][kMaxE];
+    hist_tile(topk_idx, S, E, 1, 0, cnt, local_rank, hist);
+    __syncthreads();
+    scanpos_tile(0, topk_idx, S, E, R, 1, cnt, local_rank, expert_counts, expert_offsets,
+                 rank_counts, rank_offsets, pos, slot_src, hdr);
+}
+
 }  // namespace
 
 hipError_t launch_dispatch_layout(const int32_t* topk_idx, int T, int k, int E, int R,
@@ -307,6 +337,12 @@ hipError_t launch_dispatch_layout(const int32_t* topk_idx, int T, int k, int E, 
     int32_t* base = reinterpret_cast<int32_t*>(w + p.off_base);
     int32_t* rank = reinterpret_cast<int32_t*>(w + p.off_rank);
 
+    if (p.nTiles == 1) {
+        EP_LAUNCH(layout_single_kernel, dim3(1), dim3(kBlock), 0, s, topk_idx, p.S, E, R, cnt,
+                  rank, expert_counts, expert_offsets, rank_counts, rank_offsets, pos, slot_src,
+                  hdr);
+        return hipGetLastError();
+    }
     EP_LAUNCH(layout_hist_kernel, dim3(p.nTiles), dim3(kBlock), 0, s,
                        topk_idx, p.S, E, p.nTiles, p.nScan, cnt, rank, status, hdr);
     hipError_t err = hipGetLastError();
