@@ -91,6 +91,7 @@ BACKWARD_EDGE = [
     (257, 520, 16, 4, 8, 304),      # k = 8 path, ragged segment, odd token count
     (64, 4096, 64, 64, 64, 305),    # the largest k
     (1000, 64, 256, 32, 8, 306),    # short rows, many tokens
+    (3, 1 << 20, 4, 2, 2, 307),     # H = 2^20 (maximum): 2 MiB rows
 ]
 
 

@@ -112,6 +112,7 @@ FUSED_EDGE = [
     (3000, 520, 33, 3, 5, 15),
     (64, 4096, 128, 16, 64, 16),   # k = 64
     (20000, 256, 16, 4, 8, 17),    # many items, k = 8 path, small rows
+    (3, 1 << 20, 4, 2, 2, 18),     # H = 2^20 (maximum): 2 MiB rows, 2048 chunk flags
 ]
 
 

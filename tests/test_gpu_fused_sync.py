@@ -71,6 +71,7 @@ SYNC_EDGE = [
     (3000, 520, 33, 3, 5, 34),
     (64, 4096, 128, 16, 64, 35),   # k = 64
     (20000, 256, 16, 4, 8, 36),    # many items, small rows
+    (3, 1 << 20, 4, 2, 2, 37),     # H = 2^20 (maximum): 2 MiB rows
 ]
 
 

@@ -151,6 +151,7 @@ EDGE = [
     (50000, 24, 8, 4, 2, 5),      # 98 tiles, ragged last tile
     (257, 520, 33, 3, 5, 6),      # odd E, odd H/8 = 65
     (64, 4096, 128, 16, 64, 7),   # k = 64 (maximum)
+    (3, 1 << 20, 4, 2, 2, 9),     # H = 2^20 (maximum): 2 MiB rows
 ]
 
 

@@ -54,6 +54,17 @@ def test_slices_random_and_degenerate(epm, seed):
     check_slices(epm, np.zeros(E + 1, np.int32), 9)          # no slots at all
 
 
+def test_slices_largest_expert_count(epm):
+    """E = 2^20 (the largest accepted): four search steps of 64 pivots."""
+    rng = np.random.default_rng(1300)
+    E = 1 << 20
+    counts = rng.integers(0, 3, size=E)
+    eo = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    say(f"slices E={E} S={int(eo[-1])}")
+    for P in (1, 17, 256):                 # the oracle scans linearly per worker
+        check_slices(epm, eo, P)
+
+
 def run_copy(epm, src, S, row_bytes, C, **kw):
     dst = torch.zeros_like(src)
     clock = torch.zeros(2 * C, dtype=torch.int64, device=DEV)
