@@ -161,3 +161,27 @@ def test_binding_refuses_cpu_tensors(ep):
     import torch
     with pytest.raises(ValueError, match="GPU"):
         ep.ep_route_topk(torch.zeros((4, 8)), 2)
+
+
+def test_header_is_plain_c_and_host_calls_work(tmp_path):
+    """A C99 program compiled against include/ep_route_topk.h (gcc, -pedantic
+    -Werror) and linked to the library: the boundary needs no C++ and no
+    torch; its host-side entry points (validation, sizes, the LPT scheduler)
+    run without a GPU."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    from combine_ep_route_topk_amd import ep
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lib_dir = os.path.dirname(ep.LIB_PATH)
+    exe = str(tmp_path / "abi_check")
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I", os.path.join(root, "include"),
+                    os.path.join(root, "tests", "c_abi", "abi_check.c"),
+                    "-L", lib_dir, "-lep_route_topk", "-Wl,-rpath," + lib_dir, "-o", exe],
+                   check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    assert "c abi ok" in r.stdout
