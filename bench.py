@@ -231,6 +231,8 @@ def main():
         "roofline": roofline,
     }
 
+    result["copy_achievable"] = copy_achievable(torch, dev, stream)
+
     if not args.no_isolated:
         result["isolated"] = bench_isolated(ep, torch, hip, ops, names, set_events, dev, stream)
 
@@ -398,6 +400,31 @@ def bench_backward(ep, torch, hip, set_events, w, x, lay, wt, send, dev, stream,
     res["what"] = "combine_grad -> dispatch_grad, identity experts, back to back"
     del grad_y, grad_w, grad_x
     return res
+
+
+def copy_achievable(torch, dev, stream, mib=448, reps=20):
+    """The "achievable" line beside the 8 TB/s peak: a plain device-to-device
+    copy of the send buffer's size (torch copy_), read + write bytes over its
+    median time."""
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        b.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    us = float(np.median(times))
+    del a, b
+    return {"gbps": round(2 * n / (us * 1e-6) / 1e9, 1), "us": round(us, 2),
+            "pct_of_peak": round(100 * 2 * n / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+            "what": f"torch copy_ of {mib} MiB, read + write bytes, median of {reps}"}
 
 
 def bench_isolated(ep, torch, hip, ops, names, set_events, dev, stream, reps=30):
