@@ -308,6 +308,9 @@ hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* y,
     // need more waves than dispatch's plain copy to keep the write path busy
     // (measured on MI355X at T=4096, H=7168, k=8: 119 us with 128 workgroups,
     // 90.7 us with 192, 93-95 us with 256-1024).
+    // a small batch: one vector per lane on an uncapped grid, as in dispatch
+    if (small_scatter(T, H, k))
+        return launch_scatter<1>(grad_out, pos, w, T, nvec, k, grad_y, kMaxGrid, s);
     const uint32_t cap = dispatch_grid_cap() * 3 / 2;
     if (nvec % (kWave * 7) == 0) return launch_scatter<7>(grad_out, pos, w, T, nvec, k, grad_y, cap, s);
     if (nvec >= kWave * 8) return launch_scatter<8>(grad_out, pos, w, T, nvec, k, grad_y, cap, s);

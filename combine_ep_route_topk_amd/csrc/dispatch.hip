@@ -99,11 +99,10 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(
 
 template <int U>
 hipError_t launch_u(const uint16_t* x, int T, int nvec, int k, const int32_t* pos,
-                    uint16_t* send, hipStream_t s)
+                    uint16_t* send, uint32_t cap, hipStream_t s)
 {
     const uint32_t segs = uint32_t((nvec + kWave * U - 1) / (kWave * U));
     const uint32_t items = uint32_t((T + kWavesPerBlock - 1) / kWavesPerBlock) * segs;
-    const uint32_t cap = dispatch_grid_cap();
     const uint32_t grid = items < cap ? items : cap;
     EP_LAUNCH((dispatch_kernel<U>), dim3(grid), dim3(kBlock), 0, s, x, T, nvec, k, pos,
               send, segs, items);
@@ -128,14 +127,24 @@ uint32_t dispatch_grid_cap() {
     return cached[slot];
 }
 
+bool small_scatter(int T, int H, int k)
+{
+    return int64_t(T) * k * H * 2 <= kSmallScatterBytes;
+}
+
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int k, const int32_t* pos,
                            uint16_t* send, hipStream_t s)
 {
     const int nvec = H / 8;                   // 16-byte vectors per row
-    if (nvec % (kWave * 7) == 0) return launch_u<7>(x, T, nvec, k, pos, send, s);
-    if (nvec >= kWave * 8) return launch_u<8>(x, T, nvec, k, pos, send, s);
-    if (nvec >= kWave * 4) return launch_u<4>(x, T, nvec, k, pos, send, s);
-    return launch_u<1>(x, T, nvec, k, pos, send, s);
+    // A small batch is bound by latency, not by the write path: one vector per
+    // lane and an uncapped grid put the most requests in flight (measured on
+    // MI355X at T=128, H=7168, k=8: 8.2 -> 5.0 us).
+    if (small_scatter(T, H, k)) return launch_u<1>(x, T, nvec, k, pos, send, kMaxGrid, s);
+    const uint32_t cap = dispatch_grid_cap();
+    if (nvec % (kWave * 7) == 0) return launch_u<7>(x, T, nvec, k, pos, send, cap, s);
+    if (nvec >= kWave * 8) return launch_u<8>(x, T, nvec, k, pos, send, cap, s);
+    if (nvec >= kWave * 4) return launch_u<4>(x, T, nvec, k, pos, send, cap, s);
+    return launch_u<1>(x, T, nvec, k, pos, send, cap, s);
 }
 
 }  // namespace ep

@@ -153,6 +153,10 @@ inline size_t fused_row_stride(int H) {
 // Grid cap of the kernels that scatter whole rows (dispatch, the backward
 // combine's gradient scatter): half the CU count of the current device.
 uint32_t dispatch_grid_cap();
+// Scatters writing at most this many bytes are latency-bound: they run one
+// vector per lane on an uncapped grid instead.
+constexpr int64_t kSmallScatterBytes = int64_t(64) << 20;
+bool small_scatter(int T, int H, int k);
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int normalize,
                              int32_t* topk_idx, float* topk_w, hipStream_t s);
