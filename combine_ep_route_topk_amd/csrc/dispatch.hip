@@ -15,6 +15,8 @@
 // write-back of ~32 MB of dirty lines in front of the next kernel (measured
 // on MI355X at T=4096, H=7168, k=8: the route/layout/dispatch/combine step
 // 213 -> 205 us).
+#include <atomic>
+
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -111,20 +113,24 @@ hipError_t launch_u(const uint16_t* x, int T, int nvec, int k, const int32_t* po
 
 }  // namespace
 
-// Half the CU count of the current device (cached per device).
+// Half the CU count of the current device (cached per device; the cache
+// entries are atomic, so concurrent first calls from several threads are
+// safe -- they store the same value).
 uint32_t dispatch_grid_cap() {
-    static uint32_t cached[64] = {};
+    static std::atomic<uint32_t> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
     const int slot = dev < 64 ? dev : 63;
-    if (cached[slot] == 0) {
+    uint32_t v = cached[slot].load(std::memory_order_relaxed);
+    if (v == 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus < 2)
             cus = 256;
-        cached[slot] = uint32_t(cus / 2);
+        v = uint32_t(cus / 2);
+        cached[slot].store(v, std::memory_order_relaxed);
     }
-    return cached[slot];
+    return v;
 }
 
 bool small_scatter(int T, int H, int k)

@@ -56,6 +56,8 @@
 // of all finishes the per-expert / per-rank counts, records the error word
 // and resets the counters and the epoch for the next call (the workspace is
 // reused without a memset).
+#include <atomic>
+
 #include "ep_combine_dev.h"
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -820,13 +822,16 @@ __global__ __launch_bounds__(kBlock) void sentinel_reset_kernel(uint8_t* rows, i
         store16(rows + s * stride, v);
 }
 
+// Resident workgroups of the persistent kernel on the current device
+// (cached per device and instantiation; atomic entries, as above).
 int resident_grid(const void* kernel) {
-    static int cached[64][2] = {};
+    static std::atomic<int> cached[64][2];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
     const int slot = dev < 64 ? dev : 63;
     const int which = kernel == reinterpret_cast<const void*>(&fused_kernel<8>) ? 0 : 1;
-    if (cached[slot][which] > 0) return cached[slot][which];
+    const int have = cached[slot][which].load(std::memory_order_relaxed);
+    if (have > 0) return have;
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess ||
         per_cu < 1)
@@ -834,8 +839,8 @@ int resident_grid(const void* kernel) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 1)
         cus = 256;
-    cached[slot][which] = per_cu * cus;
-    return cached[slot][which];
+    cached[slot][which].store(per_cu * cus, std::memory_order_relaxed);
+    return per_cu * cus;
 }
 
 }  // namespace
