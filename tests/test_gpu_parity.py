@@ -236,3 +236,42 @@ def test_streams_are_respected(epm):
         out = epm.ep_combine(send, lay["pos"], wt, stream=s)
     s.synchronize()
     assert np.array_equal(bits(out), c.x)
+
+
+def test_concurrent_host_threads_on_separate_streams(epm):
+    """Calls on different streams with separate buffers and workspaces are
+    independent: two host threads run the whole chain at once, each on its
+    own stream (ctypes releases the interpreter lock during the calls), and
+    each gets the oracle's answer."""
+    import threading
+    c = get_case("glm45air")
+    w = c.w
+    results, errors = {}, []
+    logits = torch.from_numpy(c.logits).to(DEV)
+    x = to_dev_bits(c.x)
+    torch.cuda.synchronize()
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            for _ in range(5):
+                idx, wt = epm.ep_route_topk(logits, w.k, stream=s)
+                lay = epm.ep_dispatch_layout(idx, w.E, w.R, stream=s)
+                send = epm.ep_dispatch(x, lay["pos"], stream=s)
+                out = epm.ep_combine(send, lay["pos"], wt, stream=s)
+            s.synchronize()
+            results[i] = (bits(out), lay["pos"].cpu().numpy())
+        except Exception as e:            # reported below, in the test's thread
+            errors.append(repr(e))
+
+    say("two host threads, two streams")
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    for i in range(2):
+        out, pos = results[i]
+        assert np.array_equal(out, c.x)
+        np.testing.assert_array_equal(pos, c.lay["pos"])
