@@ -113,10 +113,9 @@ hipError_t launch_u(const uint16_t* x, int T, int nvec, int k, const int32_t* po
 
 }  // namespace
 
-// Half the CU count of the current device (cached per device; the cache
-// entries are atomic, so concurrent first calls from several threads are
-// safe -- they store the same value).
-uint32_t dispatch_grid_cap() {
+// Cached per device; the cache entries are atomic, so concurrent first calls
+// from several threads are safe (they store the same value).
+uint32_t device_cu_count() {
     static std::atomic<uint32_t> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
@@ -127,7 +126,7 @@ uint32_t dispatch_grid_cap() {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus < 2)
             cus = 256;
-        v = uint32_t(cus / 2);
+        v = uint32_t(cus);
         cached[slot].store(v, std::memory_order_relaxed);
     }
     return v;

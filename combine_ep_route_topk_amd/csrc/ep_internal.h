@@ -150,11 +150,13 @@ inline size_t fused_row_stride(int H) {
 }
 
 // ----------------------------------------------------------------- launchers
+// The CU count of the current device (cached per device).
+uint32_t device_cu_count();
 // Grid cap of the kernels that scatter whole rows (dispatch, the backward
 // combine's gradient scatter): half the CU count of the current device.
-uint32_t dispatch_grid_cap();
-// Scatters writing at most this many bytes are latency-bound: they run one
-// vector per lane on an uncapped grid instead.
+inline uint32_t dispatch_grid_cap() { return device_cu_count() / 2; }
+// Scatters writing (gathers reading) at most this many bytes are
+// latency-bound: they run one vector per lane on an uncapped grid instead.
 constexpr int64_t kSmallScatterBytes = int64_t(64) << 20;
 bool small_scatter(int T, int H, int k);
 
@@ -173,6 +175,11 @@ hipError_t launch_dispatch(const uint16_t* x, int T, int H, int k, const int32_t
 hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w,
                           int T, int H, int k, uint16_t* out, hipStream_t s);
 
+// The batched combine on a grid of `grid` workgroups, whatever the batch
+// size (w == nullptr: every weight 1).  Requires H % 512 == 0; returns
+// hipErrorInvalidValue otherwise.  launch_combine picks it for large batches.
+hipError_t launch_combine_batched(const uint16_t* y, const int32_t* pos, const float* w, int T,
+                                  int H, int k, uint16_t* out, uint32_t grid, hipStream_t s);
 hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* y,
                                const int32_t* pos, const float* w, int T, int H, int k,
                                uint16_t* grad_y, float* grad_w, hipStream_t s);

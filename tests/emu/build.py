@@ -3,9 +3,8 @@ for the host CPU against a small emulation of the HIP device API (lane fibers,
 wave rendezvous, workgroup barriers; see fake/hip/hip_runtime.h).
 
 Test infrastructure only.  It lets the CPU test suite run the real kernel code
--- including the fused persistent mode, whose GPU launch is switched off in the
-product build -- against the CPU oracle, with a limited number of co-resident
-workgroups."""
+-- the fused persistent mode included -- against the CPU oracle, with a limited
+number of co-resident workgroups."""
 import concurrent.futures as cf
 import os
 import shutil

@@ -159,4 +159,14 @@ void launch(dim3 grid, dim3 block, std::function<void()> body) {
 }  // namespace emu
 
 extern "C" void emu_set_pool(int n) { emu::g_pool = n; }
+
+// The batched combine on a chosen grid, so that small inputs take several
+// full and partial batches (the library picks it only for large batches).
+#include "../../combine_ep_route_topk_amd/csrc/ep_internal.h"
+extern "C" int emu_combine_batched(const uint16_t* y, const int32_t* pos, const float* w, int T,
+                                   int H, int k, uint16_t* out, int grid)
+{
+    const hipError_t e = ep::launch_combine_batched(y, pos, w, T, H, k, out, uint32_t(grid), nullptr);
+    return e == hipSuccess ? 0 : int(e);
+}
 extern "C" int emu_errors() { return emu::g_errors.load(); }

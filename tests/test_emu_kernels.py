@@ -344,3 +344,78 @@ def test_emulated_slices_and_window_copy(emu, seed):
     assert rc == 0 and bad[0] == 1
     assert np.array_equal(dst[:S * row_bytes], src[:S * row_bytes])
     assert np.all(clock[1::2] >= clock[0::2])
+
+
+BATCHED = [
+    # T, H, E, R, k, grid, seed: one full batch, then a partial one
+    (300, 512, 64, 8, 8, 2, 1101),      # k = 8 path: 300 items, 224 per batch
+    (97, 1024, 32, 4, 6, 1, 1102),      # runtime-k path: 194 items, 112 per batch
+    (40, 1536, 16, 4, 3, 1, 1103),      # 120 items: one full batch and 8 more
+]
+
+
+def batched(emu, y, pos, w, T, H, k, grid):
+    out = aligned(T * H * 2, 16).view(np.uint16).reshape(T, H)
+    out[:] = 0xFFFF
+    emu.emu_combine_batched.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + \
+        [ctypes.c_void_p, ctypes.c_int]
+    rc = emu.emu_combine_batched(p(y), p(pos), None if w is None else p(w), T, H, k, p(out), grid)
+    assert rc == 0 and emu.emu_errors() == 0
+    return out
+
+
+def unbatched(emu, y, pos, w, T, H, k):
+    """The one-item-per-wave kernels (ep_combine / ep_dispatch_grad at these
+    small sizes): the same f32 arithmetic, so the same bits."""
+    out = aligned(T * H * 2, 16).view(np.uint16).reshape(T, H)
+    if w is None:
+        rc = emu.ep_dispatch_grad(p(y), p(pos), T, H, k, p(out), None)
+    else:
+        rc = emu.ep_combine(p(y), p(pos), p(w), T, H, k, p(out), None)
+    assert rc == 0, emu.ep_last_error().decode()
+    return out
+
+
+def batched_inputs(T, H, E, R, k, seed):
+    rng = np.random.default_rng(seed)
+    o_idx, o_w = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
+    pos = np.ascontiguousarray(oracle.dispatch_layout(o_idx, E, R)["pos"])
+    y = aligned(T * k * H * 2, 16).view(np.uint16).reshape(T * k, H)
+    y[:] = wl.make_rows(T * k, H, seed + 1)
+    return y, pos, np.ascontiguousarray(o_w)
+
+
+@pytest.mark.parametrize("T,H,E,R,k,grid,seed", BATCHED)
+def test_emulated_batched_combine(emu, T, H, E, R, k, grid, seed):
+    """The batched combine (a batch's outputs held back and stored together)
+    on a tiny grid, so full and partial batches both run: the same bits as
+    the one-item-per-wave kernel, weighted and with unit weights (the backward
+    of dispatch), and the oracle's bits but for rare differences (the oracle
+    sums in f64, the kernels chain f32 fused multiply-adds; the GPU tests
+    hold the one-item-per-wave kernel to the derived error bound)."""
+    y, pos, w = batched_inputs(T, H, E, R, k, seed)
+    out = batched(emu, y, pos, w, T, H, k, grid)
+    assert np.array_equal(out, unbatched(emu, y, pos, w, T, H, k))
+    assert np.mean(out == oracle.combine(y, pos, w)) > 0.99
+    out1 = batched(emu, y, pos, None, T, H, k, grid)
+    assert np.array_equal(out1, unbatched(emu, y, pos, None, T, H, k))
+    assert np.mean(out1 == oracle.dispatch_grad(y, pos)) > 0.99
+
+
+def test_emulated_batched_combine_skips_picks_outside(emu):
+    """A pick whose pos lies outside [0, T*k) counts as a row of zeros, in a
+    batch that is otherwise full (the checked path) and in the partial one."""
+    T, H, E, R, k, grid = 200, 512, 64, 8, 8, 1
+    y, pos, w = batched_inputs(T, H, E, R, k, 1111)
+    bad = pos.copy()
+    lost = [pos[5, 2], pos[150, 7], pos[199, 0]]
+    bad[5, 2], bad[150, 7], bad[199, 0] = -1, T * k + 3, T * k
+    out = batched(emu, y, bad, w, T, H, k, grid)
+    assert np.array_equal(out, unbatched(emu, y, bad, w, T, H, k))
+    y0 = y.copy()
+    y0[lost] = 0
+    assert np.array_equal(out, unbatched(emu, y0, pos, w, T, H, k))
+    # H not a multiple of 512: refused
+    emu.emu_combine_batched.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + \
+        [ctypes.c_void_p, ctypes.c_int]
+    assert emu.emu_combine_batched(p(y), p(pos), p(w), T, 256, k, p(out), grid) != 0

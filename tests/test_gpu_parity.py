@@ -275,3 +275,53 @@ def test_concurrent_host_threads_on_separate_streams(epm):
         out, pos = results[i]
         assert np.array_equal(out, c.x)
         np.testing.assert_array_equal(pos, c.lay["pos"])
+
+
+# Gathers reading over 64 MiB with rows of whole 1 KiB segments take the
+# batched combine (outputs held back in registers and stored a batch at a
+# time on one workgroup per CU): full and partial batches, runtime k.
+BATCHED = [
+    # T, H, E, R, k, seed
+    (5000, 1536, 64, 8, 8, 41),      # a single partial batch
+    (4096, 4096, 64, 16, 6, 42),     # runtime-k path: one full batch and a partial one
+    (20000, 1024, 256, 32, 8, 43),   # one full batch and a partial one
+]
+
+
+@pytest.mark.parametrize("T,H,E,R,k,seed", BATCHED)
+def test_combine_batched_sizes(epm, T, H, E, R, k, seed):
+    rng = np.random.default_rng(seed)
+    o_idx, _ = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
+    pos = oracle.dispatch_layout(o_idx, E, R)["pos"]
+    y = wl.make_rows(T * k, H, seed + 1)
+    wt = rng.random((T, k), dtype=np.float32) - np.float32(0.25)
+    say(f"combine (batched sizes) T={T} H={H} k={k}")
+    d_y, d_pos = to_dev_bits(y), torch.from_numpy(pos).to(DEV)
+    out = epm.ep_combine(d_y, d_pos, torch.from_numpy(wt).to(DEV))
+    gx = epm.ep_dispatch_grad(d_y, d_pos)
+    torch.cuda.synchronize()
+    assert check_combine(bits(out), oracle.combine(y, pos, wt), y, pos, wt) > 0.99
+    assert check_combine(bits(gx), oracle.dispatch_grad(y, pos), y, pos,
+                         np.ones((T, k), np.float32)) > 0.99
+
+
+def test_combine_batched_skips_picks_outside(epm):
+    """pos entries outside [0, T*k) contribute nothing, also in the batched
+    combine: in a batch that is otherwise full and in the partial one."""
+    T, H, E, R, k = 4096, 4096, 128, 16, 8
+    rng = np.random.default_rng(44)
+    o_idx, o_w = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
+    pos = oracle.dispatch_layout(o_idx, E, R)["pos"]
+    y = wl.make_rows(T * k, H, 45)
+    bad = pos.copy()
+    picks = [(5, 2, -1), (1000, 0, T * k), (4000, 7, T * k + 9)]
+    lost = [pos[t, j] for t, j, _ in picks]
+    for t, j, v in picks:
+        bad[t, j] = v
+    say("combine (batched sizes) with picks outside the buffer")
+    out = epm.ep_combine(to_dev_bits(y), torch.from_numpy(bad).to(DEV),
+                         torch.from_numpy(o_w).to(DEV))
+    torch.cuda.synchronize()
+    y0 = y.copy()
+    y0[lost] = 0
+    assert check_combine(bits(out), oracle.combine(y0, pos, o_w), y0, pos, o_w) > 0.99
