@@ -325,3 +325,23 @@ def test_combine_batched_skips_picks_outside(epm):
     y0 = y.copy()
     y0[lost] = 0
     assert check_combine(bits(out), oracle.combine(y0, pos, o_w), y0, pos, o_w) > 0.99
+
+
+def test_dispatch_large_skips_picks_outside(epm):
+    """A pos entry outside [0, T*k) writes nothing, also at sizes that take the
+    capped grid (whole 1 KiB segments, and a ragged row of 513 vectors)."""
+    for T, H, E, R, k, seed in ((4096, 4096, 128, 16, 8, 46), (4096, 4104, 64, 8, 6, 47)):
+        rng = np.random.default_rng(seed)
+        o_idx, _ = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
+        pos = oracle.dispatch_layout(o_idx, E, R)["pos"]
+        x = wl.make_rows(T, H, seed + 1)
+        bad = pos.copy()
+        lost = [pos[3, 1], pos[2000, 0], pos[T - 1, k - 1]]
+        bad[3, 1], bad[2000, 0], bad[T - 1, k - 1] = -1, T * k, T * k + 77
+        say(f"dispatch (large) T={T} H={H} k={k}, picks outside the buffer")
+        send = poison_bits((T * k, H))
+        epm.ep_dispatch(to_dev_bits(x), torch.from_numpy(bad).to(DEV), send)
+        torch.cuda.synchronize()
+        ref = oracle.dispatch(x, pos)
+        ref[lost] = 0xFFFF
+        assert np.array_equal(bits(send), ref)
