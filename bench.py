@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-pipelined", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the leg that replays the step from a captured HIP graph")
     ap.add_argument("--fused-modes", default="0,1,2,3,4",
                     help="comma-separated fused synchronisation modes to time")
     ap.add_argument("--partition-sweep", action="store_true",
@@ -247,6 +249,17 @@ def main():
             "what": "route + layout of the next batch on a second stream during this batch's "
                     "dispatch and combine; every step still runs all four ops"}
 
+    if not args.no_graph:
+        ms_g, ok_g = bench_graph(ep, torch, w, logits, x, dev, K, args.warmup)
+        result["graph"] = {
+            "ms_per_step": round(ms_g, 4),
+            "value": round(step_bytes / (ms_g * 1e-3) / 1e9, 1) if ok_g else None,
+            "tokens_per_s": round(T / (ms_g * 1e-3), 1) if ok_g else None,
+            "parity": ok_g,
+            "steps_per_graph": GRAPH_STEPS,
+            "what": "steps captured in a HIP graph and replayed: the same kernels, one graph "
+                    "launch per steps_per_graph steps instead of four entry-point calls per step"}
+
     if not args.no_fused:
         result["fused"] = bench_fused(ep, torch, w, x, idx, wt, stream, K, args.warmup,
                                       tuple(int(m) for m in args.fused_modes.split(",") if m))
@@ -320,6 +333,57 @@ def bench_pipelined(ep, torch, w, logits, x, dev, K, W):
     for b in buf:
         ok = ok and ep.ep_get_device_error(b["lay"]["workspace"]) == ep.EP_OK
     return wall / K * 1e3, ok, t_enq / K * 1e3
+
+
+GRAPH_STEPS = 8
+
+
+def bench_graph(ep, torch, w, logits, x, dev, K, W):
+    """GRAPH_STEPS steps (route -> layout -> dispatch -> combine each) captured
+    once in a HIP graph on a side stream and replayed.  The library launches
+    only kernels (no memory set or copy nodes, no allocation), so the graph
+    holds the eager steps' kernels; one graph launch replaces GRAPH_STEPS x 4
+    entry-point calls.  (One step per graph is slower than the eager step on
+    MI355X: the graph launch itself costs about what it saves.)  Returns the
+    wall time per step over ceil(K / GRAPH_STEPS) replays and the parity of
+    the output."""
+    T, H, E, R, k = w.T, w.H, w.E, w.R, w.k
+    s = torch.cuda.Stream(device=dev)              # default priority
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wt = torch.empty((T, k), dtype=torch.float32, device=dev)
+    lay = ep.layout_outputs(T, k, E, R, dev, slot_src=False)
+    send = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ops = [ep.bind_route_topk(logits, k, True, idx, wt, s),
+           ep.bind_dispatch_layout(idx, E, R, lay, s),
+           ep.bind_dispatch(x, lay["pos"], send, s),
+           ep.bind_combine(send, lay["pos"], wt, out, s)]
+    s.wait_stream(torch.cuda.current_stream(dev))
+    for _ in range(2):                             # eager warm-up on the capture stream
+        for op in ops:
+            op()
+    s.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(GRAPH_STEPS):
+            for op in ops:
+                op()
+    out.fill_(0)
+    torch.cuda.synchronize()
+    for _ in range(max(W // GRAPH_STEPS, 1)):
+        g.replay()
+    torch.cuda.synchronize()
+    ok = torch.equal(out.view(torch.int16), x.view(torch.int16))
+    reps = max(-(-K // GRAPH_STEPS), 1)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ok = ok and torch.equal(out.view(torch.int16), x.view(torch.int16))
+    ok = ok and ep.ep_get_device_error(lay["workspace"]) == ep.EP_OK
+    del g
+    return wall / (reps * GRAPH_STEPS) * 1e3, ok
 
 
 def make_step(ops, set_events):
