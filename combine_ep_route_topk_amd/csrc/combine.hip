@@ -8,17 +8,21 @@
 // fp32 accumulation in the fixed order j = 0..k-1 (a product, then fused
 // multiply-adds), one round-to-nearest-even to bf16 at the end.
 //
-// HBM-bound gather (k reads, 1 write per row).  A wave owns one (token, row
-// segment) item: per pick it issues U coalesced 16-byte loads per lane from
+// HBM-bound gather (k reads, 1 write per row).  A wave works on (token, row
+// segment) items: per pick it issues coalesced 16-byte loads per lane from
 // row pos[t][j]; the k row indices and weights are wave-uniform scalar loads.
-// For the common k = 8 the pick loop is unrolled so all 8*U loads of a lane
-// can be in flight before the first FMA.  The row loads are nontemporal: each
-// expert-output row is read exactly once, and keeping them out of the
-// Infinity Cache leaves it to the data the next kernels re-read (measured on
-// MI355X at T=4096, H=7168, k=8: combine 108 -> 97 us and the following
-// dispatch 111 -> 95 us).  The output rows are stored streaming and
-// agent-coherent, through a descriptor over the token's row, so they do not
-// stay dirty in the L2 for the next kernel to flush.
+// For the common k = 8 the pick loop is unrolled so all 8 loads of a lane
+// can be in flight before the first FMA.  Large batches run batched
+// (combine_batched_kernel: a batch's results are held in registers and
+// stored together, so reads and writes do not interleave item by item);
+// small batches and ragged rows take one item per wave (combine_kernel).
+// The row loads are nontemporal: each expert-output row is read exactly
+// once, and keeping them out of the Infinity Cache leaves it to the data the
+// next kernels re-read (measured on MI355X at T=4096, H=7168, k=8: combine
+// 108 -> 97 us and the following dispatch 111 -> 95 us).  The output rows
+// are stored streaming and agent-coherent, through a descriptor over the
+// token's row, so they do not stay dirty in the L2 for the next kernel to
+// flush.
 //
 // The same kernel with every weight 1 is the backward of dispatch
 // (HyperParallel-MoE sec. 2.2, Fig. 2(b): the backward Combine returns the
