@@ -45,6 +45,11 @@ def lib():
         L.ep_oracle_dispatch_grad.argtypes = [P, P, i64, i32, i32, P]
         L.ep_oracle_slices.argtypes = [P, i32, i32, P, P, P]
         L.ep_oracle_lpt.argtypes = [P, P, i32, P, i32, i32, P, P, P]
+        L.ep_oracle_rank_coalesce.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, P]
+        L.ep_oracle_rank_coalesce.restype = i64
+        L.ep_oracle_exchange_waves.argtypes = [i32, P]
+        L.ep_oracle_incast_degree.argtypes = [P, i32]
+        L.ep_oracle_incast_degree.restype = i32
         for f in ("ep_oracle_route_topk", "ep_oracle_dispatch_layout",
                   "ep_oracle_dispatch", "ep_oracle_combine",
                   "ep_oracle_combine_tokens", "ep_oracle_fused_trailer",
@@ -199,6 +204,42 @@ def lpt(cost, peer, cap_of_peer, C: int):
     _check(lib().ep_oracle_lpt(_p(cost), _p(peer), U, _p(cap), cap.shape[0], C, _p(core),
                                _p(stripe), _p(load)), "lpt")
     return core[:U], stripe[:U], load
+
+
+def rank_coalesce(topk_idx, E: int, R: int):
+    """One send record per (token, destination rank) -> dict with rank_counts
+    i32 [R], rank_offsets i32 [R+1], row_of_pick i32 [T][k], send_pos i32
+    [T][k], row_src i32 [C], row_experts u64 [C] (C = rank_offsets[R])."""
+    idx = _c(topk_idx, np.int32)
+    T, k = idx.shape
+    S = T * k
+    out = dict(rank_counts=np.empty(R, np.int32), rank_offsets=np.empty(R + 1, np.int32),
+               row_of_pick=np.empty((T, k), np.int32), send_pos=np.empty((T, k), np.int32),
+               row_src=np.empty(max(S, 1), np.int32), row_experts=np.empty(max(S, 1), np.uint64))
+    C = lib().ep_oracle_rank_coalesce(_p(idx), T, k, E, R, _p(out["rank_counts"]),
+                                      _p(out["rank_offsets"]), _p(out["row_of_pick"]),
+                                      _p(out["send_pos"]), _p(out["row_src"]),
+                                      _p(out["row_experts"]))
+    _check(min(C, 0), "rank_coalesce")
+    out["row_src"] = out["row_src"][:C]
+    out["row_experts"] = out["row_experts"][:C]
+    return out
+
+
+def exchange_waves(N: int):
+    """Cyclic exchange waves -> i32 [N-1][N]: peer[k-1][s] = (s + k) mod N."""
+    peer = np.empty((max(N - 1, 0), N), np.int32)
+    _check(lib().ep_oracle_exchange_waves(N, _p(peer) if peer.size else ctypes.c_void_p(1)),
+           "exchange_waves")
+    return peer
+
+
+def incast_degree(dst) -> int:
+    """Largest number of senders of one wave with the same receiver."""
+    dst = _c(dst, np.int32)
+    d = lib().ep_oracle_incast_degree(_p(dst), dst.shape[0])
+    _check(min(d, 0), "incast_degree")
+    return int(d)
 
 
 def fused_trailers(epoch: int, slot_src):

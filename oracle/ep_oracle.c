@@ -429,3 +429,98 @@ int ep_oracle_lpt(const double* cost, const int32_t* peer, int32_t U,
     free(fan);
     return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Rank-level token coalescing: RailWave sec. 3.1-3.2 -- transfer records   */
+/* per destination keep the backend's token coalescing; a record may carry  */
+/* several destinations of one token.  One record per (token, rank).        */
+/* ------------------------------------------------------------------------ */
+
+int64_t ep_oracle_rank_coalesce(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E,
+                                int32_t R, int32_t* rank_counts, int32_t* rank_offsets,
+                                int32_t* row_of_pick, int32_t* send_pos, int32_t* row_src,
+                                uint64_t* row_experts)
+{
+    if (!topk_idx || !rank_counts || !rank_offsets || !row_of_pick || !send_pos ||
+        !row_src || !row_experts || T < 0 || k < 1 || E < 1 || R < 1 || E % R != 0)
+        return -1;
+    const int32_t L = E / R;
+    if (L > 64) return -2;
+    const int64_t S = T * (int64_t)k;
+    for (int64_t s = 0; s < S; ++s)
+        if (topk_idx[s] < 0 || topk_idx[s] >= E) return -4;
+
+    /* first[s]: pick s = t*k + j is the token's first pick of its rank */
+    unsigned char* first = (unsigned char*)malloc((size_t)(S > 0 ? S : 1));
+    if (!first) return -5;
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t j = 0; j < k; ++j) {
+            const int32_t r = topk_idx[t * k + j] / L;
+            int f = 1;
+            for (int32_t i = 0; i < j; ++i)
+                if (topk_idx[t * k + i] / L == r) f = 0;
+            first[t * k + j] = (unsigned char)f;
+        }
+
+    /* records per rank, and where each rank's records start */
+    for (int32_t r = 0; r < R; ++r) rank_counts[r] = 0;
+    for (int64_t s = 0; s < S; ++s)
+        if (first[s]) rank_counts[topk_idx[s] / L] += 1;
+    int64_t run = 0;
+    for (int32_t r = 0; r < R; ++r) {
+        rank_offsets[r] = (int32_t)run;
+        run += rank_counts[r];
+    }
+    rank_offsets[R] = (int32_t)run;
+
+    /* rows in token order inside each rank */
+    int32_t* cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)R);
+    if (!cursor) { free(first); return -5; }
+    for (int32_t r = 0; r < R; ++r) cursor[r] = rank_offsets[r];
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < k; ++j) {
+            const int64_t s = t * k + j;
+            const int32_t r = topk_idx[s] / L;
+            if (first[s]) {
+                const int32_t row = cursor[r]++;
+                row_src[row] = (int32_t)t;
+                row_experts[row] = 0;
+                row_of_pick[s] = row;
+                send_pos[s] = row;
+            } else {
+                int32_t j0 = 0;
+                while (topk_idx[t * k + j0] / L != r) ++j0;
+                row_of_pick[s] = row_of_pick[t * k + j0];
+                send_pos[s] = -1;
+            }
+            row_experts[row_of_pick[s]] |= (uint64_t)1 << (topk_idx[s] % L);
+        }
+    }
+    free(cursor);
+    free(first);
+    return run;
+}
+
+/* Cyclic exchange waves: RailWave sec. 3.2, eq. (10). */
+int ep_oracle_exchange_waves(int32_t N, int32_t* peer)
+{
+    if (N < 1 || !peer) return -1;
+    for (int32_t k = 1; k < N; ++k)
+        for (int32_t s = 0; s < N; ++s)
+            peer[(int64_t)(k - 1) * N + s] = (s + k) % N;
+    return 0;
+}
+
+/* Incast degree of a wave: RailWave App. A.6, Table 8 ("peak incast"). */
+int32_t ep_oracle_incast_degree(const int32_t* dst, int32_t N)
+{
+    if (N < 1 || !dst) return -1;
+    int32_t best = 0;
+    for (int32_t d = 0; d < N; ++d) {
+        int32_t n = 0;
+        for (int32_t s = 0; s < N; ++s)
+            if (dst[s] == d && s != d) ++n;
+        if (n > best) best = n;
+    }
+    return best;
+}

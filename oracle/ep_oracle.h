@@ -22,7 +22,11 @@
  *   [RAIL]   "RailWave: Adaptive Spatial and Temporal Scheduling for
  *            Expert-Parallel Communication" -- "System Design", Fig. 3 (combine
  *            returns outputs to their original token positions using the
- *            metadata saved by dispatch).
+ *            metadata saved by dispatch); sec. 3.1-3.2 (transfer records per
+ *            destination, token coalescing kept in the counts, one record
+ *            may carry several destinations of a token; cyclic pairwise
+ *            exchange waves, eq. (10)); App. A.6, Table 8 (replay schedules
+ *            and their peak incast degrees).
  *   [HPMOE]  "HyperParallel-MoE: Multi-Core Interleaved Scheduling for Fast MoE
  *            Training on Ascend NPUs" -- sec. 2.2 (router picks top-k experts,
  *            outputs weighted by routing scores and combined), sec. 4.1
@@ -144,6 +148,35 @@ int ep_oracle_lpt(const double* cost, const int32_t* peer, int32_t U,
  * { epoch as little-endian u64, slot_src[slot] as u32, 0 as u32 }. */
 int ep_oracle_fused_trailer(uint64_t epoch, const int32_t* slot_src,
                             int64_t slot, uint8_t trailer[16]);
+
+/* Rank-level token coalescing of the send records [RAIL sec. 3.1-3.2: the
+ * transfer records of a destination keep the backend's token coalescing, and
+ * one record may carry several destinations of the same token].  Read here:
+ * one record per (token t, destination rank r) that t sends to, with
+ * r = expert / L and L = E/R local experts per rank (L <= 64); the record
+ * carries the set of r's local experts (expert mod L, a bit mask) that t
+ * picked.  Records are ordered rank-major, then by ascending token.
+ * Outputs: rank_counts [R], rank_offsets [R+1] (rank_offsets[R] = C, the
+ * number of records), row_of_pick [T*k] (the record of pick (t, j)),
+ * send_pos [T*k] (the record for the first pick of each (t, r) in pick
+ * order, -1 for that token's later picks of the same rank: dispatching x
+ * with it writes every record once), row_src [C] (the token of each record),
+ * row_experts [C].  Returns C, or a negative value on a rejected argument. */
+int64_t ep_oracle_rank_coalesce(const int32_t* topk_idx, int64_t T, int32_t k, int32_t E,
+                                int32_t R, int32_t* rank_counts, int32_t* rank_offsets,
+                                int32_t* row_of_pick, int32_t* send_pos, int32_t* row_src,
+                                uint64_t* row_experts);
+
+/* Cyclic pairwise exchange waves [RAIL sec. 3.2, eq. (10)]: with N nodes,
+ * wave k = 1..N-1 sends from node s to node (s + k) mod N.  Writes
+ * peer[(k-1)*N + s]. */
+int ep_oracle_exchange_waves(int32_t N, int32_t* peer);
+
+/* Incast degree of one wave [RAIL App. A.6, Table 8]: the largest number of
+ * senders that send to the same node.  dst[s] is node s's receiver in the
+ * wave; dst[s] < 0 or dst[s] == s means s sends nothing.  Returns the
+ * degree, or a negative value on a rejected argument. */
+int32_t ep_oracle_incast_degree(const int32_t* dst, int32_t N);
 
 #ifdef __cplusplus
 }
