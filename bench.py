@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-pipelined", action="store_true")
+    ap.add_argument("--no-coalesce", action="store_true",
+                    help="skip the rank-coalesced send leg (one record per token and rank)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the leg that replays the step from a captured HIP graph")
     ap.add_argument("--fused-modes", default="0,1,2,3,4",
@@ -260,6 +262,9 @@ def main():
             "what": "steps captured in a HIP graph and replayed: the same kernels, one graph "
                     "launch per steps_per_graph steps instead of four entry-point calls per step"}
 
+    if not args.no_coalesce and w.E // w.R <= 64:
+        result["coalesce"] = bench_coalesce(ep, torch, w, idx, x, dev, K)
+
     if not args.no_fused:
         result["fused"] = bench_fused(ep, torch, w, x, idx, wt, stream, K, args.warmup,
                                       tuple(int(m) for m in args.fused_modes.split(",") if m))
@@ -333,6 +338,52 @@ def bench_pipelined(ep, torch, w, logits, x, dev, K, W):
     for b in buf:
         ok = ok and ep.ep_get_device_error(b["lay"]["workspace"]) == ep.EP_OK
     return wall / K * 1e3, ok, t_enq / K * 1e3
+
+
+def bench_coalesce(ep, torch, w, idx, x, dev, K):
+    """Rank-level token coalescing (RailWave sec. 3.1-3.2: one send record per
+    token and destination rank): ep_rank_coalesce then ep_dispatch with its
+    first-pick positions, against ep_dispatch_layout then ep_dispatch.  The
+    records replace the T*k per-expert rows a multi-GPU exchange would send.
+    Reports both pairs' times (back to back, HIP events on the stream), the
+    record count and the parity of the coalesced rows."""
+    T, H, E, R, k = w.T, w.H, w.E, w.R, w.k
+    s = torch.cuda.current_stream(dev)
+    lay = ep.layout_outputs(T, k, E, R, dev, slot_src=False)
+    co = ep.coalesce_outputs(T, k, E, R, dev)
+    send = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        for _ in range(K):
+            fn()
+        b.record(s)
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / K
+
+    def plain():
+        ep.ep_dispatch_layout(idx, E, R, out=lay)
+        ep.ep_dispatch(x, lay["pos"], send)
+
+    def coalesced():
+        ep.ep_rank_coalesce(idx, E, R, out=co)
+        ep.ep_dispatch(x, co["send_pos"], send)
+
+    us_plain = timed(plain)
+    us_co = timed(coalesced)
+    torch.cuda.synchronize()
+    C = int(co["rank_offsets"][R].item())
+    src = co["row_src"][:C].long()
+    ok = bool(torch.equal(send[:C].view(torch.int16), x[src].view(torch.int16)))
+    ok = ok and ep.ep_get_device_error(co["workspace"]) == ep.EP_OK
+    return {"records": C, "picks": T * k, "records_per_pick": round(C / (T * k), 4),
+            "us_layout_dispatch": round(us_plain, 2), "us_coalesce_dispatch": round(us_co, 2),
+            "rows_written_saved_bytes": (T * k - C) * H * 2, "parity": ok,
+            "what": "ep_rank_coalesce + ep_dispatch(send_pos) against ep_dispatch_layout + "
+                    "ep_dispatch, back to back"}
 
 
 GRAPH_STEPS = 8

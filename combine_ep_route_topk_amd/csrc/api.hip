@@ -412,6 +412,51 @@ ep_status ep_window_copy(const void* src, void* dst, int64_t row_bytes, int64_t 
                     fn);
 }
 
+size_t ep_rank_coalesce_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t R)
+{
+    if (T < 1 || k < 1 || E < 1 || R < 1) return 0;
+    return ep::coalesce_plan(T, k, R).bytes;
+}
+
+ep_status ep_rank_coalesce(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32_t R,
+                           int32_t* rank_counts, int32_t* rank_offsets, int32_t* row_of_pick,
+                           int32_t* send_pos, int32_t* row_src, uint64_t* row_experts,
+                           void* workspace, size_t workspace_bytes, void* stream)
+{
+    const char* fn = "ep_rank_coalesce";
+    TimingScope timing_scope;
+    EP_TRY(check_routing_sizes(fn, T, k, E));
+    if (R < 1 || E % R != 0)
+        return fail(EP_ERR_INVALID_ARG, "%s: R=%d must be >= 1 and divide E=%d", fn, R, E);
+    if (E / R > 64)
+        return fail(EP_ERR_UNSUPPORTED, "%s: E/R=%d local experts per rank exceed 64", fn, E / R);
+    EP_REQUIRE_PTR(fn, topk_idx, 4);
+    EP_REQUIRE_PTR(fn, rank_counts, 4);
+    EP_REQUIRE_PTR(fn, rank_offsets, 4);
+    EP_REQUIRE_PTR(fn, row_of_pick, 4);
+    EP_REQUIRE_PTR(fn, send_pos, 4);
+    EP_REQUIRE_PTR(fn, row_src, 4);
+    EP_REQUIRE_PTR(fn, row_experts, 8);
+    EP_REQUIRE_PTR(fn, workspace, 256);
+    const size_t need = ep::coalesce_plan(T, k, R).bytes;
+    if (workspace_bytes < need)
+        return fail(EP_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn,
+                    workspace_bytes, need);
+    return launched(ep::launch_rank_coalesce(topk_idx, T, k, E, R, rank_counts, rank_offsets,
+                                             row_of_pick, send_pos, row_src, row_experts,
+                                             workspace, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+ep_status ep_exchange_waves(int32_t N, int32_t* peer)
+{
+    const char* fn = "ep_exchange_waves";
+    if (N < 1 || N > 32768) return fail(EP_ERR_INVALID_ARG, "%s: N=%d must be in [1, 32768]", fn, N);
+    if (N > 1 && !peer) return fail(EP_ERR_INVALID_ARG, "%s: peer is NULL", fn);
+    ep::exchange_waves(N, peer);
+    return ok();
+}
+
 ep_status ep_get_device_error(const void* workspace, void* stream)
 {
     const char* fn = "ep_get_device_error";

@@ -135,6 +135,28 @@ inline FusedPlan fused_plan(int T, int k, int E) {
     return f;
 }
 
+// Rank-coalescing workspace: the layout's (over R "experts"), then each
+// pick's key, then the layout's per-rank outputs (which duplicate its
+// per-expert ones when every rank holds one expert).
+struct CoalescePlan {
+    LayoutPlan lay;
+    size_t off_keys;          // i32 [T*k]
+    size_t off_rank_counts;   // i32 [R]
+    size_t off_rank_offsets;  // i32 [R+1]
+    size_t bytes;
+};
+
+inline CoalescePlan coalesce_plan(int T, int k, int R) {
+    CoalescePlan c{};
+    c.lay = layout_plan(T, k, R);
+    size_t off = c.lay.bytes;
+    c.off_keys = off;         off += align256(sizeof(int32_t) * c.lay.S);
+    c.off_rank_counts = off;  off += align256(sizeof(int32_t) * size_t(R));
+    c.off_rank_offsets = off; off += align256(sizeof(int32_t) * (size_t(R) + 1));
+    c.bytes = off;
+    return c;
+}
+
 // Default bound of a device-side wait, in polling rounds (each round is one
 // agent-scope load plus a short sleep, roughly a microsecond).
 constexpr uint32_t kDefaultSpinLimit = uint32_t(1) << 20;
@@ -168,6 +190,22 @@ hipError_t launch_dispatch_layout(const int32_t* topk_idx, int T, int k, int E, 
                                   int32_t* rank_counts, int32_t* rank_offsets,
                                   int32_t* pos, int32_t* slot_src, void* ws,
                                   hipStream_t s);
+// The layout with a chosen expected slot total: the device error word reports
+// an id outside [0, E) only when expect >= 0 and fewer than `expect` slots
+// were counted.  expect = -1 lets slots with a negative id be skipped on
+// purpose (the rank-coalescing pass marks a token's repeated ranks so).
+hipError_t launch_dispatch_layout_skips(const int32_t* topk_idx, int T, int k, int E, int R,
+                                        int32_t* expert_counts, int32_t* expert_offsets,
+                                        int32_t* rank_counts, int32_t* rank_offsets,
+                                        int32_t* pos, int32_t* slot_src, void* ws,
+                                        int64_t expect, hipStream_t s);
+
+hipError_t launch_rank_coalesce(const int32_t* topk_idx, int T, int k, int E, int R,
+                                int32_t* rank_counts, int32_t* rank_offsets,
+                                int32_t* row_of_pick, int32_t* send_pos, int32_t* row_src,
+                                uint64_t* row_experts, void* ws, hipStream_t s);
+// Host: peer[(w-1)*N + s] = (s + w) mod N for w = 1..N-1.
+void exchange_waves(int32_t N, int32_t* peer);
 
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int k, const int32_t* pos,
                            uint16_t* send, hipStream_t s);

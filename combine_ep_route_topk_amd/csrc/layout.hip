@@ -137,7 +137,8 @@ __global__ __launch_bounds__(kBlock) void layout_pos_kernel(
     const int32_t* __restrict__ base, const int32_t* __restrict__ local_rank,
     int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
-    int32_t* __restrict__ pos, int32_t* __restrict__ slot_src, WsHeader* __restrict__ hdr)
+    int32_t* __restrict__ pos, int32_t* __restrict__ slot_src, WsHeader* __restrict__ hdr,
+    int64_t expect)
 {
     const int64_t s = int64_t(blockIdx.x) * kBlock + threadIdx.x;
     if (s < S) {
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(kBlock) void layout_pos_kernel(
         if (threadIdx.x == 0) {
             uint32_t err = kDevOk;
             if (hdr->timeout.v) err = kDevTimeout;
-            else if (expert_offsets[E] != S) err = kDevBadExpert;
+            else if (expect >= 0 && expert_offsets[E] != expect) err = kDevBadExpert;
             hdr->error = err;
             hdr->magic = kLayoutMagic;
         }
@@ -178,7 +179,8 @@ __device__ __forceinline__ void scanpos_tile(
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ local_rank,
     int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
-    int32_t* __restrict__ pos, int32_t* __restrict__ slot_src, WsHeader* __restrict__ hdr)
+    int32_t* __restrict__ pos, int32_t* __restrict__ slot_src, WsHeader* __restrict__ hdr,
+    int64_t expect)
 {
     __shared__ int sh_off[kMaxE + 1];      // expert offsets (exclusive scan)
     __shared__ int sh_base[kMaxE];         // first row of (expert, this tile)
@@ -272,7 +274,7 @@ __device__ __forceinline__ void scanpos_tile(
             if (r < R) rank_counts[r] = sh_off[(r + 1) * L] - sh_off[r * L];
         }
         if (tid == 0) {
-            hdr->error = sh_off[E] != S ? kDevBadExpert : kDevOk;
+            hdr->error = expect >= 0 && sh_off[E] != expect ? kDevBadExpert : kDevOk;
             hdr->magic = kLayoutMagic;
         }
     }
@@ -297,10 +299,11 @@ __global__ __launch_bounds__(kBlock) void layout_scanpos_kernel(
     const int32_t* __restrict__ cnt, const int32_t* __restrict__ local_rank,
     int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
-    int32_t* __restrict__ pos, int32_t* __restrict__ slot_src, WsHeader* __restrict__ hdr)
+    int32_t* __restrict__ pos, int32_t* __restrict__ slot_src, WsHeader* __restrict__ hdr,
+    int64_t expect)
 {
     scanpos_tile(blockIdx.x, topk_idx, S, E, R, nTiles, cnt, local_rank, expert_counts,
-                 expert_offsets, rank_counts, rank_offsets, pos, slot_src, hdr);
+                 expert_offsets, rank_counts, rank_offsets, pos, slot_src, hdr, expect);
 }
 
 // A layout of one tile (T*k <= kTileSlots, e.g. a decode batch): histogram,
@@ -313,13 +316,14 @@ __global__ __launch_bounds__(kBlock) void layout_single_kernel(
     int32_t* __restrict__ cnt, int32_t* __restrict__ local_rank,
     int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
-    int32_t* __restrict__ pos, int32_t* __restrict__ slot_src, WsHeader* __restrict__ hdr)
+    int32_t* __restrict__ pos, int32_t* __restrict__ slot_src, WsHeader* __restrict__ hdr,
+    int64_t expect)
 {
     __shared__ int32_t hist[kWavesPerBlock][kMaxE];
     hist_tile(topk_idx, S, E, 1, 0, cnt, local_rank, hist);
     __syncthreads();
     scanpos_tile(0, topk_idx, S, E, R, 1, cnt, local_rank, expert_counts, expert_offsets,
-                 rank_counts, rank_offsets, pos, slot_src, hdr);
+                 rank_counts, rank_offsets, pos, slot_src, hdr, expect);
 }
 
 }  // namespace
@@ -328,6 +332,17 @@ hipError_t launch_dispatch_layout(const int32_t* topk_idx, int T, int k, int E, 
                                   int32_t* expert_counts, int32_t* expert_offsets,
                                   int32_t* rank_counts, int32_t* rank_offsets,
                                   int32_t* pos, int32_t* slot_src, void* ws, hipStream_t s)
+{
+    return launch_dispatch_layout_skips(topk_idx, T, k, E, R, expert_counts, expert_offsets,
+                                        rank_counts, rank_offsets, pos, slot_src, ws,
+                                        int64_t(T) * k, s);
+}
+
+hipError_t launch_dispatch_layout_skips(const int32_t* topk_idx, int T, int k, int E, int R,
+                                        int32_t* expert_counts, int32_t* expert_offsets,
+                                        int32_t* rank_counts, int32_t* rank_offsets,
+                                        int32_t* pos, int32_t* slot_src, void* ws,
+                                        int64_t expect, hipStream_t s)
 {
     const LayoutPlan p = layout_plan(T, k, E);
     char* w = static_cast<char*>(ws);
@@ -340,7 +355,7 @@ hipError_t launch_dispatch_layout(const int32_t* topk_idx, int T, int k, int E, 
     if (p.nTiles == 1) {
         EP_LAUNCH(layout_single_kernel, dim3(1), dim3(kBlock), 0, s, topk_idx, p.S, E, R, cnt,
                   rank, expert_counts, expert_offsets, rank_counts, rank_offsets, pos, slot_src,
-                  hdr);
+                  hdr, expect);
         return hipGetLastError();
     }
     EP_LAUNCH(layout_hist_kernel, dim3(p.nTiles), dim3(kBlock), 0, s,
@@ -350,7 +365,7 @@ hipError_t launch_dispatch_layout(const int32_t* topk_idx, int T, int k, int E, 
     if (p.nCnt <= kRedundantScanMax) {
         EP_LAUNCH(layout_scanpos_kernel, dim3(p.nTiles), dim3(kBlock), 0, s,
                   topk_idx, p.S, E, R, p.nTiles, cnt, rank, expert_counts, expert_offsets,
-                  rank_counts, rank_offsets, pos, slot_src, hdr);
+                  rank_counts, rank_offsets, pos, slot_src, hdr, expect);
         return hipGetLastError();
     }
     EP_LAUNCH(layout_scan_kernel, dim3(p.nScan), dim3(kBlock), 0, s,
@@ -361,7 +376,7 @@ hipError_t launch_dispatch_layout(const int32_t* topk_idx, int T, int k, int E, 
     const int grid = int((p.S + kBlock - 1) / kBlock);
     EP_LAUNCH(layout_pos_kernel, dim3(grid), dim3(kBlock), 0, s,
                        topk_idx, p.S, E, R, p.nTiles, base, rank, expert_counts,
-                       expert_offsets, rank_counts, rank_offsets, pos, slot_src, hdr);
+                       expert_offsets, rank_counts, rank_offsets, pos, slot_src, hdr, expect);
     return hipGetLastError();
 }
 

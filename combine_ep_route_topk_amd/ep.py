@@ -55,6 +55,10 @@ _SIGS = {
                                         ctypes.POINTER(ctypes.c_uint64), _u32, _i32, _P],
                                        ctypes.c_int),
     "ep_expert_slices": ([_P, _i32, _i32, _P, _P, _P, _P], ctypes.c_int),
+    "ep_rank_coalesce_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
+    "ep_rank_coalesce": ([_P, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P, _P, _P, _sz, _P],
+                         ctypes.c_int),
+    "ep_exchange_waves": ([_i32, _P], ctypes.c_int),
     "ep_lpt_task_count": ([_P, _i32, ctypes.c_int64], ctypes.c_int64),
     "ep_lpt_partition": ([_P, _i32, ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P, _i32, _i32,
                           _P, ctypes.c_int64, _P, _P], ctypes.c_int),
@@ -343,6 +347,51 @@ def ep_expert_slices(expert_offsets: torch.Tensor, P: int, out: dict | None = No
     _check(_lib.ep_expert_slices(_ptr(expert_offsets), E, P, _ptr(out["start"]),
                                  _ptr(out["expert"]), _ptr(out["offset"]), _P(_stream(stream, dev))))
     return out
+
+
+# ------------------------------------------------------------------- coalescing
+def coalesce_outputs(T: int, k: int, E: int, R: int, device) -> dict:
+    """Allocate the output tensors of ep_rank_coalesce."""
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(
+        rank_counts=torch.empty(R, **i32), rank_offsets=torch.empty(R + 1, **i32),
+        row_of_pick=torch.empty((T, k), **i32), send_pos=torch.empty((T, k), **i32),
+        row_src=torch.empty(T * k, **i32),
+        row_experts=torch.empty(T * k, dtype=torch.int64, device=device),
+        workspace=torch.empty(int(_lib.ep_rank_coalesce_workspace_bytes(T, k, E, R)),
+                              dtype=torch.uint8, device=device))
+
+
+def ep_rank_coalesce(topk_idx: torch.Tensor, E: int, R: int, out: dict | None = None,
+                     stream=None) -> dict:
+    """topk_idx i32 [T][k] -> dict(rank_counts, rank_offsets, row_of_pick,
+    send_pos, row_src, row_experts (u64 bit masks in an int64 tensor),
+    workspace): one send record per (token, destination rank).  The number of
+    records is rank_offsets[R]; row_src and row_experts are valid below it."""
+    _need(topk_idx, "topk_idx", torch.int32)
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    if out is None:
+        out = coalesce_outputs(T, k, E, R, dev)
+    ws = out["workspace"]
+    _need(ws, "workspace", torch.uint8)
+    for name, shape in (("rank_counts", (R,)), ("rank_offsets", (R + 1,)),
+                        ("row_of_pick", (T, k)), ("send_pos", (T, k)), ("row_src", (T * k,))):
+        _need(out[name], name, torch.int32, shape)
+    _need(out["row_experts"], "row_experts", torch.int64, (T * k,))
+    _check(_lib.ep_rank_coalesce(
+        _ptr(topk_idx), T, k, E, R, _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]),
+        _ptr(out["row_of_pick"]), _ptr(out["send_pos"]), _ptr(out["row_src"]),
+        _ptr(out["row_experts"]), _ptr(ws), ws.numel(), _P(_stream(stream, dev))))
+    return out
+
+
+def ep_exchange_waves(N: int):
+    """HOST: the cyclic exchange waves -> numpy int32 [N-1][N], peer[w-1][s] =
+    (s + w) mod N."""
+    peer = _np.zeros((max(N - 1, 0), max(N, 1)), _np.int32)
+    _check(_lib.ep_exchange_waves(int(N), peer.ctypes.data if peer.size else None))
+    return peer[:, :N]
 
 
 def ep_lpt_partition(rank_offsets, row_bytes: int, unit_rows: int, C: int, alpha=(0.0,),

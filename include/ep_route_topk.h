@@ -72,7 +72,7 @@ const char* ep_last_error(void);
  * device work only).  After this call, the NEXT compute entry point called on
  * the same thread (ep_route_topk, ep_dispatch_layout, ep_dispatch, ep_combine,
  * ep_combine_grad, ep_dispatch_grad, ep_fused_dispatch_combine[_sync],
- * ep_expert_slices, ep_window_copy) records `start_event` when its first kernel
+ * ep_expert_slices, ep_window_copy, ep_rank_coalesce) records `start_event` when its first kernel
  * starts and `stop_event` when its last kernel ends, taken from the kernels'
  * own dispatch packets -- the same interval a kernel-trace profiler reports,
  * with no marker packet in between.  Either event may be NULL.  The hook then
@@ -370,6 +370,52 @@ ep_status ep_fused_dispatch_combine_sync(const uint16_t* x, const int32_t* topk_
                                          uint8_t* send_rows, uint16_t* out, void* workspace,
                                          size_t workspace_bytes, uint64_t* epoch_out,
                                          uint32_t spin_limit, int32_t sync, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Rank-level token coalescing of the send records [RAIL sec. 3.1-3.2: the
+ * transfer records of a destination keep the backend's token coalescing, and
+ * one record may carry several destinations of the same token].  One record
+ * per (token t, destination rank r) that t sends to, r = expert / L with
+ * L = E/R local experts per rank; records are rank-major, then by ascending
+ * token.  This is the sender's half of a multi-GPU exchange: a token whose
+ * picks share a rank sends its row there once.
+ *   topk_idx     i32 [T][k]   expert ids in [0, E); E % R == 0, L <= 64.
+ *   rank_counts  i32 [R]      out: records per rank.
+ *   rank_offsets i32 [R+1]    out: exclusive prefix of rank_counts;
+ *                             rank_offsets[R] = C, the number of records.
+ *   row_of_pick  i32 [T][k]   out: the record row of pick (t, j).
+ *   send_pos     i32 [T][k]   out: row_of_pick for the token's first pick of
+ *                             each rank (in pick order), -1 for its later
+ *                             picks of that rank.  ep_dispatch(x, send_pos)
+ *                             then writes every record's row exactly once
+ *                             (rows C and above of its send buffer untouched).
+ *   row_src      i32 [T*k]    out: entries [0, C): each record's token.
+ *   row_experts  u64 [T*k]    out: entries [0, C): bit i set when the
+ *                             record's token picked local expert i of the
+ *                             record's rank (expert r*L + i).
+ *   workspace    ep_rank_coalesce_workspace_bytes(T, k, E, R) bytes,
+ *                256-byte aligned, caller-owned; no initialisation needed.
+ * Every output is a caller-owned device buffer.  Errors: EP_ERR_INVALID_ARG
+ * (sizes, NULL, alignment: 4 bytes, 8 for row_experts), EP_ERR_UNSUPPORTED
+ * (L > 64, E > 1024, k > 64, T*k >= 2^30), EP_ERR_WORKSPACE.  A pick whose id
+ * lies outside [0, E) gets row_of_pick = send_pos = -1, belongs to no record,
+ * and makes ep_get_device_error(workspace) report EP_ERR_DEVICE.
+ * ------------------------------------------------------------------------- */
+size_t ep_rank_coalesce_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t R);
+ep_status ep_rank_coalesce(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E, int32_t R,
+                           int32_t* rank_counts, int32_t* rank_offsets, int32_t* row_of_pick,
+                           int32_t* send_pos, int32_t* row_src, uint64_t* row_experts,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Cyclic pairwise exchange waves [RAIL sec. 3.2, eq. (10)]: with N nodes,
+ * wave w = 1..N-1 sends from node s to node (s + w) mod N, so every node has
+ * one outgoing and one incoming peer per wave and every ordered pair of
+ * distinct nodes appears exactly once.  Host function: peer is a host array
+ * of (N-1)*N ints, peer[(w-1)*N + s] = (s + w) mod N.  N in [1, 32768];
+ * EP_ERR_INVALID_ARG otherwise or for a NULL peer with N > 1.
+ * ------------------------------------------------------------------------- */
+ep_status ep_exchange_waves(int32_t N, int32_t* peer);
 
 /* ---------------------------------------------------------------------------
  * Reads a layout or fused workspace's error word: synchronises `stream` first,

@@ -52,6 +52,16 @@ int main(void)
         CHECK(ep_lpt_partition(ro, 3, 16, 4, NULL, alpha, beta, cap, 1, 2, tasks, 4,
                                core_begin, load) == EP_ERR_INVALID_ARG);
     }
+    {
+        int32_t peer[3 * 4];
+        int32_t w, q;
+        CHECK(ep_exchange_waves(4, peer) == EP_OK);
+        for (w = 1; w < 4; ++w)
+            for (q = 0; q < 4; ++q) CHECK(peer[(w - 1) * 4 + q] == (q + w) % 4);
+        CHECK(ep_rank_coalesce_workspace_bytes(4096, 8, 256, 32) > 0);
+        CHECK(ep_rank_coalesce(NULL, 4, 2, 8, 2, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0,
+                               NULL) == EP_ERR_INVALID_ARG);
+    }
     printf("c abi ok\n");
     return 0;
 }

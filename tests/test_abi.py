@@ -157,6 +157,39 @@ def test_backward_validation(ep):
     assert rc == ep.EP_ERR_UNSUPPORTED and "T*H" in msg
 
 
+def test_rank_coalesce_validation(ep):
+    lib = ep.library()
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    need = lib.ep_rank_coalesce_workspace_bytes(64, 4, 16, 4)
+    assert need >= lib.ep_dispatch_layout_workspace_bytes(64, 4, 4, 4) + 64 * 4 * 4
+    assert lib.ep_rank_coalesce_workspace_bytes(0, 4, 16, 4) == 0
+    args = lambda T, k, E, R, re=f, nb=need: (f, T, k, E, R, f, f, f, f, f, re, f, nb, None)
+    rc, msg = call(lib, "ep_rank_coalesce", *args(64, 4, 16, 3))
+    assert rc == ep.EP_ERR_INVALID_ARG and "divide" in msg
+    rc, msg = call(lib, "ep_rank_coalesce", *args(64, 4, 130, 1))
+    assert rc == ep.EP_ERR_UNSUPPORTED and "64" in msg          # 130 local experts per rank
+    rc, _ = call(lib, "ep_rank_coalesce", *args(64, 4, 16, 4, re=P(FAKE + 4)))
+    assert rc == ep.EP_ERR_INVALID_ARG                          # row_experts not 8-byte aligned
+    rc, _ = call(lib, "ep_rank_coalesce", *args(64, 4, 16, 4, nb=need - 1))
+    assert rc == ep.EP_ERR_WORKSPACE
+
+
+def test_exchange_waves_host_function(ep):
+    """Host-only: the library's cyclic exchange waves equal the oracle's, and
+    the page's 4-node permutation schedule (RailWave App. A.6, Table 8)."""
+    import json
+    import numpy as np
+    import oracle
+    for N in (1, 2, 3, 4, 8, 13):
+        np.testing.assert_array_equal(ep.ep_exchange_waves(N), oracle.exchange_waves(N))
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "railwave_table8.json")))
+    np.testing.assert_array_equal(ep.ep_exchange_waves(4), g["schedules"]["Permutation"]["waves"])
+    lib = ep.library()
+    assert call(lib, "ep_exchange_waves", 0, None)[0] == ep.EP_ERR_INVALID_ARG
+    assert call(lib, "ep_exchange_waves", 3, None)[0] == ep.EP_ERR_INVALID_ARG
+
+
 def test_binding_refuses_cpu_tensors(ep):
     import torch
     with pytest.raises(ValueError, match="GPU"):

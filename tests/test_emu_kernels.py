@@ -419,3 +419,71 @@ def test_emulated_batched_combine_skips_picks_outside(emu):
     emu.emu_combine_batched.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + \
         [ctypes.c_void_p, ctypes.c_int]
     assert emu.emu_combine_batched(p(y), p(pos), p(w), T, 256, k, p(out), grid) != 0
+
+
+COALESCE = [
+    # T, E, R, k, seed
+    (128, 256, 32, 8, 1201),     # the decode-like shape: one layout tile over R ranks
+    (700, 64, 8, 6, 1202),       # five tiles, runtime k
+    (300, 16, 16, 4, 1203),      # one expert per rank: the expert layout itself
+    (50, 40, 1, 5, 1204),        # one rank: one record per token
+    (257, 128, 2, 8, 1205),      # 64 local experts per rank (the mask's full width)
+]
+
+
+def coalesce_emu(L, idx, E, R):
+    T, k = idx.shape
+    out = dict(rank_counts=np.zeros(R, np.int32), rank_offsets=np.zeros(R + 1, np.int32),
+               row_of_pick=np.zeros((T, k), np.int32), send_pos=np.zeros((T, k), np.int32),
+               row_src=np.full(T * k, -7, np.int32), row_experts=np.zeros(T * k, np.uint64))
+    L.ep_rank_coalesce_workspace_bytes.restype = ctypes.c_size_t
+    ws = aligned(L.ep_rank_coalesce_workspace_bytes(T, k, E, R))
+    idx = np.ascontiguousarray(idx)
+    rc = L.ep_rank_coalesce(p(idx), T, k, E, R, p(out["rank_counts"]), p(out["rank_offsets"]),
+                            p(out["row_of_pick"]), p(out["send_pos"]), p(out["row_src"]),
+                            p(out["row_experts"]), p(ws), ctypes.c_size_t(ws.size), None)
+    assert rc == 0, L.ep_last_error().decode()
+    return out, L.ep_get_device_error(p(ws), None)
+
+
+@pytest.mark.parametrize("T,E,R,k,seed", COALESCE)
+def test_emulated_rank_coalesce_matches_oracle(emu, T, E, R, k, seed):
+    """RailWave sec. 3.1-3.2 (one send record per token and destination rank):
+    the emulated key, layout and rows kernels against the oracle, bit for bit;
+    dispatching x with send_pos writes each record's token row."""
+    rng = np.random.default_rng(seed)
+    idx, _ = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
+    got, status = coalesce_emu(emu, idx, E, R)
+    assert status == 0
+    ref = oracle.rank_coalesce(idx, E, R)
+    C = int(ref["rank_offsets"][R])
+    for key in ("rank_counts", "rank_offsets", "row_of_pick", "send_pos"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    np.testing.assert_array_equal(got["row_src"][:C], ref["row_src"])
+    np.testing.assert_array_equal(got["row_experts"][:C], ref["row_experts"])
+    assert np.all(got["row_src"][C:] == -7)            # rows beyond the records untouched
+    H = 16
+    x = aligned(T * H * 2, 16).view(np.uint16).reshape(T, H)
+    x[:] = wl.make_rows(T, H, seed + 1)
+    send = aligned(T * k * H * 2, 16).view(np.uint16).reshape(T * k, H)
+    send[:] = 0xFFFF
+    assert emu.ep_dispatch(p(x), T, H, k, p(got["send_pos"]), p(send), None) == 0
+    np.testing.assert_array_equal(send[:C], x[ref["row_src"]])
+    assert np.all(send[C:] == 0xFFFF)
+
+
+def test_emulated_rank_coalesce_reports_bad_ids(emu):
+    T, E, R, k = 64, 32, 4, 4
+    rng = np.random.default_rng(1210)
+    idx, _ = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
+    bad = idx.copy()
+    bad[5, 1], bad[40, 3] = E, -2
+    got, status = coalesce_emu(emu, bad, E, R)
+    assert status != 0                                  # EP_ERR_DEVICE
+    assert got["row_of_pick"][5, 1] == -1 and got["send_pos"][40, 3] == -1
+    # the other picks: the records of the routing without the two bad picks
+    keep = np.ones((T, k), bool)
+    keep[5, 1] = keep[40, 3] = False
+    recs = sorted({(int(e) // (E // R), t) for t in range(T) for j, e in enumerate(bad[t]) if keep[t, j]})
+    assert int(got["rank_offsets"][R]) == len(recs)
+    np.testing.assert_array_equal(got["row_src"][:len(recs)], [t for _, t in recs])
