@@ -48,6 +48,7 @@ def lib():
         L.ep_oracle_rank_coalesce.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, P]
         L.ep_oracle_rank_coalesce.restype = i64
         L.ep_oracle_exchange_waves.argtypes = [i32, P]
+        L.ep_oracle_expand_records.argtypes = [P, i64, i32, P, P, P]
         L.ep_oracle_incast_degree.argtypes = [P, i32]
         L.ep_oracle_incast_degree.restype = i32
         for f in ("ep_oracle_route_topk", "ep_oracle_dispatch_layout",
@@ -223,6 +224,21 @@ def rank_coalesce(topk_idx, E: int, R: int):
     _check(min(C, 0), "rank_coalesce")
     out["row_src"] = out["row_src"][:C]
     out["row_experts"] = out["row_experts"][:C]
+    return out
+
+
+def expand_records(masks, L: int):
+    """Receiver-side expansion of coalesced records -> dict(expert_counts i32
+    [L], expert_offsets i32 [L+1], pos i32 [C][L] (-1 where a record does not
+    feed that expert))."""
+    masks = _c(masks, np.uint64)
+    C = masks.shape[0]
+    out = dict(expert_counts=np.empty(L, np.int32), expert_offsets=np.empty(L + 1, np.int32),
+               pos=np.empty((C, L), np.int32))
+    _check(lib().ep_oracle_expand_records(_p(masks) if C else ctypes.c_void_p(8), C, L,
+                                          _p(out["expert_counts"]), _p(out["expert_offsets"]),
+                                          _p(out["pos"]) if C else ctypes.c_void_p(8)),
+           "expand_records")
     return out
 
 

@@ -501,6 +501,34 @@ int64_t ep_oracle_rank_coalesce(const int32_t* topk_idx, int64_t T, int32_t k, i
     return run;
 }
 
+/* Receiver-side expansion of coalesced records: RailWave sec. 3.1-3.2 and   */
+/* StrataCL's level-2 expert windows -- a stable counting sort of the        */
+/* (record, local expert) pairs by expert.                                    */
+int ep_oracle_expand_records(const uint64_t* masks, int64_t C, int32_t L, int32_t* expert_counts,
+                             int32_t* expert_offsets, int32_t* pos)
+{
+    if (!masks || !expert_counts || !expert_offsets || !pos || C < 0 || L < 1 || L > 64)
+        return -1;
+    for (int32_t i = 0; i < L; ++i) expert_counts[i] = 0;
+    for (int64_t c = 0; c < C; ++c) {
+        if (L < 64 && (masks[c] >> L) != 0) return -2;       /* a bit past the last expert */
+        for (int32_t i = 0; i < L; ++i)
+            if ((masks[c] >> i) & 1u) expert_counts[i] += 1;
+    }
+    int64_t run = 0;
+    for (int32_t i = 0; i < L; ++i) {
+        expert_offsets[i] = (int32_t)run;
+        run += expert_counts[i];
+    }
+    expert_offsets[L] = (int32_t)run;
+    for (int32_t i = 0; i < L; ++i) {
+        int64_t next = expert_offsets[i];
+        for (int64_t c = 0; c < C; ++c)
+            pos[c * L + i] = ((masks[c] >> i) & 1u) ? (int32_t)next++ : -1;
+    }
+    return 0;
+}
+
 /* Cyclic exchange waves: RailWave sec. 3.2, eq. (10). */
 int ep_oracle_exchange_waves(int32_t N, int32_t* peer)
 {

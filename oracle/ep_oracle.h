@@ -167,6 +167,18 @@ int64_t ep_oracle_rank_coalesce(const int32_t* topk_idx, int64_t T, int32_t k, i
                                 int32_t* row_of_pick, int32_t* send_pos, int32_t* row_src,
                                 uint64_t* row_experts);
 
+/* A receiver's expansion of coalesced records into its local experts'
+ * slots [RAIL sec. 3.1-3.2 (records carrying several destinations of one
+ * token); STRATA appendix "Hierarchical Workload Partitioning for MoE
+ * Dispatch/Combine", level 2: expert windows of base offsets and token-local
+ * indices].  Record c (in arrival order) feeds local expert i when bit i of
+ * masks[c] is set.  Slots are expert-major, then in record order:
+ * expert_counts [L], expert_offsets [L+1], pos [C*L] (pos[c*L + i] = the
+ * slot of record c's row for expert i, or -1 when bit i is clear).  L in
+ * [1, 64]. */
+int ep_oracle_expand_records(const uint64_t* masks, int64_t C, int32_t L, int32_t* expert_counts,
+                             int32_t* expert_offsets, int32_t* pos);
+
 /* Cyclic pairwise exchange waves [RAIL sec. 3.2, eq. (10)]: with N nodes,
  * wave k = 1..N-1 sends from node s to node (s + k) mod N.  Writes
  * peer[(k-1)*N + s]. */

@@ -150,3 +150,47 @@ def test_exchange_waves_cover_every_pair_once(N):
     for w in range(N - 1):
         assert sorted(peer[w]) == list(range(N))        # one sender per receiver
         assert oracle.incast_degree(peer[w]) == 1
+
+
+def test_expand_records_hand_example():
+    # masks 0b011, 0b100, 0b001 over L = 3 local experts:
+    # expert 0 <- records 0, 2; expert 1 <- record 0; expert 2 <- record 1
+    e = oracle.expand_records(np.array([3, 4, 1], np.uint64), 3)
+    np.testing.assert_array_equal(e["expert_counts"], [2, 1, 1])
+    np.testing.assert_array_equal(e["expert_offsets"], [0, 2, 3, 4])
+    np.testing.assert_array_equal(e["pos"], [[0, 2, -1], [-1, -1, 3], [1, -1, -1]])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_expanding_each_ranks_records_gives_its_expert_segment(seed):
+    """The receiver's side: rank r's records (its segment of the coalesced
+    send buffer, with their masks) expanded into its local experts' slots give
+    exactly rank r's segment of the plain dispatch, and its expert counts."""
+    rng = np.random.default_rng(700 + seed)
+    R = int(rng.choice([1, 2, 4, 8]))
+    L = int(rng.choice([1, 3, 8, 16]))
+    E, T, H = R * L, int(rng.integers(1, 80)), 8
+    k = int(rng.integers(1, E + 1))
+    idx = random_idx(rng, T, E, k)
+    x = rng.integers(0, 1 << 16, size=(T, H), dtype=np.uint16)
+    c = oracle.rank_coalesce(idx, E, R)
+    records = x[c["row_src"]]
+    lay = oracle.dispatch_layout(idx, E, R)
+    send = oracle.dispatch(x, lay["pos"])
+    for r in range(R):
+        a, b = c["rank_offsets"][r], c["rank_offsets"][r + 1]
+        e = oracle.expand_records(c["row_experts"][a:b], L)
+        np.testing.assert_array_equal(e["expert_counts"], lay["expert_counts"][r * L:(r + 1) * L])
+        n = int(e["expert_offsets"][L])
+        recv = np.empty((n, H), np.uint16)
+        for rec in range(b - a):
+            for i in range(L):
+                if e["pos"][rec, i] >= 0:
+                    recv[e["pos"][rec, i]] = records[a + rec]
+        lo, hi = lay["rank_offsets"][r], lay["rank_offsets"][r + 1]
+        np.testing.assert_array_equal(recv, send[lo:hi])
+
+
+def test_expand_records_rejects_a_bit_past_the_last_expert():
+    with pytest.raises(ValueError):
+        oracle.expand_records(np.array([1 << 5], np.uint64), 4)
