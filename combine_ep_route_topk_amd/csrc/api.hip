@@ -448,6 +448,45 @@ ep_status ep_rank_coalesce(const int32_t* topk_idx, int32_t T, int32_t k, int32_
                     fn);
 }
 
+size_t ep_expand_records_workspace_bytes(int32_t C, int32_t L)
+{
+    if (C < 1 || L < 1 || L > 64) return 0;
+    return ep::coalesce_plan(C, L, L).bytes;
+}
+
+ep_status ep_expand_records(const uint16_t* rows, const uint64_t* masks, int32_t C, int32_t H,
+                            int32_t L, int32_t* expert_counts, int32_t* expert_offsets,
+                            int32_t* pos, uint16_t* recv, int64_t recv_rows, void* workspace,
+                            size_t workspace_bytes, void* stream)
+{
+    const char* fn = "ep_expand_records";
+    TimingScope timing_scope;
+    if (C < 1) return fail(EP_ERR_INVALID_ARG, "%s: C=%d must be >= 1", fn, C);
+    if (L < 1 || L > 64) return fail(EP_ERR_INVALID_ARG, "%s: L=%d must be in [1, 64]", fn, L);
+    if (int64_t(C) * L >= (int64_t(1) << 30))
+        return fail(EP_ERR_UNSUPPORTED, "%s: C*L=%lld must be < 2^30", fn, (long long)C * L);
+    if (H < 8 || H % 8 != 0)
+        return fail(EP_ERR_INVALID_ARG, "%s: H=%d must be a positive multiple of 8", fn, H);
+    if (H > (1 << 20)) return fail(EP_ERR_UNSUPPORTED, "%s: H=%d exceeds 2^20", fn, H);
+    if (recv_rows < 0)
+        return fail(EP_ERR_INVALID_ARG, "%s: recv_rows=%lld must be >= 0", fn, (long long)recv_rows);
+    EP_REQUIRE_PTR(fn, rows, 16);
+    EP_REQUIRE_PTR(fn, masks, 8);
+    EP_REQUIRE_PTR(fn, expert_counts, 4);
+    EP_REQUIRE_PTR(fn, expert_offsets, 4);
+    EP_REQUIRE_PTR(fn, pos, 4);
+    EP_REQUIRE_PTR(fn, recv, 16);
+    EP_REQUIRE_PTR(fn, workspace, 256);
+    const size_t need = ep::coalesce_plan(C, L, L).bytes;
+    if (workspace_bytes < need)
+        return fail(EP_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn,
+                    workspace_bytes, need);
+    return launched(ep::launch_expand_records(rows, masks, C, H, L, expert_counts, expert_offsets,
+                                              pos, recv, recv_rows, workspace,
+                                              static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 ep_status ep_exchange_waves(int32_t N, int32_t* peer)
 {
     const char* fn = "ep_exchange_waves";
@@ -473,6 +512,8 @@ ep_status ep_get_device_error(const void* workspace, void* stream)
     if (head[1] == ep::kDevOk) return ok();
     if (head[1] == ep::kDevTimeout)
         return fail(EP_ERR_TIMEOUT, "%s: a bounded device-side wait expired", fn);
+    if (head[1] == ep::kDevOverflow)
+        return fail(EP_ERR_DEVICE, "%s: the slots outnumber the receive buffer's rows", fn);
     if (head[1] == ep::kDevSentinel)
         return fail(EP_ERR_DEVICE, "%s: a payload row began with the sentinel mode's reserved "
                     "pattern", fn);

@@ -25,6 +25,14 @@
 // Dispatching x with the first-pick positions (repeats -1, which ep_dispatch
 // skips) then writes every record exactly once.
 //
+// The receiver's side (ep_expand_records): the records of one rank, each with
+// its mask, expand into that rank's local experts' slots -- expert-major,
+// then in record order (StrataCL appendix, level 2: expert windows).  It is
+// a stable counting sort of the (record, set bit) pairs by expert, i.e. the
+// dispatch layout over C "tokens" with L "picks" (key = the bit's expert, or
+// -1 when clear) and L experts, followed by a dispatch of the record rows
+// with those positions into a receive buffer of a given row count.
+//
 // RailWave sec. 3.2, eq. (10): the cyclic pairwise exchange sends, in wave
 // k = 1..N-1, from node s to node (s + k) mod N, so every node has one
 // outgoing and one incoming peer per wave and every ordered pair appears
@@ -118,7 +126,66 @@ __global__ __launch_bounds__(kBlock) void coalesce_rows_kernel(
     if (pl.active && !valid) hdr->error = kDevBadExpert;
 }
 
+// ---------------------------------------------------------------- receiver
+// A thread per (record c, local expert i): key = i when record c feeds expert
+// i (bit i of its mask), else -1.
+__global__ __launch_bounds__(kBlock) void expand_keys_kernel(const uint64_t* __restrict__ masks,
+                                                             int C, int L,
+                                                             int32_t* __restrict__ keys)
+{
+    const int64_t q = int64_t(blockIdx.x) * kBlock + threadIdx.x;
+    if (q >= int64_t(C) * L) return;
+    const int64_t c = q / L;
+    const int i = int(q - c * L);
+    keys[q] = ((masks[c] >> i) & 1u) ? i : -1;
+}
+
+// After the layout has written its error word: a mask bit at or past L (no
+// such expert) or more slots than the receive buffer has rows is an error.
+// Two such faults at once may report either one.
+__global__ __launch_bounds__(kBlock) void expand_finish_kernel(
+    const uint64_t* __restrict__ masks, int C, int L, const int32_t* __restrict__ expert_offsets,
+    int64_t recv_rows, WsHeader* __restrict__ hdr)
+{
+    bool bad = false;
+    if (L < 64)
+        for (int64_t c = int64_t(blockIdx.x) * kBlock + threadIdx.x; c < C;
+             c += int64_t(gridDim.x) * kBlock)
+            bad |= (masks[c] >> L) != 0;
+    if (bad) hdr->error = kDevBadExpert;
+    if (blockIdx.x == 0 && threadIdx.x == 0 && int64_t(expert_offsets[L]) > recv_rows)
+        hdr->error = kDevOverflow;
+}
+
 }  // namespace
+
+hipError_t launch_expand_records(const uint16_t* rows, const uint64_t* masks, int C, int H, int L,
+                                 int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
+                                 uint16_t* recv, int64_t recv_rows, void* ws, hipStream_t s)
+{
+    // the layout over (C records) x (L bits) with the L local experts as its
+    // experts and one rank; its workspace shape is the coalescing pass's
+    const CoalescePlan p = coalesce_plan(C, L, L);
+    char* w = static_cast<char*>(ws);
+    int32_t* keys = reinterpret_cast<int32_t*>(w + p.off_keys);
+    int32_t* lay_rank_counts = reinterpret_cast<int32_t*>(w + p.off_rank_counts);
+    int32_t* lay_rank_offsets = reinterpret_cast<int32_t*>(w + p.off_rank_offsets);
+    const int64_t n = int64_t(C) * L;
+    EP_LAUNCH(expand_keys_kernel, dim3(uint32_t((n + kBlock - 1) / kBlock)), dim3(kBlock), 0, s,
+              masks, C, L, keys);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_dispatch_layout_skips(keys, C, L, L, 1, expert_counts, expert_offsets,
+                                     lay_rank_counts, lay_rank_offsets, pos, nullptr, w, -1, s);
+    if (e != hipSuccess) return e;
+    const uint32_t bound = uint32_t(recv_rows < n ? recv_rows : n);
+    e = launch_dispatch_bounded(rows, C, H, L, pos, recv, bound, s);
+    if (e != hipSuccess) return e;
+    const int64_t blocks = (int64_t(C) + kBlock - 1) / kBlock;
+    EP_LAUNCH(expand_finish_kernel, dim3(uint32_t(blocks < 1024 ? blocks : 1024)), dim3(kBlock),
+              0, s, masks, C, L, expert_offsets, recv_rows, reinterpret_cast<WsHeader*>(w));
+    return hipGetLastError();
+}
 
 hipError_t launch_rank_coalesce(const int32_t* topk_idx, int T, int k, int E, int R,
                                 int32_t* rank_counts, int32_t* rank_offsets,

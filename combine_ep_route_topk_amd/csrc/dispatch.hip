@@ -74,14 +74,15 @@ __device__ __noinline__ void copy_tail(const char* __restrict__ src, char* __res
 // waves) already saturate the write path (measured at the same shape:
 // dispatch alone 92.4 -> 87.7-89.0 us with 96-128 workgroups; the whole
 // route/layout/dispatch/combine step 205.5-207.2 -> 199.4-202.1 us).
+// Rows at or past S (T*k, or a smaller receive buffer's row count) are never
+// written.
 template <int U>
 __global__ __launch_bounds__(kBlock) void dispatch_kernel(
     const uint16_t* __restrict__ x, int T, int nvec, int k,
     const int32_t* __restrict__ pos, uint16_t* __restrict__ send,
-    uint32_t segs, uint32_t items)
+    uint32_t segs, uint32_t items, uint32_t S)
 {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const uint32_t S = uint32_t(T) * uint32_t(k);
     const int64_t row_bytes = int64_t(nvec) * 16;
     char* dst = reinterpret_cast<char*>(send);
     for (uint32_t b = blockIdx.x; b < items; b += gridDim.x) {
@@ -101,13 +102,13 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(
 
 template <int U>
 hipError_t launch_u(const uint16_t* x, int T, int nvec, int k, const int32_t* pos,
-                    uint16_t* send, uint32_t cap, hipStream_t s)
+                    uint16_t* send, uint32_t cap, uint32_t bound, hipStream_t s)
 {
     const uint32_t segs = uint32_t((nvec + kWave * U - 1) / (kWave * U));
     const uint32_t items = uint32_t((T + kWavesPerBlock - 1) / kWavesPerBlock) * segs;
     const uint32_t grid = items < cap ? items : cap;
     EP_LAUNCH((dispatch_kernel<U>), dim3(grid), dim3(kBlock), 0, s, x, T, nvec, k, pos,
-              send, segs, items);
+              send, segs, items, bound);
     return hipGetLastError();
 }
 
@@ -140,16 +141,23 @@ bool small_scatter(int T, int H, int k)
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int k, const int32_t* pos,
                            uint16_t* send, hipStream_t s)
 {
+    return launch_dispatch_bounded(x, T, H, k, pos, send, uint32_t(T) * uint32_t(k), s);
+}
+
+hipError_t launch_dispatch_bounded(const uint16_t* x, int T, int H, int k, const int32_t* pos,
+                                   uint16_t* send, uint32_t bound, hipStream_t s)
+{
     const int nvec = H / 8;                   // 16-byte vectors per row
     // A small batch is bound by latency, not by the write path: one vector per
     // lane and an uncapped grid put the most requests in flight (measured on
     // MI355X at T=128, H=7168, k=8: 8.2 -> 5.0 us).
-    if (small_scatter(T, H, k)) return launch_u<1>(x, T, nvec, k, pos, send, kMaxGrid, s);
+    if (small_scatter(T, H, k))
+        return launch_u<1>(x, T, nvec, k, pos, send, kMaxGrid, bound, s);
     const uint32_t cap = dispatch_grid_cap();
-    if (nvec % (kWave * 7) == 0) return launch_u<7>(x, T, nvec, k, pos, send, cap, s);
-    if (nvec >= kWave * 8) return launch_u<8>(x, T, nvec, k, pos, send, cap, s);
-    if (nvec >= kWave * 4) return launch_u<4>(x, T, nvec, k, pos, send, cap, s);
-    return launch_u<1>(x, T, nvec, k, pos, send, cap, s);
+    if (nvec % (kWave * 7) == 0) return launch_u<7>(x, T, nvec, k, pos, send, cap, bound, s);
+    if (nvec >= kWave * 8) return launch_u<8>(x, T, nvec, k, pos, send, cap, bound, s);
+    if (nvec >= kWave * 4) return launch_u<4>(x, T, nvec, k, pos, send, cap, bound, s);
+    return launch_u<1>(x, T, nvec, k, pos, send, cap, bound, s);
 }
 
 }  // namespace ep

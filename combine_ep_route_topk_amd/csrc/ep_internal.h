@@ -50,7 +50,8 @@ constexpr int kMaxK = 64;
 constexpr uint32_t kMaxGrid = uint32_t(1) << 20;
 
 // Error codes stored in a workspace's error word (host maps them to ep_status).
-enum : uint32_t { kDevOk = 0, kDevBadExpert = 1, kDevTimeout = 2, kDevSentinel = 3 };
+enum : uint32_t { kDevOk = 0, kDevBadExpert = 1, kDevTimeout = 2, kDevSentinel = 3,
+                  kDevOverflow = 4 };
 
 // Magic words marking initialised workspaces.
 constexpr uint32_t kLayoutMagic = 0x45504C57u;   // "EPLW"
@@ -146,6 +147,8 @@ struct CoalescePlan {
     size_t bytes;
 };
 
+// The receiver's expansion uses the same shape of workspace: the layout's
+// over (C records, L bits, L experts), the keys, and one rank's outputs.
 inline CoalescePlan coalesce_plan(int T, int k, int R) {
     CoalescePlan c{};
     c.lay = layout_plan(T, k, R);
@@ -204,11 +207,17 @@ hipError_t launch_rank_coalesce(const int32_t* topk_idx, int T, int k, int E, in
                                 int32_t* rank_counts, int32_t* rank_offsets,
                                 int32_t* row_of_pick, int32_t* send_pos, int32_t* row_src,
                                 uint64_t* row_experts, void* ws, hipStream_t s);
+hipError_t launch_expand_records(const uint16_t* rows, const uint64_t* masks, int C, int H, int L,
+                                 int32_t* expert_counts, int32_t* expert_offsets, int32_t* pos,
+                                 uint16_t* recv, int64_t recv_rows, void* ws, hipStream_t s);
 // Host: peer[(w-1)*N + s] = (s + w) mod N for w = 1..N-1.
 void exchange_waves(int32_t N, int32_t* peer);
 
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int k, const int32_t* pos,
                            uint16_t* send, hipStream_t s);
+// Dispatch into a buffer of `bound` rows: positions at or past it are skipped.
+hipError_t launch_dispatch_bounded(const uint16_t* x, int T, int H, int k, const int32_t* pos,
+                                   uint16_t* send, uint32_t bound, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* pos, const float* w,
                           int T, int H, int k, uint16_t* out, hipStream_t s);

@@ -59,6 +59,9 @@ _SIGS = {
     "ep_rank_coalesce": ([_P, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P, _P, _P, _sz, _P],
                          ctypes.c_int),
     "ep_exchange_waves": ([_i32, _P], ctypes.c_int),
+    "ep_expand_records_workspace_bytes": ([_i32, _i32], _sz),
+    "ep_expand_records": ([_P, _P, _i32, _i32, _i32, _P, _P, _P, _P, ctypes.c_int64, _P, _sz, _P],
+                          ctypes.c_int),
     "ep_lpt_task_count": ([_P, _i32, ctypes.c_int64], ctypes.c_int64),
     "ep_lpt_partition": ([_P, _i32, ctypes.c_int64, ctypes.c_int64, _P, _P, _P, _P, _i32, _i32,
                           _P, ctypes.c_int64, _P, _P], ctypes.c_int),
@@ -383,6 +386,36 @@ def ep_rank_coalesce(topk_idx: torch.Tensor, E: int, R: int, out: dict | None = 
         _ptr(topk_idx), T, k, E, R, _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]),
         _ptr(out["row_of_pick"]), _ptr(out["send_pos"]), _ptr(out["row_src"]),
         _ptr(out["row_experts"]), _ptr(ws), ws.numel(), _P(_stream(stream, dev))))
+    return out
+
+
+def ep_expand_records(rows: torch.Tensor, masks: torch.Tensor, L: int, recv_rows: int,
+                      out: dict | None = None, stream=None) -> dict:
+    """rows bf16 [C][H] (one rank's records), masks int64 [C] (u64 bit masks
+    of local experts) -> dict(expert_counts i32 [L], expert_offsets i32 [L+1],
+    pos i32 [C][L], recv bf16 [recv_rows][H], workspace): the records expanded
+    into the rank's local experts' slots."""
+    _bits_ok(rows, "rows")
+    C, H = rows.shape
+    _need(masks, "masks", torch.int64, (C,))
+    dev = rows.device
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = dict(expert_counts=torch.empty(L, **i32), expert_offsets=torch.empty(L + 1, **i32),
+                   pos=torch.empty((C, L), **i32),
+                   recv=torch.empty((recv_rows, H), dtype=rows.dtype, device=dev),
+                   workspace=torch.empty(int(_lib.ep_expand_records_workspace_bytes(C, L)),
+                                         dtype=torch.uint8, device=dev))
+    _need(out["expert_counts"], "expert_counts", torch.int32, (L,))
+    _need(out["expert_offsets"], "expert_offsets", torch.int32, (L + 1,))
+    _need(out["pos"], "pos", torch.int32, (C, L))
+    _bits_ok(out["recv"], "recv", (recv_rows, H))
+    ws = out["workspace"]
+    _need(ws, "workspace", torch.uint8)
+    _check(_lib.ep_expand_records(
+        _ptr(rows), _ptr(masks), C, H, L, _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
+        _ptr(out["pos"]), _ptr(out["recv"]), recv_rows, _ptr(ws), ws.numel(),
+        _P(_stream(stream, dev))))
     return out
 
 

@@ -72,7 +72,8 @@ const char* ep_last_error(void);
  * device work only).  After this call, the NEXT compute entry point called on
  * the same thread (ep_route_topk, ep_dispatch_layout, ep_dispatch, ep_combine,
  * ep_combine_grad, ep_dispatch_grad, ep_fused_dispatch_combine[_sync],
- * ep_expert_slices, ep_window_copy, ep_rank_coalesce) records `start_event` when its first kernel
+ * ep_expert_slices, ep_window_copy, ep_rank_coalesce, ep_expand_records) records `start_event` when
+ * its first kernel
  * starts and `stop_event` when its last kernel ends, taken from the kernels'
  * own dispatch packets -- the same interval a kernel-trace profiler reports,
  * with no marker packet in between.  Either event may be NULL.  The hook then
@@ -406,6 +407,36 @@ ep_status ep_rank_coalesce(const int32_t* topk_idx, int32_t T, int32_t k, int32_
                            int32_t* rank_counts, int32_t* rank_offsets, int32_t* row_of_pick,
                            int32_t* send_pos, int32_t* row_src, uint64_t* row_experts,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * A receiver's expansion of coalesced records into its local experts' slots
+ * [RAIL sec. 3.1-3.2 (a record carries several destinations of one token);
+ * STRATA appendix "Hierarchical Workload Partitioning for MoE
+ * Dispatch/Combine", level 2: expert windows].  Record c (in arrival order)
+ * feeds local expert i when bit i of masks[c] is set; slots are
+ * expert-major, then in record order.  For one rank's segment of
+ * ep_rank_coalesce's records (rows [rank_offsets[r], rank_offsets[r+1]) and
+ * their row_experts), recv equals that rank's segment of the plain dispatch.
+ *   rows           bf16 [C][H]   the records' rows; H % 8 == 0.
+ *   masks          u64 [C]       each record's local experts (bits < L).
+ *   expert_counts  i32 [L]       out: slots per local expert.
+ *   expert_offsets i32 [L+1]     out: exclusive prefix; [L] = total slots.
+ *   pos            i32 [C][L]    out: slot of record c's row for expert i,
+ *                                -1 where bit i is clear.
+ *   recv           bf16 [recv_rows][H]  out: slot rows; rows at or past the
+ *                                total are untouched.
+ * C >= 1, L in [1, 64], C*L < 2^30.  workspace:
+ * ep_expand_records_workspace_bytes(C, L) bytes, 256-byte aligned,
+ * caller-owned; no initialisation needed.  Errors: EP_ERR_INVALID_ARG,
+ * EP_ERR_UNSUPPORTED, EP_ERR_WORKSPACE as for the other entry points.  A mask
+ * bit at or past L, or more slots than recv_rows (the rows past recv_rows are
+ * not written), makes ep_get_device_error(workspace) report EP_ERR_DEVICE.
+ * ------------------------------------------------------------------------- */
+size_t ep_expand_records_workspace_bytes(int32_t C, int32_t L);
+ep_status ep_expand_records(const uint16_t* rows, const uint64_t* masks, int32_t C, int32_t H,
+                            int32_t L, int32_t* expert_counts, int32_t* expert_offsets,
+                            int32_t* pos, uint16_t* recv, int64_t recv_rows, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Cyclic pairwise exchange waves [RAIL sec. 3.2, eq. (10)]: with N nodes,

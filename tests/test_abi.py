@@ -175,6 +175,22 @@ def test_rank_coalesce_validation(ep):
     assert rc == ep.EP_ERR_WORKSPACE
 
 
+def test_expand_records_validation(ep):
+    lib = ep.library()
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    need = lib.ep_expand_records_workspace_bytes(100, 8)
+    assert need > 0 and lib.ep_expand_records_workspace_bytes(100, 65) == 0
+    args = lambda C, H, L, nb=need, rows=f: (rows, f, C, H, L, f, f, f, f, ctypes.c_int64(64),
+                                             f, nb, None)
+    assert call(lib, "ep_expand_records", *args(0, 16, 8))[0] == ep.EP_ERR_INVALID_ARG
+    assert call(lib, "ep_expand_records", *args(100, 16, 65))[0] == ep.EP_ERR_INVALID_ARG
+    assert call(lib, "ep_expand_records", *args(100, 12, 8))[0] == ep.EP_ERR_INVALID_ARG
+    assert call(lib, "ep_expand_records", *args(100, 16, 8, rows=P(FAKE + 8)))[0] == \
+        ep.EP_ERR_INVALID_ARG                                   # rows not 16-byte aligned
+    assert call(lib, "ep_expand_records", *args(100, 16, 8, nb=need - 1))[0] == ep.EP_ERR_WORKSPACE
+
+
 def test_exchange_waves_host_function(ep):
     """Host-only: the library's cyclic exchange waves equal the oracle's, and
     the page's 4-node permutation schedule (RailWave App. A.6, Table 8)."""

@@ -487,3 +487,69 @@ def test_emulated_rank_coalesce_reports_bad_ids(emu):
     recs = sorted({(int(e) // (E // R), t) for t in range(T) for j, e in enumerate(bad[t]) if keep[t, j]})
     assert int(got["rank_offsets"][R]) == len(recs)
     np.testing.assert_array_equal(got["row_src"][:len(recs)], [t for _, t in recs])
+
+
+def expand_emu(L_lib, rows, masks, L, recv_rows):
+    C, H = rows.shape
+    out = dict(expert_counts=np.zeros(L, np.int32), expert_offsets=np.zeros(L + 1, np.int32),
+               pos=np.zeros((C, L), np.int32))
+    recv = aligned(max(recv_rows, 1) * H * 2, 16).view(np.uint16)[:recv_rows * H].reshape(recv_rows, H)
+    recv[:] = 0xFFFF
+    L_lib.ep_expand_records_workspace_bytes.restype = ctypes.c_size_t
+    ws = aligned(L_lib.ep_expand_records_workspace_bytes(C, L))
+    ra = aligned(rows.nbytes, 16).view(np.uint16).reshape(C, H)
+    ra[:] = rows
+    ma = np.ascontiguousarray(masks, dtype=np.uint64)
+    L_lib.ep_expand_records.argtypes = [ctypes.c_void_p] * 2 + [ctypes.c_int32] * 3 + \
+        [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    rc = L_lib.ep_expand_records(p(ra), p(ma), C, H, L, p(out["expert_counts"]),
+                                 p(out["expert_offsets"]), p(out["pos"]), p(recv), recv_rows,
+                                 p(ws), ws.size, None)
+    assert rc == 0, L_lib.ep_last_error().decode()
+    return out, recv, L_lib.ep_get_device_error(p(ws), None)
+
+
+@pytest.mark.parametrize("T,E,R,k,seed", [(300, 64, 8, 6, 1401), (128, 256, 32, 8, 1402),
+                                          (90, 128, 2, 8, 1403)])
+def test_emulated_expand_records_gives_each_ranks_segment(emu, T, E, R, k, seed):
+    """The receiver's side of coalescing: each rank's records, expanded into
+    its local experts' slots, equal its segment of the plain dispatch."""
+    rng = np.random.default_rng(seed)
+    idx, _ = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
+    H, L = 16, E // R
+    x = wl.make_rows(T, H, seed + 1)
+    c = oracle.rank_coalesce(idx, E, R)
+    lay = oracle.dispatch_layout(idx, E, R)
+    send = oracle.dispatch(x, lay["pos"])
+    records = x[c["row_src"]]
+    for r in range(R):
+        a, b = int(c["rank_offsets"][r]), int(c["rank_offsets"][r + 1])
+        if a == b:
+            continue
+        n = int(lay["rank_counts"][r])
+        got, recv, status = expand_emu(emu, records[a:b], c["row_experts"][a:b], L, n)
+        assert status == 0
+        ref = oracle.expand_records(c["row_experts"][a:b], L)
+        for key in ("expert_counts", "expert_offsets", "pos"):
+            np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+        np.testing.assert_array_equal(recv, send[lay["rank_offsets"][r]:lay["rank_offsets"][r + 1]])
+
+
+def test_emulated_expand_records_reports_overflow_and_stray_bits(emu):
+    rows = wl.make_rows(6, 8, 1410)
+    masks = np.array([3, 1, 2, 4, 1, 6], np.uint64)        # 9 slots over L = 3
+    got, recv, status = expand_emu(emu, rows, masks, 3, 9)
+    assert status == 0
+    got, recv, status = expand_emu(emu, rows, masks, 3, 7)  # room for 7 of 9 slots
+    assert status != 0
+    ref = oracle.expand_records(masks, 3)
+    full = np.full((9, 8), 0xFFFF, np.uint16)
+    for c in range(6):
+        for i in range(3):
+            if ref["pos"][c, i] >= 0:
+                full[ref["pos"][c, i]] = rows[c]
+    np.testing.assert_array_equal(recv, full[:7])           # nothing past the buffer
+    bad = masks.copy()
+    bad[2] |= np.uint64(1 << 3)                             # no local expert 3
+    _, _, status = expand_emu(emu, rows, bad, 3, 9)
+    assert status != 0

@@ -102,3 +102,54 @@ def test_coalesce_reports_bad_ids(epm):
     epm.ep_rank_coalesce(torch.from_numpy(good).to(DEV), E, R, out=got)
     torch.cuda.synchronize()
     assert epm.ep_get_device_error(got["workspace"]) == epm.EP_OK
+
+
+@pytest.mark.parametrize("name", ["decode", "glm45air", "dsv3"])
+def test_coalesced_exchange_end_to_end(epm, name):
+    """Sender and receiver of the coalesced exchange on one GPU: the records
+    (ep_rank_coalesce + ep_dispatch(send_pos)) of every rank, expanded by
+    ep_expand_records into that rank's local experts' slots, equal the rank's
+    segment of the plain dispatch, and its slot positions equal the oracle's."""
+    w = wl.WORKLOADS[name]
+    T, H, E, R, k = w.T, w.H, w.E, w.R, w.k
+    L = E // R
+    idx, _ = oracle.route_topk(wl.make_logits(w), k, 1)
+    x = wl.make_rows(T, H, w.seed)
+    d_idx, d_x = torch.from_numpy(idx).to(DEV), to_dev_bits(x)
+    say(f"coalesced exchange end to end {w.describe()}")
+    co = epm.ep_rank_coalesce(d_idx, E, R)
+    records = epm.ep_dispatch(d_x, co["send_pos"])
+    lay = epm.ep_dispatch_layout(d_idx, E, R)
+    plain = epm.ep_dispatch(d_x, lay["pos"])
+    torch.cuda.synchronize()
+    ro = co["rank_offsets"].cpu().numpy()
+    pro = lay["rank_offsets"].cpu().numpy()
+    masks = co["row_experts"]
+    ref = oracle.rank_coalesce(idx, E, R)
+    for r in range(R):
+        a, b = int(ro[r]), int(ro[r + 1])
+        if a == b:
+            continue
+        n = int(pro[r + 1] - pro[r])
+        got = epm.ep_expand_records(records[a:b], masks[a:b], L, n)
+        torch.cuda.synchronize()
+        assert epm.ep_get_device_error(got["workspace"]) == epm.EP_OK, f"rank {r}"
+        assert torch.equal(got["recv"].view(torch.int16), plain[pro[r]:pro[r + 1]].view(torch.int16)), f"rank {r}"
+        e_ref = oracle.expand_records(ref["row_experts"][a:b], L)
+        np.testing.assert_array_equal(got["pos"].cpu().numpy(), e_ref["pos"], err_msg=f"rank {r}")
+        np.testing.assert_array_equal(got["expert_counts"].cpu().numpy(),
+                                      lay["expert_counts"][r * L:(r + 1) * L].cpu().numpy())
+    # the plain dispatch itself against the oracle
+    assert np.array_equal(bits(plain), oracle.dispatch(x, oracle.dispatch_layout(idx, E, R)["pos"]))
+
+
+def test_expand_records_reports_overflow(epm):
+    rows = to_dev_bits(wl.make_rows(6, 64, 1420))
+    masks = torch.tensor([3, 1, 2, 4, 1, 6], dtype=torch.int64, device=DEV)    # 9 slots, L = 3
+    say("expand records into a buffer that is too small")
+    got = epm.ep_expand_records(rows, masks, 3, 7)
+    torch.cuda.synchronize()
+    assert epm.ep_get_device_error(got["workspace"]) == epm.EP_ERR_DEVICE
+    got = epm.ep_expand_records(rows, masks, 3, 9, out=None)
+    torch.cuda.synchronize()
+    assert epm.ep_get_device_error(got["workspace"]) == epm.EP_OK
