@@ -33,11 +33,17 @@ __device__ __forceinline__ int wave_sum(int v) {
 // have completed they are visible on every XCD, so a persistent caller can
 // publish "tile done" after a wait for its own stores instead of an L2
 // write-back.  `hist` is the block's LDS scratch.
-__device__ __forceinline__ void hist_tile(const int32_t* __restrict__ topk_idx, int64_t S,
-                                          int E, int nTiles, int tile,
-                                          int32_t* __restrict__ cnt,
-                                          int32_t* __restrict__ local_rank,
-                                          int32_t (*hist)[kMaxE])
+// The LDS part of hist_tile: after it, hist[w][e] holds wave w's exclusive
+// offset among the tile's slots of expert e (waves in order), key[c] / rank[c]
+// the expert (-1 if none) and in-wave rank of this lane's slot in chunk c, and
+// -- where given -- cnt[e * nTiles + tile] (agent-coherent store) and
+// sh_tot[e] (LDS) the tile's count of expert e.
+__device__ __forceinline__ void tile_ranks(const int32_t* __restrict__ topk_idx, int64_t S,
+                                           int E, int nTiles, int tile,
+                                           int32_t* __restrict__ cnt, int* sh_tot,
+                                           int32_t (*hist)[kMaxE],
+                                           int (&key)[kChunksPerWave],
+                                           int (&rank)[kChunksPerWave])
 {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -47,8 +53,6 @@ __device__ __forceinline__ void hist_tile(const int32_t* __restrict__ topk_idx, 
     __syncthreads();
 
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-    int key[kChunksPerWave];
-    int rank[kChunksPerWave];
     const int64_t wave_first =
         int64_t(tile) * kTileSlots + int64_t(wave) * kChunksPerWave * kWave;
 #pragma unroll
@@ -80,10 +84,27 @@ __device__ __forceinline__ void hist_tile(const int32_t* __restrict__ topk_idx, 
             hist[w][e] = run;
             run += c;
         }
-        st_relaxed(reinterpret_cast<uint32_t*>(&cnt[int64_t(e) * nTiles + tile]), uint32_t(run));
+        if (cnt)
+            st_relaxed(reinterpret_cast<uint32_t*>(&cnt[int64_t(e) * nTiles + tile]),
+                       uint32_t(run));
+        if (sh_tot) sh_tot[e] = run;
     }
     __syncthreads();
+}
 
+__device__ __forceinline__ void hist_tile(const int32_t* __restrict__ topk_idx, int64_t S,
+                                          int E, int nTiles, int tile,
+                                          int32_t* __restrict__ cnt,
+                                          int32_t* __restrict__ local_rank,
+                                          int32_t (*hist)[kMaxE])
+{
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int lane = lane_id();
+    int key[kChunksPerWave];
+    int rank[kChunksPerWave];
+    tile_ranks(topk_idx, S, E, nTiles, tile, cnt, nullptr, hist, key, rank);
+    const int64_t wave_first =
+        int64_t(tile) * kTileSlots + int64_t(wave) * kChunksPerWave * kWave;
 #pragma unroll
     for (int c = 0; c < kChunksPerWave; ++c) {
         const int64_t s = wave_first + c * kWave + lane;

@@ -307,23 +307,83 @@ __global__ __launch_bounds__(kBlock) void layout_scanpos_kernel(
 }
 
 // A layout of one tile (T*k <= kTileSlots, e.g. a decode batch): histogram,
-// scan and positions in ONE workgroup and one launch -- nothing crosses
-// workgroups, so the kernel boundary between hist and scan+positions is not
-// needed.  The workgroup's own stores of cnt and local_rank are visible to
-// its other threads after the barrier.
+// scan and positions in ONE workgroup and one launch, with nothing in global
+// memory between the steps -- the per-expert totals and each wave's offsets
+// stay in LDS and every slot's expert and in-wave rank in registers, so the
+// slot ids are read once and no counter or rank makes a round trip.
 __global__ __launch_bounds__(kBlock) void layout_single_kernel(
     const int32_t* __restrict__ topk_idx, int64_t S, int E, int R,
-    int32_t* __restrict__ cnt, int32_t* __restrict__ local_rank,
     int32_t* __restrict__ expert_counts, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ rank_counts, int32_t* __restrict__ rank_offsets,
     int32_t* __restrict__ pos, int32_t* __restrict__ slot_src, WsHeader* __restrict__ hdr,
     int64_t expect)
 {
     __shared__ int32_t hist[kWavesPerBlock][kMaxE];
-    hist_tile(topk_idx, S, E, 1, 0, cnt, local_rank, hist);
+    __shared__ int sh_tot[kMaxE];
+    __shared__ int sh_off[kMaxE + 1];
+    __shared__ int sh_wave_total[kWavesPerBlock];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = lane_id();
+    int key[kChunksPerWave];
+    int rank[kChunksPerWave];
+    tile_ranks(topk_idx, S, E, 1, 0, nullptr, sh_tot, hist, key, rank);
+
+    // exclusive scan of the totals over the experts, kExpPerThread per thread
+    int tot[kExpPerThread];
+    int tsum = 0;
+#pragma unroll
+    for (int q = 0; q < kExpPerThread; ++q) {
+        const int e = tid * kExpPerThread + q;
+        tot[q] = e < E ? sh_tot[e] : 0;
+        tsum += tot[q];
+    }
+    const int incl = wave_inclusive_sum(tsum);
+    if (lane == kWave - 1) sh_wave_total[wave] = incl;
     __syncthreads();
-    scanpos_tile(0, topk_idx, S, E, R, 1, cnt, local_rank, expert_counts, expert_offsets,
-                 rank_counts, rank_offsets, pos, slot_src, hdr, expect);
+    int run = incl - tsum;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w)
+        if (w < wave) run += sh_wave_total[w];
+#pragma unroll
+    for (int q = 0; q < kExpPerThread; ++q) {
+        const int e = tid * kExpPerThread + q;
+        if (e < E) {
+            sh_off[e] = run;
+            expert_offsets[e] = run;
+            expert_counts[e] = tot[q];
+            if (e == E - 1) {
+                sh_off[E] = run + tot[q];
+                expert_offsets[E] = run + tot[q];
+            }
+        }
+        run += tot[q];
+    }
+    __syncthreads();
+    const int L = E / R;
+    for (int r = tid; r <= R; r += kBlock) {
+        rank_offsets[r] = sh_off[r * L];
+        if (r < R) rank_counts[r] = sh_off[(r + 1) * L] - sh_off[r * L];
+    }
+    if (tid == 0) {
+        hdr->error = expect >= 0 && sh_off[E] != expect ? kDevBadExpert : kDevOk;
+        hdr->magic = kLayoutMagic;
+    }
+    // positions: the expert's offset, the wave's offset inside the expert,
+    // the slot's rank inside the wave
+    const int64_t wave_first = int64_t(wave) * kChunksPerWave * kWave;
+#pragma unroll
+    for (int c = 0; c < kChunksPerWave; ++c) {
+        const int64_t s = wave_first + c * kWave + lane;
+        if (s >= S) continue;
+        if (key[c] >= 0) {
+            const int p = sh_off[key[c]] + hist[wave][key[c]] + rank[c];
+            pos[s] = p;
+            if (slot_src) slot_src[p] = int(s);
+        } else {
+            pos[s] = -1;
+        }
+    }
 }
 
 }  // namespace
@@ -353,9 +413,9 @@ hipError_t launch_dispatch_layout_skips(const int32_t* topk_idx, int T, int k, i
     int32_t* rank = reinterpret_cast<int32_t*>(w + p.off_rank);
 
     if (p.nTiles == 1) {
-        EP_LAUNCH(layout_single_kernel, dim3(1), dim3(kBlock), 0, s, topk_idx, p.S, E, R, cnt,
-                  rank, expert_counts, expert_offsets, rank_counts, rank_offsets, pos, slot_src,
-                  hdr, expect);
+        EP_LAUNCH(layout_single_kernel, dim3(1), dim3(kBlock), 0, s, topk_idx, p.S, E, R,
+                  expert_counts, expert_offsets, rank_counts, rank_offsets, pos, slot_src, hdr,
+                  expect);
         return hipGetLastError();
     }
     EP_LAUNCH(layout_hist_kernel, dim3(p.nTiles), dim3(kBlock), 0, s,
