@@ -189,6 +189,17 @@ __device__ __forceinline__ void scanpos_tile(
     const int wave = tid / kWave;
     const int lane = lane_id();
 
+    // this thread's slots of the tile: their ids and ranks are loaded first,
+    // so those loads overlap the counter loads below
+    constexpr int kSlotsPerThread = kTileSlots / kBlock;
+    int se[kSlotsPerThread], sr[kSlotsPerThread];
+#pragma unroll
+    for (int u = 0; u < kSlotsPerThread; ++u) {
+        const int64_t s = int64_t(tile) * kTileSlots + u * kBlock + tid;
+        se[u] = s < S ? topk_idx[s] : -1;
+        sr[u] = s < S && unsigned(se[u]) < unsigned(E) ? local_rank[s] : 0;
+    }
+
     // per expert: its total over all tiles and its count before this tile.
     // Each round issues all its loads (kExpPerThread experts x 4 vectors of 4
     // counters) before adding any: the counters come from L2, and a loop of
@@ -280,12 +291,13 @@ __device__ __forceinline__ void scanpos_tile(
     }
 
     // positions of this tile's slots
-    for (int i = tid; i < kTileSlots; i += kBlock) {
-        const int64_t s = int64_t(tile) * kTileSlots + i;
+#pragma unroll
+    for (int u = 0; u < kSlotsPerThread; ++u) {
+        const int64_t s = int64_t(tile) * kTileSlots + u * kBlock + tid;
         if (s >= S) break;
-        const int e = topk_idx[s];
+        const int e = se[u];
         if (unsigned(e) < unsigned(E)) {
-            const int p = sh_base[e] + local_rank[s];
+            const int p = sh_base[e] + sr[u];
             pos[s] = p;
             if (slot_src) slot_src[p] = int(s);
         } else {
