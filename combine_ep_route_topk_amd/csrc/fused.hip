@@ -822,8 +822,15 @@ __global__ __launch_bounds__(kBlock) void sentinel_reset_kernel(uint8_t* rows, i
         store16(rows + s * stride, v);
 }
 
-// Resident workgroups of the persistent kernel on the current device
-// (cached per device and instantiation; atomic entries, as above).
+// The persistent grid: at most kFusedPerCu workgroups per CU, and no more
+// than can be resident (cached per device and instantiation; atomic entries,
+// as above).  Fewer workgroups than fit leave fewer concurrent streams of
+// scattered row writes and fewer pollers, as in dispatch's capped grid
+// (measured on MI355X at T=4096, H=7168, k=8, one call: 217.7 us with every
+// resident workgroup (5 per CU), 212.1 / 209.6 / 206.5 us with 256 / 384 /
+// 512 workgroups; the other sync modes alike).
+constexpr int kFusedPerCu = 2;
+
 int resident_grid(const void* kernel) {
     static std::atomic<int> cached[64][2];
     int dev = 0;
@@ -836,6 +843,7 @@ int resident_grid(const void* kernel) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
+    if (per_cu > kFusedPerCu) per_cu = kFusedPerCu;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus < 1)
         cus = 256;
