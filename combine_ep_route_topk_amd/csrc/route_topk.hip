@@ -6,8 +6,12 @@
 // softmax is monotone, so the picks are the same and stay exact).
 //
 // Mapping: a group of G lanes (a power of two, G >= k) owns one token; lane g
-// holds logits e = i*G + g for i < nv = ceil(E/G) <= 16, so each load
-// instruction reads G consecutive floats of a row.  A pick is one 64-bit key:
+// holds up to 16 logits of the row.  With E % 4 == 0 and 16-byte aligned
+// logits, lane g loads 16-byte vectors: its key i holds expert
+// ((i/4)*G + g)*4 + i%4, so each load instruction reads 4*G consecutive
+// floats of a row and a lane issues 4 loads instead of 16 (measured on MI355X
+// at T=4096, E=256, k=8: 10.1 -> 9.1 us warm, 14.4 -> 12.0 us cold); else
+// key i holds expert i*G + g (nv = ceil(E/G) <= 16 keys).  A pick is one 64-bit key:
 // the logit's bits made order-preserving as an unsigned integer (with -0.0
 // read as +0.0, since the two compare equal) in the high half and ~e in the
 // low half, so the largest key is the largest logit with the lowest expert
@@ -85,7 +89,13 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-template <int G>
+// The expert that lane g's key i holds.
+template <int G, bool VEC>
+__device__ __forceinline__ int slot_expert(int i, int g) {
+    return VEC ? ((i >> 2) * G + g) * 4 + (i & 3) : i * G + g;
+}
+
+template <int G, bool VEC>
 __global__ __launch_bounds__(kBlock) void route_topk_kernel(
     const float* __restrict__ logits, int T, int E, int k, int normalize,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w)
@@ -100,12 +110,31 @@ __global__ __launch_bounds__(kBlock) void route_topk_kernel(
 
     float v[kMaxNv];
     uint64_t key[kMaxNv];
+    if constexpr (VEC) {                 // E % 4 == 0: a vector is all inside or all past E
 #pragma unroll
-    for (int i = 0; i < kMaxNv; ++i) {
-        const int e = i * G + g;
-        const bool ok = live && i < nv && e < E;
-        v[i] = ok ? row[e] : 0.0f;
-        key[i] = ok ? (uint64_t(order_bits(v[i])) << 32) | uint32_t(~uint32_t(e)) : 0;
+        for (int i = 0; i < kMaxNv; i += 4) {
+            const int e0 = slot_expert<G, true>(i, g);
+            const bool ok = live && e0 < E;
+            const float4 f = ok ? *reinterpret_cast<const float4*>(row + e0)
+                                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            v[i] = f.x;
+            v[i + 1] = f.y;
+            v[i + 2] = f.z;
+            v[i + 3] = f.w;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                key[i + c] = ok ? (uint64_t(order_bits(v[i + c])) << 32) |
+                                      uint32_t(~uint32_t(e0 + c))
+                                : 0;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kMaxNv; ++i) {
+            const int e = slot_expert<G, false>(i, g);
+            const bool ok = live && i < nv && e < E;
+            v[i] = ok ? row[e] : 0.0f;
+            key[i] = ok ? (uint64_t(order_bits(v[i])) << 32) | uint32_t(~uint32_t(e)) : 0;
+        }
     }
 
     uint64_t my_key = 0, top_key = 0;
@@ -133,7 +162,7 @@ __global__ __launch_bounds__(kBlock) void route_topk_kernel(
         float z = 0.0f;
 #pragma unroll
         for (int i = 0; i < kMaxNv; ++i)
-            if (i < nv && i * G + g < E) z += expf(v[i] - m);
+            if ((VEC || i < nv) && slot_expert<G, VEC>(i, g) < E) z += expf(v[i] - m);
         denom = group_sum<G>(z);
     }
     if (live && g < k) {
@@ -148,8 +177,12 @@ hipError_t launch_g(const float* logits, int T, int E, int k, int normalize,
 {
     const int64_t threads = int64_t(T) * G;
     const int grid = int((threads + kBlock - 1) / kBlock);
-    EP_LAUNCH((route_topk_kernel<G>), dim3(grid), dim3(kBlock), 0, s,
-              logits, T, E, k, normalize, idx, w);
+    if (E % 4 == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0)
+        EP_LAUNCH((route_topk_kernel<G, true>), dim3(grid), dim3(kBlock), 0, s,
+                  logits, T, E, k, normalize, idx, w);
+    else
+        EP_LAUNCH((route_topk_kernel<G, false>), dim3(grid), dim3(kBlock), 0, s,
+                  logits, T, E, k, normalize, idx, w);
     return hipGetLastError();
 }
 

@@ -28,6 +28,8 @@ typedef void* hipStream_t;
 enum { hipSuccess = 0, hipErrorInvalidValue = 1, hipErrorNotSupported = 801 };
 struct alignas(16) int4 { int x, y, z, w; };
 inline int4 make_int4(int a, int b, int c, int d) { return int4{a, b, c, d}; }
+struct alignas(16) float4 { float x, y, z, w; };
+inline float4 make_float4(float a, float b, float c, float d) { return float4{a, b, c, d}; }
 struct dim3 { unsigned x, y, z; dim3(unsigned a = 1, unsigned b = 1, unsigned c = 1) : x(a), y(b), z(c) {} };
 
 namespace emu {

@@ -345,3 +345,20 @@ def test_dispatch_large_skips_picks_outside(epm):
         ref = oracle.dispatch(x, pos)
         ref[lost] = 0xFFFF
         assert np.array_equal(bits(send), ref)
+
+
+def test_route_unaligned_logits_take_the_scalar_path(epm):
+    """Logits 4- but not 16-byte aligned (and E % 4 != 0) read one float per
+    load; the picks and weights are the same as the oracle's."""
+    for T, E, k, norm in ((1000, 256, 8, 1), (333, 64, 6, 0), (77, 33, 5, 1)):
+        rng = np.random.default_rng(T + E)
+        logits = rng.standard_normal((T, E), dtype=np.float32)
+        flat = torch.empty(T * E + 1, dtype=torch.float32, device=DEV)
+        d = flat[1:].view(T, E)                    # 4 bytes past a 256-byte boundary
+        d.copy_(torch.from_numpy(logits))
+        say(f"route with unaligned logits T={T} E={E} k={k} normalize={norm}")
+        idx, w = epm.ep_route_topk(d, k, bool(norm))
+        torch.cuda.synchronize()
+        o_idx, o_w = oracle.route_topk(logits, k, norm)
+        np.testing.assert_array_equal(idx.cpu().numpy(), o_idx)
+        check_route_weights(w.cpu().numpy(), o_w, logits, o_idx, bool(norm), E)
