@@ -362,3 +362,59 @@ def test_route_unaligned_logits_take_the_scalar_path(epm):
         o_idx, o_w = oracle.route_topk(logits, k, norm)
         np.testing.assert_array_equal(idx.cpu().numpy(), o_idx)
         check_route_weights(w.cpu().numpy(), o_w, logits, o_idx, bool(norm), E)
+
+
+def test_maximum_slot_count(epm):
+    """T*k just under the 2^30 limit (T = 134,000,000 tokens, k = 8, E = 16,
+    H = 8): the layout's separate look-back scan over ~4,000 blocks, and every
+    output checked by properties on the GPU, plus sampled tokens against the
+    oracle.  About 50 GB of device memory."""
+    T, E, R, k, H = 134_000_000, 16, 4, 8, 8
+    S = T * k
+    assert S < (1 << 30)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(1_000_003)
+    say(f"maximum slot count T={T} k={k} E={E}: route")
+    logits = torch.randn((T, E), generator=g, dtype=torch.float32, device=DEV)
+    idx, w = epm.ep_route_topk(logits, k)
+    torch.cuda.synchronize()
+    sample = torch.randint(0, T, (10_000,), generator=g, device=DEV)
+    o_idx, o_w = oracle.route_topk(logits[sample].cpu().numpy(), k, 1)
+    np.testing.assert_array_equal(idx[sample].cpu().numpy(), o_idx)
+    check_route_weights(w[sample].cpu().numpy(), o_w, logits[sample].cpu().numpy(), o_idx, True, E)
+    del logits
+
+    say("maximum slot count: layout")
+    lay = epm.ep_dispatch_layout(idx, E, R)
+    torch.cuda.synchronize()
+    assert epm.ep_get_device_error(lay["workspace"]) == epm.EP_OK
+    flat = idx.reshape(-1)
+    counts = torch.bincount(flat, minlength=E)
+    assert torch.equal(lay["expert_counts"].long(), counts)
+    offs = torch.zeros(E + 1, dtype=torch.int64, device=DEV)
+    offs[1:] = torch.cumsum(counts, 0)
+    assert torch.equal(lay["expert_offsets"].long(), offs)
+    pos = lay["pos"].reshape(-1).long()
+    src = lay["slot_src"].long()
+    # pos and slot_src are inverse permutations of [0, S)
+    assert torch.equal(src[pos], torch.arange(S, device=DEV))
+    del pos
+    # slots in expert-major order, ascending source slot inside each expert
+    e_of = flat[src]
+    assert bool((e_of[1:] >= e_of[:-1]).all())
+    same = e_of[1:] == e_of[:-1]
+    assert bool((src[1:][same] > src[:-1][same]).all())
+    del e_of, same, src, flat
+    torch.cuda.empty_cache()
+
+    say("maximum slot count: dispatch and combine")
+    # finite rows (N(0, 1) in bf16), like the workloads': the round trip is exact for them
+    x = torch.randn((T, H), generator=g, dtype=torch.bfloat16, device=DEV)
+    send = epm.ep_dispatch(x, lay["pos"])
+    out = epm.ep_combine(send, lay["pos"], w)
+    torch.cuda.synchronize()
+    xs = x.view(torch.int16)
+    assert torch.equal(out.view(torch.int16), xs), "combine(dispatch(x)) != x"
+    rows = lay["pos"][sample].long()                       # [n][k] slots of sampled tokens
+    got = send.view(torch.int16)[rows.reshape(-1)].reshape(len(sample), k, H)
+    assert torch.equal(got, xs[sample][:, None, :].expand(-1, k, -1))
