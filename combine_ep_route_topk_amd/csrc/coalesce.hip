@@ -98,10 +98,15 @@ __global__ __launch_bounds__(kBlock) void coalesce_rows_kernel(
 {
     const PickLane pl = pick_lane(T, k);
     const uint32_t S = uint32_t(T) * uint32_t(k);
-    const int32_t e = pl.active ? topk_idx[pl.t * k + pl.j] : -1;
+    // both loads unconditional (an idle lane reads slot 0 and drops it), so
+    // they are in flight together rather than one after the other
+    const int64_t slot = pl.active ? pl.t * k + pl.j : 0;
+    const int32_t e_raw = topk_idx[slot];
+    const int32_t p_raw = send_pos[slot];
+    const int32_t e = pl.active ? e_raw : -1;
     const bool valid = uint32_t(e) < uint32_t(E);
     const int32_t r = valid ? e / L : -1;
-    const int32_t p = pl.active ? send_pos[pl.t * k + pl.j] : -1;
+    const int32_t p = pl.active ? p_raw : -1;
     int j0 = -1;
     int32_t row = -1;
     uint64_t mask = 0;

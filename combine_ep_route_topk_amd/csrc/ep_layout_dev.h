@@ -48,17 +48,29 @@ __device__ __forceinline__ void tile_ranks(const int32_t* __restrict__ topk_idx,
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int lane = lane_id();
+    const int64_t wave_first =
+        int64_t(tile) * kTileSlots + int64_t(wave) * kChunksPerWave * kWave;
+
+    // All chunks' slot ids are loaded first (their latency overlaps the
+    // counter reset), each from a clamped in-bounds address (slot 0 for a
+    // slot past S, then dropped): a guarded load would become a branch with a
+    // full memory wait inside, and the chunks' loads would go out one round
+    // trip at a time.
+    int ids[kChunksPerWave];
+#pragma unroll
+    for (int c = 0; c < kChunksPerWave; ++c) {
+        const int64_t s = wave_first + c * kWave + lane;
+        ids[c] = topk_idx[s < S ? s : 0];
+    }
 
     for (int i = tid; i < kWavesPerBlock * E; i += kBlock) hist[i / E][i % E] = 0;
     __syncthreads();
 
     const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-    const int64_t wave_first =
-        int64_t(tile) * kTileSlots + int64_t(wave) * kChunksPerWave * kWave;
 #pragma unroll
     for (int c = 0; c < kChunksPerWave; ++c) {
         const int64_t s = wave_first + c * kWave + lane;
-        const int e = s < S ? topk_idx[s] : -1;
+        const int e = s < S ? ids[c] : -1;
         const bool valid = unsigned(e) < unsigned(E);
         uint64_t peers = ballot(valid);
         for (int b = 0; b < nbits; ++b) {

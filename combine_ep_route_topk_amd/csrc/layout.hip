@@ -143,8 +143,9 @@ __global__ __launch_bounds__(kBlock) void layout_pos_kernel(
     const int64_t s = int64_t(blockIdx.x) * kBlock + threadIdx.x;
     if (s < S) {
         const int e = topk_idx[s];
+        const int lr = local_rank[s];     // loaded with the id, not after it
         if (unsigned(e) < unsigned(E)) {
-            const int p = base[int64_t(e) * nTiles + s / kTileSlots] + local_rank[s];
+            const int p = base[int64_t(e) * nTiles + s / kTileSlots] + lr;
             pos[s] = p;
             if (slot_src) slot_src[p] = int(s);
         } else {
@@ -190,14 +191,24 @@ __device__ __forceinline__ void scanpos_tile(
     const int lane = lane_id();
 
     // this thread's slots of the tile: their ids and ranks are loaded first,
-    // so those loads overlap the counter loads below
+    // so those loads overlap the counter loads below.  Every load in this
+    // kernel is unconditional, from a clamped in-bounds address whose value is
+    // then dropped (slot 0 for a slot past S; a rank whose slot has no valid
+    // expert is never used): a guarded load becomes a branch with a full
+    // memory wait inside, which would put the loads one round trip apart.
     constexpr int kSlotsPerThread = kTileSlots / kBlock;
     int se[kSlotsPerThread], sr[kSlotsPerThread];
 #pragma unroll
     for (int u = 0; u < kSlotsPerThread; ++u) {
         const int64_t s = int64_t(tile) * kTileSlots + u * kBlock + tid;
-        se[u] = s < S ? topk_idx[s] : -1;
-        sr[u] = s < S && unsigned(se[u]) < unsigned(E) ? local_rank[s] : 0;
+        const int64_t sc = s < S ? s : 0;
+        se[u] = topk_idx[sc];
+        sr[u] = local_rank[sc];
+    }
+#pragma unroll
+    for (int u = 0; u < kSlotsPerThread; ++u) {
+        const int64_t s = int64_t(tile) * kTileSlots + u * kBlock + tid;
+        if (s >= S) se[u] = -1;
     }
 
     // per expert: its total over all tiles and its count before this tile.
@@ -216,9 +227,11 @@ __device__ __forceinline__ void scanpos_tile(
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int t = t0 + 4 * m;
-                    c[q][m] = (e0 + q < E && t < nTiles)
-                                  ? *reinterpret_cast<const int4*>(cnt + int64_t(e0 + q) * nTiles + t)
-                                  : make_int4(0, 0, 0, 0);
+                    const bool in = e0 + q < E && t < nTiles;
+                    const int4 x =
+                        *reinterpret_cast<const int4*>(cnt + (in ? int64_t(e0 + q) * nTiles + t : 0));
+                    const int mk = in ? -1 : 0;       // a mask, not a branch
+                    c[q][m] = make_int4(x.x & mk, x.y & mk, x.z & mk, x.w & mk);
                 }
 #pragma unroll
             for (int q = 0; q < kExpPerThread; ++q)
@@ -236,9 +249,10 @@ __device__ __forceinline__ void scanpos_tile(
 #pragma unroll
             for (int q = 0; q < kExpPerThread; ++q)
 #pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    c[q][m] = (e0 + q < E && t0 + m < nTiles)
-                                  ? cnt[int64_t(e0 + q) * nTiles + t0 + m] : 0;
+                for (int m = 0; m < 4; ++m) {
+                    const bool in = e0 + q < E && t0 + m < nTiles;
+                    c[q][m] = cnt[in ? int64_t(e0 + q) * nTiles + t0 + m : 0] & (in ? -1 : 0);
+                }
 #pragma unroll
             for (int q = 0; q < kExpPerThread; ++q)
 #pragma unroll

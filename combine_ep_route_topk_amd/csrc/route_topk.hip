@@ -102,25 +102,33 @@ __global__ __launch_bounds__(kBlock) void route_topk_kernel(
 {
     const int g = threadIdx.x % G;
     const int64_t tok = (int64_t(blockIdx.x) * kBlock + threadIdx.x) / G;
-    // Out-of-range groups keep running (with no row) so that every DPP move
-    // reads an active lane; they just store nothing.
+    // Out-of-range groups keep running (on row 0, with every key dropped) so
+    // that every DPP move reads an active lane; they just store nothing.
     const bool live = tok < T;
     const float* row = logits + (live ? tok : 0) * E;
     const int nv = (E + G - 1) / G;
 
+    // Every load is unconditional, from a clamped in-bounds address (a key
+    // past E reads element 0 of the row and is then dropped): a guarded load
+    // becomes a branch with a full wait for memory inside it, so the loads
+    // would go out one round trip at a time instead of all together.
     float v[kMaxNv];
     uint64_t key[kMaxNv];
     if constexpr (VEC) {                 // E % 4 == 0: a vector is all inside or all past E
+        float4 f[kMaxNv / 4];
+#pragma unroll
+        for (int i = 0; i < kMaxNv; i += 4) {
+            const int e0 = slot_expert<G, true>(i, g);
+            f[i / 4] = *reinterpret_cast<const float4*>(row + (e0 < E ? e0 : 0));
+        }
 #pragma unroll
         for (int i = 0; i < kMaxNv; i += 4) {
             const int e0 = slot_expert<G, true>(i, g);
             const bool ok = live && e0 < E;
-            const float4 f = ok ? *reinterpret_cast<const float4*>(row + e0)
-                                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            v[i] = f.x;
-            v[i + 1] = f.y;
-            v[i + 2] = f.z;
-            v[i + 3] = f.w;
+            v[i] = f[i / 4].x;
+            v[i + 1] = f[i / 4].y;
+            v[i + 2] = f[i / 4].z;
+            v[i + 3] = f[i / 4].w;
 #pragma unroll
             for (int c = 0; c < 4; ++c)
                 key[i + c] = ok ? (uint64_t(order_bits(v[i + c])) << 32) |
@@ -131,8 +139,12 @@ __global__ __launch_bounds__(kBlock) void route_topk_kernel(
 #pragma unroll
         for (int i = 0; i < kMaxNv; ++i) {
             const int e = slot_expert<G, false>(i, g);
+            v[i] = row[i < nv && e < E ? e : 0];
+        }
+#pragma unroll
+        for (int i = 0; i < kMaxNv; ++i) {
+            const int e = slot_expert<G, false>(i, g);
             const bool ok = live && i < nv && e < E;
-            v[i] = ok ? row[e] : 0.0f;
             key[i] = ok ? (uint64_t(order_bits(v[i])) << 32) | uint32_t(~uint32_t(e)) : 0;
         }
     }
