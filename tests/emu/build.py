@@ -6,6 +6,8 @@ Test infrastructure only.  It lets the CPU test suite run the real kernel code
 -- the fused persistent mode included -- against the CPU oracle, with a limited
 number of co-resident workgroups."""
 import concurrent.futures as cf
+import fcntl
+import glob
 import os
 import shutil
 import subprocess
@@ -25,11 +27,29 @@ def compiler():
     return None
 
 
+def _inputs():
+    return (glob.glob(os.path.join(CSRC, "*")) + glob.glob(os.path.join(ROOT, "include", "*.h")) +
+            glob.glob(os.path.join(HERE, "fake", "**", "*"), recursive=True) +
+            [os.path.join(HERE, "emu_runtime.cpp"), os.path.abspath(__file__)])
+
+
 def build(extra=()):
+    """Builds the library unless it is newer than every input (and no extra
+    flags are asked for).  Concurrent callers -- parallel test workers --
+    take turns on a lock file, so none links another's half-written objects."""
     cxx = compiler()
     if cxx is None:
         raise RuntimeError("clang++ not found")
     os.makedirs(OUT, exist_ok=True)
+    with open(os.path.join(OUT, ".lock"), "w") as lock:
+        fcntl.flock(lock, fcntl.LOCK_EX)
+        if not extra and os.path.exists(LIB) and \
+                os.path.getmtime(LIB) >= max(os.path.getmtime(f) for f in _inputs()):
+            return LIB
+        return _build(cxx, extra)
+
+
+def _build(cxx, extra):
     flags = ["-std=c++17", "-O1", "-g", "-fPIC",
              "-I", os.path.join(HERE, "fake"), "-I", os.path.join(ROOT, "include"), *extra]
     jobs = [(os.path.join(CSRC, f), os.path.join(OUT, f + ".o"), True)

@@ -349,8 +349,11 @@ def test_emulated_slices_and_window_copy(emu, seed):
 BATCHED = [
     # T, H, E, R, k, grid, seed: one full batch, then a partial one
     (300, 512, 64, 8, 8, 2, 1101),      # k = 8 path: 300 items, 224 per batch
-    (97, 1024, 32, 4, 6, 1, 1102),      # runtime-k path: 194 items, 112 per batch
-    (40, 1536, 16, 4, 3, 1, 1103),      # 120 items: one full batch and 8 more
+    (97, 1024, 32, 4, 6, 1, 1102),      # k = 6 path: 194 items, 112 per batch
+    (40, 1536, 16, 4, 3, 1, 1103),      # runtime k: 120 items, one full batch and 8 more
+    (150, 1024, 32, 8, 4, 1, 1104),     # k = 4 path: 300 items
+    (130, 512, 16, 4, 2, 1, 1105),      # k = 2 path: 130 items
+    (60, 1024, 32, 4, 5, 1, 1106),      # runtime k: 5 picks, one group of 4 and one of 1
 ]
 
 

@@ -283,8 +283,11 @@ def test_concurrent_host_threads_on_separate_streams(epm):
 BATCHED = [
     # T, H, E, R, k, seed
     (5000, 1536, 64, 8, 8, 41),      # a single partial batch
-    (4096, 4096, 64, 16, 6, 42),     # runtime-k path: one full batch and a partial one
+    (4096, 4096, 64, 16, 6, 42),     # k = 6 (compile-time): one full batch and a partial one
     (20000, 1024, 256, 32, 8, 43),   # one full batch and a partial one
+    (8192, 2048, 64, 8, 4, 44),      # k = 4 (compile-time)
+    (9000, 4096, 32, 8, 2, 45),      # k = 2 (compile-time)
+    (5000, 2048, 64, 8, 5, 46),      # runtime-k path (picks loaded in groups of 4)
 ]
 
 
