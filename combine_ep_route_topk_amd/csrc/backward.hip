@@ -296,12 +296,19 @@ hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* y,
 {
     const int nvec = H / 8;
     const uint32_t grid = uint32_t(T) < kMaxGrid ? uint32_t(T) : kMaxGrid;
-    if (k == 8)
-        EP_LAUNCH((combine_grad_dot_kernel<8>), dim3(grid), dim3(kBlock), 0, s, grad_out, y,
-                  pos, T, nvec, k, grad_w);
-    else
-        EP_LAUNCH((combine_grad_dot_kernel<0>), dim3(grid), dim3(kBlock), 0, s, grad_out, y,
-                  pos, T, nvec, k, grad_w);
+    // The common top-k values get a compile-time pick count, so each lane's
+    // row loads of all picks are in flight together; any other k goes pick
+    // by pick.
+#define EP_DOT(KC) EP_LAUNCH((combine_grad_dot_kernel<KC>), dim3(grid), dim3(kBlock), 0, s, \
+                             grad_out, y, pos, T, nvec, k, grad_w)
+    switch (k) {
+        case 8: EP_DOT(8); break;
+        case 6: EP_DOT(6); break;
+        case 4: EP_DOT(4); break;
+        case 2: EP_DOT(2); break;
+        default: EP_DOT(0); break;
+    }
+#undef EP_DOT
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // Three quarters of the CU count: the per-element multiply and tie check

@@ -207,6 +207,9 @@ BACKWARD_SHAPES = [
     (40, 7176, 64, 8, 8, 22),     # ragged last segment, k = 8 path
     (33, 520, 16, 4, 3, 23),      # runtime-k path
     (7, 8, 4, 2, 1, 24),          # one vector per row
+    (30, 1032, 16, 4, 4, 25),     # k = 4 path, ragged last segment
+    (24, 512, 16, 4, 6, 26),      # k = 6 path
+    (20, 520, 16, 4, 5, 27),      # runtime-k path, 5 picks
 ]
 
 

@@ -87,7 +87,9 @@ BACKWARD_EDGE = [
     # T, H, E, R, k, seed
     (1, 8, 1, 1, 1, 301),           # one token, one vector per row
     (3, 16, 4, 2, 2, 302),
-    (130, 7176, 64, 8, 6, 303),     # ragged last segment, runtime-k path
+    (130, 7176, 64, 8, 6, 303),     # ragged last segment, k = 6 path
+    (500, 2048, 32, 8, 4, 308),     # k = 4 path
+    (200, 1032, 32, 4, 5, 309),     # runtime-k path, ragged last segment
     (257, 520, 16, 4, 8, 304),      # k = 8 path, ragged segment, odd token count
     (64, 4096, 64, 64, 64, 305),    # the largest k
     (1000, 64, 256, 32, 8, 306),    # short rows, many tokens
