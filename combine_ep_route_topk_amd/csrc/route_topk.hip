@@ -18,9 +18,10 @@
 // id.  Each of the k rounds takes every lane's largest untaken key and a
 // group-wide maximum through DPP row moves (quad permutes, half-row and row
 // mirrors: VALU instructions, no LDS round trip), a 16-lane swizzle for G=32
-// and a lane-0/lane-32 read for G=64.  The owner zeroes the winning key; lane
-// j keeps pick j.  The softmax sum uses the same pattern: every lane adds the
-// same pairs of operands, so all lanes hold bit-identical sums.
+// and a lane-0/lane-32 read for G=64.  A key is untaken when it lies below
+// the previous round's pick (keys are unique); lane j keeps pick j.  The
+// softmax sum uses the same pattern: every lane adds the same pairs of
+// operands, so all lanes hold bit-identical sums.
 #include "ep_device.h"
 #include "ep_internal.h"
 
@@ -149,14 +150,15 @@ __global__ __launch_bounds__(kBlock) void route_topk_kernel(
         }
     }
 
-    uint64_t my_key = 0, top_key = 0;
+    // Keys are unique (each carries its expert id), so round j's pick is the
+    // largest key below round j-1's pick: no key is modified between rounds.
+    uint64_t my_key = 0, top_key = 0, prev = ~uint64_t(0);
     for (int j = 0; j < k; ++j) {
         uint64_t best = 0;
 #pragma unroll
-        for (int i = 0; i < kMaxNv; ++i) best = key[i] > best ? key[i] : best;
+        for (int i = 0; i < kMaxNv; ++i) best = key[i] < prev && key[i] > best ? key[i] : best;
         best = group_max<G>(best);
-#pragma unroll
-        for (int i = 0; i < kMaxNv; ++i) key[i] = key[i] == best ? 0 : key[i];
+        prev = best;
         if (j == 0) top_key = best;
         if (g == j) my_key = best;
     }
