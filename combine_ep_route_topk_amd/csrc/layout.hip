@@ -174,6 +174,10 @@ __global__ __launch_bounds__(kBlock) void layout_pos_kernel(
 // are split contiguously, kExpPerThread per thread, so the scan over experts
 // is a thread-local run plus one block-wide scan.
 constexpr int kExpPerThread = kMaxE / kBlock;    // 4
+// Counters per expert per load round.  32 (one round at T*k <= 32768) was
+// slower on MI355X: scanpos 5.6 -> 5.9 us at T=4096, 11.9 -> 13.1 us at
+// T=16384 (k=8, E=256).
+constexpr int kTilesPerRound = 16;
 static_assert(kExpPerThread * kBlock == kMaxE, "expert split");
 __device__ __forceinline__ void scanpos_tile(
     int tile, const int32_t* __restrict__ topk_idx, int64_t S, int E, int R, int nTiles,
@@ -212,20 +216,21 @@ __device__ __forceinline__ void scanpos_tile(
     }
 
     // per expert: its total over all tiles and its count before this tile.
-    // Each round issues all its loads (kExpPerThread experts x 4 vectors of 4
-    // counters) before adding any: the counters come from L2, and a loop of
-    // dependent load-add steps would pay one L2 latency per step.
+    // Each round issues all its loads (kExpPerThread experts x kTilesPerRound
+    // counters, as 16-byte vectors) before adding any: the counters come from
+    // L2, and a loop of dependent load-add steps would pay one L2 latency per
+    // step.
     int tot[kExpPerThread], pre[kExpPerThread];
 #pragma unroll
     for (int q = 0; q < kExpPerThread; ++q) tot[q] = pre[q] = 0;
     const int e0 = tid * kExpPerThread;
     if (nTiles % 4 == 0) {                      // rows are 16-byte aligned
-        for (int t0 = 0; t0 < nTiles; t0 += 16) {
-            int4 c[kExpPerThread][4];
+        for (int t0 = 0; t0 < nTiles; t0 += kTilesPerRound) {
+            int4 c[kExpPerThread][kTilesPerRound / 4];
 #pragma unroll
             for (int q = 0; q < kExpPerThread; ++q)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
+                for (int m = 0; m < kTilesPerRound / 4; ++m) {
                     const int t = t0 + 4 * m;
                     const bool in = e0 + q < E && t < nTiles;
                     const int4 x =
@@ -236,7 +241,7 @@ __device__ __forceinline__ void scanpos_tile(
 #pragma unroll
             for (int q = 0; q < kExpPerThread; ++q)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
+                for (int m = 0; m < kTilesPerRound / 4; ++m) {
                     const int t = t0 + 4 * m;
                     tot[q] += c[q][m].x + c[q][m].y + c[q][m].z + c[q][m].w;
                     pre[q] += (t < tile ? c[q][m].x : 0) + (t + 1 < tile ? c[q][m].y : 0) +
