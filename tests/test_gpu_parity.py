@@ -367,6 +367,31 @@ def test_route_unaligned_logits_take_the_scalar_path(epm):
         check_route_weights(w.cpu().numpy(), o_w, logits, o_idx, bool(norm), E)
 
 
+def test_route_ties_pick_the_lowest_expert(epm):
+    """Logits drawn from five values (-0.0 and +0.0 among them) tie in every
+    row; row 0 holds one value throughout and row 1 alternates -0.0 and
+    +0.0.  Equal logits go to the lowest expert id and -0.0 ranks equal to
+    +0.0, so every pick is unique and equals the oracle's, on the vector and
+    scalar load paths and at group sizes G = 8, 16, 32 and 64."""
+    vals = np.array([-1.0, -0.0, 0.0, 0.5, 1.0], np.float32)
+    for T, E, k, norm in ((1000, 256, 8, 1), (500, 128, 8, 0), (300, 64, 6, 1), (200, 33, 5, 1),
+                          (100, 512, 8, 1), (100, 1024, 4, 0)):
+        rng = np.random.default_rng(T * E + k)
+        logits = vals[rng.integers(0, len(vals), (T, E))]
+        logits[0, :] = np.float32(0.25)
+        logits[1, :] = np.float32(-0.0)
+        logits[1, ::2] = np.float32(0.0)
+        say(f"route with ties T={T} E={E} k={k} normalize={norm}")
+        idx, w = epm.ep_route_topk(torch.from_numpy(logits).to(DEV), k, bool(norm))
+        torch.cuda.synchronize()
+        o_idx, o_w = oracle.route_topk(logits, k, norm)
+        got = idx.cpu().numpy()
+        np.testing.assert_array_equal(got, o_idx)
+        np.testing.assert_array_equal(got[0], np.arange(k))
+        np.testing.assert_array_equal(got[1], np.arange(k))
+        check_route_weights(w.cpu().numpy(), o_w, logits, o_idx, bool(norm), E)
+
+
 def test_maximum_slot_count(epm):
     """T*k just under the 2^30 limit (T = 134,000,000 tokens, k = 8, E = 16,
     H = 8): the layout's separate look-back scan over ~4,000 blocks, and every
