@@ -136,35 +136,58 @@ __device__ __forceinline__ void dots_fixed_k(const char* __restrict__ g_row,
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
         const float d = wave_sum_f(dot[j]);
-        if (lane_id() == 0) sh[wave][j] = d;
+        // a pick outside [0, S) gets exactly 0, even where grad_out holds an
+        // infinity (whose product with the zero row would be NaN)
+        if (lane_id() == 0) sh[wave][j] = uint32_t(p[j]) < S ? d : 0.0f;
     }
 }
 
-// One token, runtime k: pick by pick, each over all of the wave's segments
-// (the grad_out row is re-read from cache per pick).  Per lane the dot of a
-// pick sums the same products in the same order as dots_fixed_k.
+// One token, runtime k: picks in groups of kDotGroup, each group over all of
+// the wave's segments, its row loads issued together (the grad_out row is
+// re-read from cache per group).  Per lane the dot of a pick sums the same
+// products in the same order as dots_fixed_k; a pick outside [0, S) adds
+// nothing and gets 0.
+constexpr int kDotGroup = 4;
+
 __device__ __noinline__ void dots_any_k(const char* __restrict__ g_row,
                                         const char* __restrict__ yb,
                                         const int32_t* __restrict__ prow, int k, uint32_t S,
                                         int nvec, int64_t row_bytes, int wave,
                                         float (*sh)[kMaxK])
 {
+    const u32x4 zero = {0, 0, 0, 0};
     const int segs = (nvec + kWave - 1) / kWave;
-    for (int j = 0; j < k; ++j) {
-        const int32_t p = prow[j];
-        const bool valid = uint32_t(p) < S;
-        float dot = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += kDotGroup) {
+        int32_t p[kDotGroup];
+        bool valid[kDotGroup];
+        float dot[kDotGroup];
+#pragma unroll
+        for (int q = 0; q < kDotGroup; ++q) {
+            p[q] = j0 + q < k ? prow[j0 + q] : -1;
+            valid[q] = uint32_t(p[q]) < S;
+            dot[q] = 0.0f;
+        }
         for (int seg = wave; seg < segs; seg += kWavesPerBlock) {
             const int v = seg * kWave + lane_id();
-            if (v < nvec && valid) {
-                const int64_t off = int64_t(v) * 16;
-                float g[8];
-                unpack8(load16(g_row + off), g);
-                dot = dot8(g, load16_nt(yb + int64_t(p) * row_bytes + off), dot);
-            }
+            const bool lane_ok = v < nvec;
+            const int64_t off = int64_t(v) * 16;
+            float g[8];
+            unpack8(lane_ok ? load16(g_row + off) : zero, g);
+            u32x4 r[kDotGroup];
+#pragma unroll
+            for (int q = 0; q < kDotGroup; ++q)
+                r[q] = (lane_ok && valid[q]) ? load16_nt(yb + int64_t(p[q]) * row_bytes + off)
+                                             : zero;
+#pragma unroll
+            for (int q = 0; q < kDotGroup; ++q)
+                if (valid[q] && lane_ok) dot[q] = dot8(g, r[q], dot[q]);
         }
-        dot = wave_sum_f(dot);
-        if (lane_id() == 0) sh[wave][j] = dot;
+#pragma unroll
+        for (int q = 0; q < kDotGroup; ++q) {
+            if (j0 + q >= k) break;
+            const float d = wave_sum_f(dot[q]);
+            if (lane_id() == 0) sh[wave][j0 + q] = valid[q] ? d : 0.0f;
+        }
     }
 }
 

@@ -103,6 +103,38 @@ def test_backward_edge_shapes(epm, T, H, E, R, k, seed):
     run_and_check(epm, pos, w, g, y, f"T={T} H={H} E={E} R={R} k={k} seed={seed}")
 
 
+@pytest.mark.parametrize("k", [4, 5])
+def test_backward_grad_w_outside_the_buffer_is_zero_with_infinite_grad(epm, k):
+    """grad_w of a pick outside [0, T*k) is exactly 0 even when grad_out
+    holds an infinity (0 times infinity would be NaN), on the compile-time
+    (k = 4) and runtime (k = 5) pick paths; the other picks' grad_w equal a
+    dot product with no invalid row in it, so they do not depend on the
+    invalid picks."""
+    T, H, E, R = 40, 1024, 16, 4
+    pos, w, g, y = backward_inputs(T, H, E, R, k, 321 + k)
+    g = g.copy()
+    g[:, 5] = 0x7F80                      # +inf (bf16) in every token's row
+    pos_bad = pos.copy()
+    bad = [(2, 0), (9, k - 1), (30, 2)]
+    for t, j in bad:
+        pos_bad[t, j] = -1
+    say(f"backward, invalid pos with an infinite grad_out, T={T} H={H} k={k}")
+    gw = torch.zeros((T, k), dtype=torch.float32, device=DEV)
+    gy = torch.empty((T * k, H), dtype=torch.bfloat16, device=DEV)
+    epm.ep_combine_grad(to_dev_bits(g), to_dev_bits(y), torch.from_numpy(pos_bad).to(DEV),
+                        torch.from_numpy(w).to(DEV), grad_y=gy, grad_w=gw)
+    torch.cuda.synchronize()
+    gw_np = gw.cpu().numpy()
+    for t, j in bad:
+        assert gw_np[t, j] == 0.0 and not np.signbit(gw_np[t, j])
+    _, r_gw = oracle.combine_grad(g, y, pos, w)
+    mask = np.ones((T, k), bool)
+    for t, j in bad:
+        mask[t, j] = False
+    np.testing.assert_array_equal(np.isnan(gw_np[mask]), np.isnan(r_gw[mask]))
+    np.testing.assert_array_equal(np.isinf(gw_np[mask]), np.isinf(r_gw[mask]))
+
+
 def test_backward_skips_rows_outside_the_buffer(epm):
     """A pos entry outside [0, T*k): grad_w = 0, no grad_y row written, and no
     contribution to grad_x."""
