@@ -294,12 +294,16 @@ hipError_t launch_u(const uint16_t* y, const int32_t* pos, const float* w, int T
     const uint32_t segs = uint32_t((nvec + kWave * U - 1) / (kWave * U));
     const uint32_t items = uint32_t((T + kWavesPerBlock - 1) / kWavesPerBlock) * segs;
     const uint32_t grid = items < kMaxGrid ? items : kMaxGrid;
-    if (k == 8)
-        EP_LAUNCH((combine_kernel<U, 8, UW>), dim3(grid), dim3(kBlock), 0, s,
-                  y, pos, w, T, nvec, k, out, segs, items);
-    else
-        EP_LAUNCH((combine_kernel<U, 0, UW>), dim3(grid), dim3(kBlock), 0, s,
-                  y, pos, w, T, nvec, k, out, segs, items);
+#define EP_ITEMS(KC) EP_LAUNCH((combine_kernel<U, KC, UW>), dim3(grid), dim3(kBlock), 0, s, \
+                               y, pos, w, T, nvec, k, out, segs, items)
+    switch (k) {
+        case 8: EP_ITEMS(8); break;
+        case 6: EP_ITEMS(6); break;
+        case 4: EP_ITEMS(4); break;
+        case 2: EP_ITEMS(2); break;
+        default: EP_ITEMS(0); break;
+    }
+#undef EP_ITEMS
     return hipGetLastError();
 }
 
