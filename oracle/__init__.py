@@ -39,10 +39,12 @@ def lib():
         L.ep_oracle_dispatch_layout.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, P]
         L.ep_oracle_dispatch.argtypes = [P, i64, i32, i32, P, P]
         L.ep_oracle_combine.argtypes = [P, P, P, i64, i32, i32, P]
+        L.ep_oracle_combine_exact.argtypes = [P, P, P, i64, i32, i32, P]
         L.ep_oracle_combine_tokens.argtypes = [P, P, P, i64, i32, i32, P, i64, P]
         L.ep_oracle_fused_trailer.argtypes = [ctypes.c_uint64, P, i64, P]
         L.ep_oracle_combine_grad.argtypes = [P, P, P, P, i64, i32, i32, P, P]
         L.ep_oracle_dispatch_grad.argtypes = [P, P, i64, i32, i32, P]
+        L.ep_oracle_dispatch_grad_exact.argtypes = [P, P, i64, i32, i32, P]
         L.ep_oracle_slices.argtypes = [P, i32, i32, P, P, P]
         L.ep_oracle_lpt.argtypes = [P, P, i32, P, i32, i32, P, P, P]
         L.ep_oracle_rank_coalesce.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, P]
@@ -52,7 +54,8 @@ def lib():
         L.ep_oracle_incast_degree.argtypes = [P, i32]
         L.ep_oracle_incast_degree.restype = i32
         for f in ("ep_oracle_route_topk", "ep_oracle_dispatch_layout",
-                  "ep_oracle_dispatch", "ep_oracle_combine",
+                  "ep_oracle_dispatch", "ep_oracle_combine", "ep_oracle_combine_exact",
+                  "ep_oracle_dispatch_grad_exact",
                   "ep_oracle_combine_tokens", "ep_oracle_fused_trailer",
                   "ep_oracle_combine_grad", "ep_oracle_dispatch_grad", "ep_oracle_slices",
                   "ep_oracle_lpt"):
@@ -124,21 +127,32 @@ def dispatch(x_bits, pos, out=None):
     return send
 
 
-def combine(y_bits, pos, topk_w):
-    """y u16 [T*k][H] (send order), pos i32 [T][k], w f32 [T][k] -> out u16 [T][H]."""
+def _combine(fn, y_bits, pos, topk_w):
     y_bits = _c(y_bits, np.uint16)
     pos = _c(pos, np.int32)
     topk_w = _c(topk_w, np.float32)
     T, k = pos.shape
     H = y_bits.shape[1]
     out = np.empty((T, H), np.uint16)
-    _check(lib().ep_oracle_combine(_p(y_bits), _p(pos), _p(topk_w), T, H, k, _p(out)),
-           "combine")
+    _check(getattr(lib(), fn)(_p(y_bits), _p(pos), _p(topk_w), T, H, k, _p(out)), fn)
     return out
 
 
+def combine(y_bits, pos, topk_w):
+    """The combine contract: fp32 product for pick 0, fmaf for picks 1..k-1 in
+    order, one RNE to bf16.  y u16 [T*k][H] (send order), pos i32 [T][k],
+    w f32 [T][k] -> out u16 [T][H]."""
+    return _combine("ep_oracle_combine", y_bits, pos, topk_w)
+
+
+def combine_exact(y_bits, pos, topk_w):
+    """The accuracy reference: the exact weighted sum (in double, every
+    product exact) rounded once to bf16.  Same arguments as combine."""
+    return _combine("ep_oracle_combine_exact", y_bits, pos, topk_w)
+
+
 def combine_tokens(y_bits, pos, topk_w, tokens):
-    """Combine for the listed tokens only -> u16 [len(tokens)][H]."""
+    """combine (the fp32 chain) for the listed tokens only -> u16 [len(tokens)][H]."""
     y_bits = _c(y_bits, np.uint16)
     pos = _c(pos, np.int32)
     topk_w = _c(topk_w, np.float32)
@@ -168,17 +182,25 @@ def combine_grad(grad_out_bits, y_bits, pos, topk_w):
     return grad_y, grad_w
 
 
-def dispatch_grad(grad_send_bits, pos):
-    """Backward of dispatch: grad_send u16 [T*k][H], pos i32 [T][k] -> grad_x
-    u16 [T][H]."""
+def _dispatch_grad(fn, grad_send_bits, pos):
     grad_send_bits = _c(grad_send_bits, np.uint16)
     pos = _c(pos, np.int32)
     T, k = pos.shape
     H = grad_send_bits.shape[1]
     grad_x = np.empty((T, H), np.uint16)
-    _check(lib().ep_oracle_dispatch_grad(_p(grad_send_bits), _p(pos), T, H, k, _p(grad_x)),
-           "dispatch_grad")
+    _check(getattr(lib(), fn)(_p(grad_send_bits), _p(pos), T, H, k, _p(grad_x)), fn)
     return grad_x
+
+
+def dispatch_grad(grad_send_bits, pos):
+    """Backward of dispatch, fp32 sum in pick order then one RNE:
+    grad_send u16 [T*k][H], pos i32 [T][k] -> grad_x u16 [T][H]."""
+    return _dispatch_grad("ep_oracle_dispatch_grad", grad_send_bits, pos)
+
+
+def dispatch_grad_exact(grad_send_bits, pos):
+    """The accuracy reference for dispatch_grad: the sum in double, one RNE."""
+    return _dispatch_grad("ep_oracle_dispatch_grad_exact", grad_send_bits, pos)
 
 
 def slices(expert_offsets, P: int):

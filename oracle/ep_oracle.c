@@ -211,11 +211,46 @@ int ep_oracle_dispatch(const uint16_t* x, int64_t T, int32_t H, int32_t k,
 /* Combine: HyperParallel-MoE sec. 4.1 -- the top-k expert contributions are */
 /* accumulated according to the routing scores; RailWave "System Design" --  */
 /* combine uses the dispatch metadata to put outputs back at their original  */
-/* token positions.  Sum in double (w*y is exact there), one rounding to bf16.*/
+/* token positions.                                                          */
+/*                                                                           */
+/* The value the library computes (the contract): fp32 accumulation in the  */
+/* fixed top-k order j = 0..k-1.  acc = w0 * y0 as one fp32 product (one    */
+/* rounding), then acc = fmaf(wj, yj, acc) for j = 1..k-1 (one rounding     */
+/* each), then one round-to-nearest-even to bf16.  This file is built with  */
+/* -ffp-contract=off, so the product of pick 0 is never fused into the next */
+/* step, and fmaf is C99's correctly rounded fused multiply-add.            */
+/*                                                                           */
+/* The exact value (the accuracy reference): the same sum in double, where  */
+/* every product w*y of an fp32 weight and a bf16 value is exact, rounded   */
+/* once to bf16.                                                            */
 /* ------------------------------------------------------------------------ */
+
+/* A bf16 pattern is the upper half of the binary32 pattern of the same
+ * value, so widening is exact. */
+static float bf16_to_float(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
 
 static void combine_one(const uint16_t* y, const int32_t* pos, const float* topk_w,
                         int64_t t, int32_t H, int32_t k, uint16_t* out_row)
+{
+    const int32_t* p = pos + t * (int64_t)k;
+    const float* w = topk_w + t * (int64_t)k;
+    for (int32_t h = 0; h < H; ++h) {
+        float acc = w[0] * bf16_to_float(y[(int64_t)p[0] * H + h]);
+        for (int32_t j = 1; j < k; ++j)
+            acc = fmaf(w[j], bf16_to_float(y[(int64_t)p[j] * H + h]), acc);
+        /* float -> double is exact, so this is one rounding to bf16. */
+        out_row[h] = ep_oracle_double_to_bf16((double)acc);
+    }
+}
+
+static void combine_exact_one(const uint16_t* y, const int32_t* pos, const float* topk_w,
+                              int64_t t, int32_t H, int32_t k, uint16_t* out_row)
 {
     const int32_t* p = pos + t * (int64_t)k;
     const float* w = topk_w + t * (int64_t)k;
@@ -242,6 +277,16 @@ int ep_oracle_combine(const uint16_t* y, const int32_t* pos, const float* topk_w
     if (check_pos(pos, T, k)) return -4;
     for (int64_t t = 0; t < T; ++t)
         combine_one(y, pos, topk_w, t, H, k, out + t * (int64_t)H);
+    return 0;
+}
+
+int ep_oracle_combine_exact(const uint16_t* y, const int32_t* pos, const float* topk_w,
+                            int64_t T, int32_t H, int32_t k, uint16_t* out)
+{
+    if (!y || !pos || !topk_w || !out || T < 0 || H < 1 || k < 1) return -1;
+    if (check_pos(pos, T, k)) return -4;
+    for (int64_t t = 0; t < T; ++t)
+        combine_exact_one(y, pos, topk_w, t, H, k, out + t * (int64_t)H);
     return 0;
 }
 
@@ -323,7 +368,26 @@ int ep_oracle_dispatch_grad(const uint16_t* grad_send, const int32_t* pos,
     for (int64_t t = 0; t < T; ++t) {
         for (int32_t h = 0; h < H; ++h) {
             /* x[t] was copied to every row pos[t][j]: its gradient is the sum
-             * of those rows' gradients, in double, rounded once. */
+             * of those rows' gradients, accumulated in fp32 in pick order
+             * (one rounding per addition), then rounded once to bf16. */
+            float acc = bf16_to_float(grad_send[(int64_t)pos[t * k] * H + h]);
+            for (int32_t j = 1; j < k; ++j)
+                acc = acc + bf16_to_float(grad_send[(int64_t)pos[t * k + j] * H + h]);
+            grad_x[t * (int64_t)H + h] = ep_oracle_double_to_bf16((double)acc);
+        }
+    }
+    return 0;
+}
+
+int ep_oracle_dispatch_grad_exact(const uint16_t* grad_send, const int32_t* pos,
+                                  int64_t T, int32_t H, int32_t k, uint16_t* grad_x)
+{
+    if (!grad_send || !pos || !grad_x || T < 0 || H < 1 || k < 1) return -1;
+    if (check_pos(pos, T, k) != 0) return -4;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t h = 0; h < H; ++h) {
+            /* The same sum in double, rounded once to bf16: the accuracy
+             * reference for the fp32 sum above. */
             double acc = 0.0;
             for (int32_t j = 0; j < k; ++j) {
                 const int64_t p = pos[t * k + j];

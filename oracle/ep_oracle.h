@@ -43,10 +43,14 @@
  *   - send buffer order: expert-major (hence rank-major); inside one expert,
  *     ascending flattened slot index s = t*k + j (stable).
  *   - one row per (token, pick): S = T*k rows.
- *   - combine value = sum_j w[t][j] * y[pos[t][j]] evaluated in double
- *     (each product w*y is exact in double), rounded once to bf16 RNE.
- *   - backward: activation gradients are bf16 like the activations, each
- *     element rounded once (RNE) from its exact or double value; the
+ *   - combine value = fp32 accumulation in the fixed top-k order: the fp32
+ *     product w0*y0, then fmaf(wj, yj, acc) for j = 1..k-1, then one
+ *     round-to-nearest-even to bf16.  The exact value (the sum in double,
+ *     where each product w*y is exact, rounded once) is kept beside it as
+ *     the accuracy reference.
+ *   - backward: activation gradients are bf16 like the activations.  grad_y
+ *     is the exact product w*g rounded once (RNE); grad_x is the sum of the
+ *     k gradient rows in fp32 in pick order, rounded once; the
  *     routing-weight gradient is a double dot product over H.
  *
  * Conventions: bf16 values travel as uint16_t bit patterns.  Every function
@@ -87,13 +91,22 @@ int ep_oracle_dispatch_layout(const int32_t* topk_idx, int64_t T, int32_t k,
 int ep_oracle_dispatch(const uint16_t* x, int64_t T, int32_t H, int32_t k,
                        const int32_t* pos, uint16_t* send);
 
-/* Combine [HPMOE sec. 4.1; RAIL "System Design"]:
- * out[t][h] = bf16( sum_j w[t][j] * y[pos[t][j]][h] ).
- * y bf16 [T*k][H] in send order; out bf16 [T][H]. */
+/* Combine [HPMOE sec. 4.1; RAIL "System Design"]: for each (t, h),
+ *   acc = w[t][0] * y[pos[t][0]][h]                 one fp32 rounding;
+ *   acc = fmaf(w[t][j], y[pos[t][j]][h], acc)       j = 1..k-1, in order;
+ *   out[t][h] = bf16_rne(acc).
+ * y bf16 [T*k][H] in send order; out bf16 [T][H].  NaN comes out as the
+ * quiet NaN 0x7FC0 with its sign; fp32 overflow gives +-inf. */
 int ep_oracle_combine(const uint16_t* y, const int32_t* pos, const float* topk_w,
                       int64_t T, int32_t H, int32_t k, uint16_t* out);
 
-/* Same as ep_oracle_combine for a chosen list of tokens only: out_rows is
+/* The accuracy reference for combine: out[t][h] = bf16_rne( sum_j w[t][j] *
+ * y[pos[t][j]][h] ), the sum taken in double (every product exact) and
+ * rounded once. */
+int ep_oracle_combine_exact(const uint16_t* y, const int32_t* pos, const float* topk_w,
+                            int64_t T, int32_t H, int32_t k, uint16_t* out);
+
+/* Same as ep_oracle_combine (the fp32 chain) for a chosen list of tokens only: out_rows is
  * [n_tokens][H], row i holds token tokens[i].  Used for sampled checks at
  * full size. */
 int ep_oracle_combine_tokens(const uint16_t* y, const int32_t* pos,
@@ -117,10 +130,17 @@ int ep_oracle_combine_grad(const uint16_t* grad_out, const uint16_t* y,
 /* Backward of dispatch [HPMOE sec. 2.2, Fig. 2(b): the backward Combine
  * returns the gradient of the input activations].  send[pos[t][j]] = x[t]
  * for every j, so
- *   grad_x[t][h] = bf16( sum_j grad_send[pos[t][j]][h] )  in double, one RNE.
+ *   grad_x[t][h] = bf16_rne( sum_j grad_send[pos[t][j]][h] ),
+ * the sum accumulated in fp32 in pick order j = 0..k-1 (the combine's
+ * arithmetic with unit weights: each addition rounds once).
  * grad_send bf16 [T*k][H]; grad_x bf16 [T][H]. */
 int ep_oracle_dispatch_grad(const uint16_t* grad_send, const int32_t* pos,
                             int64_t T, int32_t H, int32_t k, uint16_t* grad_x);
+
+/* The accuracy reference for dispatch_grad: the same sum in double, rounded
+ * once to bf16. */
+int ep_oracle_dispatch_grad_exact(const uint16_t* grad_send, const int32_t* pos,
+                                  int64_t T, int32_t H, int32_t k, uint16_t* grad_x);
 
 /* Equal contiguous slices of the S = expert_offsets[E] send-buffer slots
  * for P workers [UBEP sec. 3.3, "Token-level Load Partition" and Algorithm 1

@@ -205,7 +205,9 @@ def test_dispatch_grad_of_dispatch_is_k_times_x(k):
 
 
 def test_dispatch_grad_is_a_unit_weight_combine():
-    # both round the same double sum once (generic values, k = 8)
+    # both accumulate the same fp32 sum in pick order (1 * y is exact, so each
+    # fused multiply-add of the combine is one rounded addition); generic
+    # values, k = 8
     T, H, E, R, k = 40, 56, 32, 8, 8
     pos, _ = layout(T, E, R, k, 141)
     G_bits = wl.make_rows(T * k, H, 142)

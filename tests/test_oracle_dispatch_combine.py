@@ -1,6 +1,8 @@
-"""Pins of the oracle's dispatch copy, combine reduction and bf16 rounding.
+"""Pins of the oracle's dispatch copy, exact combine reduction and bf16 rounding.
 
-Pinned against hand-derived bit patterns, exact rational arithmetic
+combine_exact (the one rounding of the exact weighted sum, the accuracy
+reference for the fp32 combine chain pinned in test_oracle_combine_chain.py)
+is pinned against hand-derived bit patterns, exact rational arithmetic
 (fractions.Fraction) for the weighted sum and its round-to-nearest-even,
 an independent bit-level f32 -> bf16 rounding, and the identities of the
 method: a weight-1 top-1 combine is a gather, one-hot weights select a row,
@@ -92,8 +94,8 @@ def test_golden_combine_cases():
     with open(os.path.join(GOLDEN, "combine_small.json")) as f:
         g = json.load(f)
     for c in g["cases"]:
-        out = oracle.combine(np.array(c["y"], np.uint16), np.array(c["pos"], np.int32),
-                             np.array(c["w"], np.float32))
+        out = oracle.combine_exact(np.array(c["y"], np.uint16), np.array(c["pos"], np.int32),
+                                   np.array(c["w"], np.float32))
         assert out.reshape(-1).tolist() == c["out"], c["why"]
 
 
@@ -103,7 +105,7 @@ def test_combine_vs_exact_rationals():
     y = wl.make_rows(T * k, H, seed=9)
     pos = rng.permutation(T * k).astype(np.int32).reshape(T, k)
     w = (rng.random((T, k), dtype=np.float32) - np.float32(0.3))
-    out = oracle.combine(y, pos, w)
+    out = oracle.combine_exact(y, pos, w)
     for t in range(T):
         for h in range(H):
             exact = sum(Fraction(float(w[t, j])) * bf16_exact(int(y[pos[t, j], h]))
@@ -115,7 +117,7 @@ def test_combine_top1_weight1_is_gather():
     T, H = 32, 40
     y = wl.make_rows(T, H, seed=12)
     pos = np.random.default_rng(1).permutation(T).astype(np.int32).reshape(T, 1)
-    out = oracle.combine(y, pos, np.ones((T, 1), np.float32))
+    out = oracle.combine_exact(y, pos, np.ones((T, 1), np.float32))
     np.testing.assert_array_equal(out, y[pos[:, 0]])
 
 
@@ -126,7 +128,7 @@ def test_combine_one_hot_selects_row():
     for hot in range(k):
         w = np.zeros((T, k), np.float32)
         w[:, hot] = 1
-        np.testing.assert_array_equal(oracle.combine(y, pos, w), y[pos[:, hot]])
+        np.testing.assert_array_equal(oracle.combine_exact(y, pos, w), y[pos[:, hot]])
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode"])
@@ -136,7 +138,7 @@ def test_round_trip_identity_experts(name):
     idx, wt = oracle.route_topk(inp["logits"], w.k, 1)
     lay = oracle.dispatch_layout(idx, w.E, w.R)
     send = oracle.dispatch(inp["x"], lay["pos"])
-    out = oracle.combine(send, lay["pos"], wt)
+    out = oracle.combine_exact(send, lay["pos"], wt)
     np.testing.assert_array_equal(out, inp["x"])
 
 
