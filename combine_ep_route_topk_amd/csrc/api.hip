@@ -96,7 +96,7 @@ extern "C" {
 
 int ep_abi_version(void) { return EP_ABI_VERSION; }
 
-const char* ep_status_string(int status) {
+const char* ep_status_string(ep_status status) {
     switch (status) {
         case EP_OK: return "EP_OK";
         case EP_ERR_INVALID_ARG: return "EP_ERR_INVALID_ARG";
@@ -267,8 +267,8 @@ ep_status ep_fused_dispatch_combine_sync(const uint16_t* x, const int32_t* topk_
                                          int32_t* expert_offsets, int32_t* rank_counts,
                                          int32_t* rank_offsets, int32_t* pos,
                                          uint8_t* send_rows, uint16_t* out, void* workspace,
-                                         size_t workspace_bytes, uint64_t* epoch_out,
-                                         uint32_t spin_limit, int32_t sync, void* stream)
+                                         size_t workspace_bytes, uint32_t spin_limit,
+                                         int32_t sync, void* stream)
 {
     const char* fn = "ep_fused_dispatch_combine";
     TimingScope timing_scope;
@@ -294,23 +294,10 @@ ep_status ep_fused_dispatch_combine_sync(const uint16_t* x, const int32_t* topk_
     if (workspace_bytes < need)
         return fail(EP_ERR_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", fn,
                     workspace_bytes, need);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (epoch_out) {
-        // The epoch this call will write is the one the workspace holds once
-        // the work queued before it has finished.
-        uint64_t e = 0;
-        hipError_t he = hipStreamSynchronize(s);
-        if (he == hipSuccess)
-            he = hipMemcpy(&e, static_cast<char*>(workspace) + offsetof(ep::WsHeader, epoch),
-                           sizeof(e), hipMemcpyDeviceToHost);
-        if (he != hipSuccess)
-            return fail(EP_ERR_LAUNCH, "%s: reading the epoch failed: %s", fn,
-                        hipGetErrorString(he));
-        *epoch_out = e;
-    }
     return launched(ep::launch_fused(x, topk_idx, topk_w, T, H, k, E, R, expert_counts,
                                      expert_offsets, rank_counts, rank_offsets, pos, send_rows,
-                                     out, workspace, spin_limit, 0, sync, s),
+                                     out, workspace, spin_limit, 0, sync,
+                                     static_cast<hipStream_t>(stream)),
                     fn);
 }
 
@@ -320,12 +307,30 @@ ep_status ep_fused_dispatch_combine(const uint16_t* x, const int32_t* topk_idx,
                                     int32_t* expert_offsets, int32_t* rank_counts,
                                     int32_t* rank_offsets, int32_t* pos, uint8_t* send_rows,
                                     uint16_t* out, void* workspace, size_t workspace_bytes,
-                                    uint64_t* epoch_out, uint32_t spin_limit, void* stream)
+                                    void* stream)
 {
     return ep_fused_dispatch_combine_sync(x, topk_idx, topk_w, T, H, k, E, R, expert_counts,
                                           expert_offsets, rank_counts, rank_offsets, pos,
-                                          send_rows, out, workspace, workspace_bytes, epoch_out,
-                                          spin_limit, ep::kSyncItemEvents, stream);
+                                          send_rows, out, workspace, workspace_bytes, 0,
+                                          ep::kSyncItemEvents, stream);
+}
+
+ep_status ep_fused_last_epoch(const void* workspace, uint64_t* epoch, void* stream)
+{
+    const char* fn = "ep_fused_last_epoch";
+    EP_REQUIRE_PTR(fn, workspace, 256);
+    if (!epoch) return fail(EP_ERR_INVALID_ARG, "%s: epoch is NULL", fn);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    ep::WsHeader h{};
+    hipError_t e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipMemcpy(&h, workspace, sizeof(h), hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return fail(EP_ERR_LAUNCH, "%s: reading the workspace failed: %s", fn,
+                    hipGetErrorString(e));
+    if (h.magic != ep::kFusedMagic)
+        return fail(EP_ERR_WORKSPACE, "%s: not a fused workspace (ep_fused_workspace_init)", fn);
+    *epoch = h.last_epoch;
+    return ok();
 }
 
 ep_status ep_expert_slices(const int32_t* expert_offsets, int32_t E, int32_t P, int64_t* start,

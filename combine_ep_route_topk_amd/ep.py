@@ -34,7 +34,7 @@ _sz = ctypes.c_size_t
 
 _SIGS = {
     "ep_abi_version": ([], ctypes.c_int),
-    "ep_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "ep_status_string": ([ctypes.c_int], ctypes.c_char_p),   # ep_status is an int-sized enum
     "ep_last_error": ([], ctypes.c_char_p),
     "ep_route_topk": ([_P, _i32, _i32, _i32, _i32, _P, _P, _P], ctypes.c_int),
     "ep_dispatch_layout_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
@@ -48,12 +48,11 @@ _SIGS = {
     "ep_fused_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
     "ep_fused_workspace_init": ([_P, _sz, _P], ctypes.c_int),
     "ep_fused_dispatch_combine": ([_P, _P, _P, _i32, _i32, _i32, _i32, _i32, _P, _P, _P, _P,
-                                   _P, _P, _P, _P, _sz, ctypes.POINTER(ctypes.c_uint64), _u32,
-                                   _P], ctypes.c_int),
+                                   _P, _P, _P, _P, _sz, _P], ctypes.c_int),
     "ep_fused_dispatch_combine_sync": ([_P, _P, _P, _i32, _i32, _i32, _i32, _i32, _P, _P, _P,
-                                        _P, _P, _P, _P, _P, _sz,
-                                        ctypes.POINTER(ctypes.c_uint64), _u32, _i32, _P],
+                                        _P, _P, _P, _P, _P, _sz, _u32, _i32, _P],
                                        ctypes.c_int),
+    "ep_fused_last_epoch": ([_P, ctypes.POINTER(ctypes.c_uint64), _P], ctypes.c_int),
     "ep_expert_slices": ([_P, _i32, _i32, _P, _P, _P, _P], ctypes.c_int),
     "ep_rank_coalesce_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
     "ep_rank_coalesce": ([_P, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P, _P, _P, _sz, _P],
@@ -305,8 +304,8 @@ def ep_fused_dispatch_combine(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: t
                               want_epoch: bool = False, stream=None,
                               sync: int = EP_FUSED_SYNC_ITEM_EVENTS) -> dict:
     """Layout + dispatch + combine (identity experts) in one persistent launch.
-    Returns the dict of outputs; with want_epoch the call also reads back the
-    epoch written into the trailers (key 'epoch').  `sync` picks how combine
+    Returns the dict of outputs; with want_epoch the call then synchronises
+    and reads back the epoch written into the trailers (key 'epoch').  `sync` picks how combine
     waits for the rows (EP_FUSED_SYNC_*)."""
     _bits_ok(x, "x")
     T, H = x.shape
@@ -315,16 +314,32 @@ def ep_fused_dispatch_combine(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: t
     _need(topk_w, "topk_w", torch.float32, (T, k))
     if out is None:
         out = fused_outputs(T, H, k, E, R, x.device)
-    ep = ctypes.c_uint64(0)
-    _check(_lib.ep_fused_dispatch_combine_sync(
-        _ptr(x), _ptr(topk_idx), _ptr(topk_w), T, H, k, E, R, _ptr(out["expert_counts"]),
-        _ptr(out["expert_offsets"]), _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]),
-        _ptr(out["pos"]), _ptr(out["send_rows"]), _ptr(out["out"]), _ptr(out["workspace"]),
-        out["workspace"].numel(), ctypes.byref(ep) if want_epoch else None, int(spin_limit),
-        int(sync), _P(_stream(stream, x.device))))
+    st = _stream(stream, x.device)
+    if sync == EP_FUSED_SYNC_ITEM_EVENTS and not spin_limit:
+        _check(_lib.ep_fused_dispatch_combine(
+            _ptr(x), _ptr(topk_idx), _ptr(topk_w), T, H, k, E, R, _ptr(out["expert_counts"]),
+            _ptr(out["expert_offsets"]), _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]),
+            _ptr(out["pos"]), _ptr(out["send_rows"]), _ptr(out["out"]),
+            _ptr(out["workspace"]), out["workspace"].numel(), _P(st)))
+    else:
+        _check(_lib.ep_fused_dispatch_combine_sync(
+            _ptr(x), _ptr(topk_idx), _ptr(topk_w), T, H, k, E, R, _ptr(out["expert_counts"]),
+            _ptr(out["expert_offsets"]), _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]),
+            _ptr(out["pos"]), _ptr(out["send_rows"]), _ptr(out["out"]),
+            _ptr(out["workspace"]), out["workspace"].numel(), int(spin_limit), int(sync),
+            _P(st)))
     if want_epoch:
-        out["epoch"] = int(ep.value)
+        out["epoch"] = ep_fused_last_epoch(out["workspace"], stream)
     return out
+
+
+def ep_fused_last_epoch(workspace: torch.Tensor, stream=None) -> int:
+    """The epoch the last completed fused call on this workspace wrote into
+    its trailers; synchronises the stream first."""
+    e = ctypes.c_uint64(0)
+    _check(_lib.ep_fused_last_epoch(_ptr(workspace), ctypes.byref(e),
+                                    _P(_stream(stream, workspace.device))))
+    return int(e.value)
 
 
 # ------------------------------------------------------------------- partition

@@ -59,8 +59,9 @@ typedef enum {
 /* Returns EP_ABI_VERSION of the built library. */
 int ep_abi_version(void);
 
-/* Static, human-readable name of a status code. */
-const char* ep_status_string(int status);
+/* Static, human-readable name of a status code ("EP_ERR_UNKNOWN" for a value
+ * outside the enum). */
+const char* ep_status_string(ep_status s);
 
 /* Detail of the last non-OK status returned on the calling thread (static
  * thread-local storage; valid until the next call on that thread). */
@@ -292,11 +293,11 @@ ep_status ep_window_copy(const void* src, void* dst, int64_t row_bytes, int64_t 
  *              calls in stream order (it carries the epoch and counters from
  *              call to call).  Two calls that share a workspace must not run
  *              concurrently.
- *   epoch_out  host pointer (may be NULL): receives the epoch this call writes
- *              into the trailers.
- *   spin_limit bound on every device-side wait, in polling rounds; 0 picks
- *              the default.  An expired wait sets the workspace error word
- *              (ep_get_device_error() -> EP_ERR_TIMEOUT) and the kernel drains.
+ * Every device-side wait is bounded (2^20 polling rounds); an expired wait sets
+ * the workspace error word (ep_get_device_error() -> EP_ERR_TIMEOUT) and the
+ * kernel drains.  ep_fused_dispatch_combine_sync takes the bound and the
+ * readiness mode as arguments; ep_fused_last_epoch reads back the epoch of
+ * the last completed call.
  * ------------------------------------------------------------------------- */
 size_t    ep_fused_row_stride_bytes(int32_t H);
 size_t    ep_fused_workspace_bytes(int32_t T, int32_t k, int32_t E, int32_t R);
@@ -309,8 +310,15 @@ ep_status ep_fused_dispatch_combine(const uint16_t* x, const int32_t* topk_idx,
                                     int32_t* rank_counts, int32_t* rank_offsets,
                                     int32_t* pos, uint8_t* send_rows, uint16_t* out,
                                     void* workspace, size_t workspace_bytes,
-                                    uint64_t* epoch_out, uint32_t spin_limit,
                                     void* stream);
+
+/* The epoch that the last completed fused call on `workspace` wrote into its
+ * trailers and flags (0 before the first call).  Synchronises `stream` first,
+ * like ep_get_device_error, so it is a host-side read: not for use while a
+ * stream is being captured into a graph.  Errors: EP_ERR_INVALID_ARG (NULL or
+ * misaligned workspace, NULL epoch), EP_ERR_WORKSPACE (not initialised by
+ * ep_fused_workspace_init), EP_ERR_LAUNCH (the read failed). */
+ep_status ep_fused_last_epoch(const void* workspace, uint64_t* epoch, void* stream);
 
 /* ---------------------------------------------------------------------------
  * The fused mode with a choice of how each combine item learns that its send
@@ -324,6 +332,10 @@ ep_status ep_fused_dispatch_combine(const uint16_t* x, const int32_t* topk_idx,
  * 16-byte store is the largest whose visibility the readers rely on, so in
  * every mode the data is made visible before its readiness word (stores with
  * the agent-coherence bit, then a wait for their completion).
+ *   spin_limit  bound on every device-side wait, in polling rounds; 0 picks
+ *               the default (2^20).  An expired wait sets the workspace error
+ *               word (ep_get_device_error() -> EP_ERR_TIMEOUT) and the kernel
+ *               drains.
  *   sync = EP_FUSED_SYNC_ITEM_EVENTS (0): ep_fused_dispatch_combine's mode.
  *          Combine waits for the event words of the scatter items of its
  *          tokens, reads pos, then checks each row's trailer.
@@ -369,8 +381,8 @@ ep_status ep_fused_dispatch_combine_sync(const uint16_t* x, const int32_t* topk_
                                          int32_t* expert_offsets, int32_t* rank_counts,
                                          int32_t* rank_offsets, int32_t* pos,
                                          uint8_t* send_rows, uint16_t* out, void* workspace,
-                                         size_t workspace_bytes, uint64_t* epoch_out,
-                                         uint32_t spin_limit, int32_t sync, void* stream);
+                                         size_t workspace_bytes, uint32_t spin_limit,
+                                         int32_t sync, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Rank-level token coalescing of the send records [RAIL sec. 3.1-3.2: the

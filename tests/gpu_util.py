@@ -1,5 +1,7 @@
 """Helpers shared by the GPU parity tests: host<->device transfers of bf16 bit
-patterns, the oracle reference chain, and the tolerances (derived below)."""
+patterns, the oracle reference chain, the bit-equality check of combine-type
+outputs, and the tolerances that remain (route weights and the weight
+gradient, derived below)."""
 import numpy as np
 import torch
 
@@ -47,45 +49,44 @@ def check_route_weights(w_gpu, w_ref, logits, idx, normalize, E):
                            f"worst rel err {np.max(err / np.abs(w_ref)):.3g}")
 
 
-# Combine.  The kernel accumulates in f32: a product, then k-1 fused
-# multiply-adds, i.e. k roundings, so |acc32 - S| <= g_k * sum_j |w_j y_j| with
-# g_k = k u / (1 - k u), u = 2^-24 (recursive-summation bound).  Both results
-# are then rounded to bf16 (half an ulp each), so
-#   |gpu - ref| <= ulp_bf16(max(|gpu|, |ref|)) + g_k * sum_j |w_j y_j|.
-# Where g_k * sum|w y| stays below a quarter ulp (no cancellation), this is
-# the 1-ulp contract: max relative error 2^-7 = 7.8e-3 < 8e-3.
-def bf16_ulp(a: np.ndarray) -> np.ndarray:
-    a = np.abs(a)
-    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
-    return 2.0 ** (np.maximum(e, -126) - 7)
+# Combine.  The contract is the oracle's fp32 chain (HyperParallel-MoE sec.
+# 4.1, read as fp32 accumulation in the fixed top-k order): acc = w0*y0 in
+# fp32, then fmaf(wj, yj, acc) for j = 1..k-1, then one RNE to bf16.  Every
+# GPU path computes exactly that, so the bar is bit equality.  A NaN output
+# compares as NaN: which quiet-NaN pattern an operation yields is left open
+# by IEEE 754 and is not part of the contract.
+def nan_bits(b: np.ndarray) -> np.ndarray:
+    return ((b & 0x7F80) == 0x7F80) & ((b & 0x007F) != 0)
 
 
-def check_combine(out_gpu_bits, ref_bits, y_bits, pos, w, chunk=256):
-    T, k = pos.shape
-    gam = k * 2.0 ** -24 / (1 - k * 2.0 ** -24)
-    g = wl.bf16_bits_to_f32(out_gpu_bits).astype(np.float64)
-    r = wl.bf16_bits_to_f32(ref_bits).astype(np.float64)
-    n_exact = 0
-    worst = 0.0
-    for t0 in range(0, T, chunk):
-        t1 = min(T, t0 + chunk)
-        Y = wl.bf16_bits_to_f32(y_bits[pos[t0:t1].reshape(-1)]).astype(np.float64)
-        Y = Y.reshape(t1 - t0, k, -1)
-        mag = np.einsum("tk,tkh->th", np.abs(w[t0:t1].astype(np.float64)), np.abs(Y))
-        gg, rr = g[t0:t1], r[t0:t1]
-        ulp = bf16_ulp(np.maximum(np.abs(gg), np.abs(rr)))
-        err = np.abs(gg - rr)
-        bad = err > ulp + gam * mag
-        assert not bad.any(), f"{bad.sum()} combine outputs outside the derived bound"
-        clean = gam * mag <= 0.25 * bf16_ulp(rr)
-        within_one = err[clean] <= bf16_ulp(rr[clean]) * 1.0000001
-        assert within_one.all(), "1-ulp contract broken where no cancellation occurs"
-        big = clean & (np.abs(rr) > 0)
-        if big.any():
-            worst = max(worst, float(np.max(err[big] / np.abs(rr[big]))))
-        n_exact += int(np.sum(out_gpu_bits[t0:t1] == ref_bits[t0:t1]))
-    assert worst <= 8e-3, worst
-    return n_exact / out_gpu_bits.size
+def assert_same_bits(got: np.ndarray, ref: np.ndarray, what: str) -> None:
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    bad = (got != ref) & ~(nan_bits(got) & nan_bits(ref))
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outputs differ from the "
+                             f"oracle's fp32 chain; first at {i}: got {int(got[i]):#06x}, "
+                             f"oracle {int(ref[i]):#06x}")
+
+
+def _ordered(b: np.ndarray) -> np.ndarray:
+    """bf16 patterns -> integers in the order of their values (+-0 -> 0), so a
+    difference of two is their distance in ulps."""
+    mag = (b & 0x7FFF).astype(np.int64)
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def accuracy_vs_exact(got: np.ndarray, exact: np.ndarray, what: str) -> dict:
+    """Informational, not a bar: how far the fp32 chain lands from one
+    rounding of the exact sum.  Reports the bit-identical fraction, how many
+    outputs are more than 1 bf16 ulp away, and the largest distance."""
+    ok = ~(nan_bits(got) | nan_bits(exact))
+    d = np.abs(_ordered(got[ok]) - _ordered(exact[ok]))
+    rep = dict(identical=float(np.mean(d == 0)) if d.size else 1.0,
+               over_1ulp=int(np.sum(d > 1)), max_ulp=int(d.max()) if d.size else 0)
+    say(f"{what}: {rep['identical']:.6f} of outputs identical to the exact sum; "
+        f"{rep['over_1ulp']} more than 1 ulp away (largest {rep['max_ulp']} ulp)")
+    return rep
 
 
 # Weight gradient of the backward combine.  grad_w[t][j] is a dot product of

@@ -130,16 +130,21 @@ def test_fused_validation(ep):
     f = P(FAKE)
     need = lib.ep_fused_workspace_bytes(64, 2, 8, 2)
     rc, _ = call(lib, "ep_fused_dispatch_combine", f, f, f, 64, 16, 2, 8, 2, f, f, f, f, f,
-                 P(FAKE + 16), f, f, need, None, 0, None)
+                 P(FAKE + 16), f, f, need, None)
     assert rc == ep.EP_ERR_INVALID_ARG            # send_rows not 128-byte aligned
     rc, _ = call(lib, "ep_fused_dispatch_combine", f, f, f, 64, 16, 2, 8, 2, f, f, f, f, f,
-                 f, f, f, need - 256, None, 0, None)
+                 f, f, f, need - 256, None)
     assert rc == ep.EP_ERR_WORKSPACE
+    e = ctypes.c_uint64(0)
+    rc, _ = call(lib, "ep_fused_last_epoch", None, ctypes.byref(e), None)
+    assert rc == ep.EP_ERR_INVALID_ARG
+    rc, _ = call(lib, "ep_fused_last_epoch", f, None, None)
+    assert rc == ep.EP_ERR_INVALID_ARG
     rc, _ = call(lib, "ep_fused_workspace_init", f, 16, None)
     assert rc == ep.EP_ERR_WORKSPACE
     for bad in (-1, 5):
         rc, msg = call(lib, "ep_fused_dispatch_combine_sync", f, f, f, 64, 16, 2, 8, 2, f, f, f,
-                       f, f, f, f, f, need, None, 0, bad, None)
+                       f, f, f, f, f, need, 0, bad, None)
         assert rc == ep.EP_ERR_INVALID_ARG and "sync" in msg
 
 

@@ -12,6 +12,7 @@ onto a wave.  The unfused kernels run too, as a check of the emulation itself
 against the results the GPU gives.
 """
 import ctypes
+import json
 import os
 
 import numpy as np
@@ -101,9 +102,10 @@ class Emu:
             p(xa), p(np.ascontiguousarray(idx)), p(np.ascontiguousarray(wt)), self.T, self.H,
             self.k, self.E, self.R, p(lay["expert_counts"]), p(lay["expert_offsets"]),
             p(lay["rank_counts"]), p(lay["rank_offsets"]), p(lay["pos"]), p(self.rows),
-            p(self.out), p(self.ws), ctypes.c_size_t(self.ws.size), ctypes.byref(e),
+            p(self.out), p(self.ws), ctypes.c_size_t(self.ws.size),
             ctypes.c_uint32(spin_limit), ctypes.c_int32(sync), None)
         self.check(rc)
+        self.check(L.ep_fused_last_epoch(p(self.ws), ctypes.byref(e), None))
         return e.value, L.ep_get_device_error(p(self.ws), None)
 
 
@@ -238,7 +240,7 @@ def test_emulated_backward_matches_oracle(emu, T, H, E, R, k, seed):
     gx = aligned(T * H * 2, 16).view(np.uint16).reshape(T, H)
     rc = emu.ep_dispatch_grad(p(y), p(pos), T, H, k, p(gx), None)
     assert rc == 0, emu.ep_last_error().decode()
-    gu.check_combine(gx, oracle.dispatch_grad(y, pos), y, pos, np.ones((T, k), np.float32))
+    gu.assert_same_bits(gx, oracle.dispatch_grad(y, pos), "dispatch_grad")
 
 
 SYNC_NAMES = {0: "item events", 1: "row flags", 2: "checksum", 3: "sentinel", 4: "chunk flags"}
@@ -396,16 +398,14 @@ def test_emulated_batched_combine(emu, T, H, E, R, k, grid, seed):
     """The batched combine (a batch's outputs held back and stored together)
     on a tiny grid, so full and partial batches both run: the same bits as
     the one-item-per-wave kernel, weighted and with unit weights (the backward
-    of dispatch), and the oracle's bits but for rare differences (the oracle
-    sums in f64, the kernels chain f32 fused multiply-adds; the GPU tests
-    hold the one-item-per-wave kernel to the derived error bound)."""
+    of dispatch), and both the oracle's fp32 chain bit for bit."""
     y, pos, w = batched_inputs(T, H, E, R, k, seed)
     out = batched(emu, y, pos, w, T, H, k, grid)
     assert np.array_equal(out, unbatched(emu, y, pos, w, T, H, k))
-    assert np.mean(out == oracle.combine(y, pos, w)) > 0.99
+    assert np.array_equal(out, oracle.combine(y, pos, w))
     out1 = batched(emu, y, pos, None, T, H, k, grid)
     assert np.array_equal(out1, unbatched(emu, y, pos, None, T, H, k))
-    assert np.mean(out1 == oracle.dispatch_grad(y, pos)) > 0.99
+    assert np.array_equal(out1, oracle.dispatch_grad(y, pos))
 
 
 def test_emulated_batched_combine_skips_picks_outside(emu):
@@ -559,3 +559,30 @@ def test_emulated_expand_records_reports_overflow_and_stray_bits(emu):
     bad[2] |= np.uint64(1 << 3)                             # no local expert 3
     _, _, status = expand_emu(emu, rows, bad, 3, 9)
     assert status != 0
+
+
+def _chain_cases():
+    with open(os.path.join(os.path.dirname(__file__), "golden", "combine_chain.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _chain_cases(), ids=lambda c: c["name"])
+def test_emulated_combine_golden_chain_cases(emu, case):
+    """The hand-derived fp32-chain cases through the kernels' own source, on
+    both combine kernels: each case's values fill every column (H = 512) of
+    every token; the one-item-per-wave kernel and the batched one (one
+    workgroup) must give the hand-derived pattern everywhere."""
+    k, T0, H = case["k"], case["T"], 512
+    reps = 4
+    T = T0 * reps
+    y1 = np.array(case["y"], np.uint16)[:, 0]
+    y = aligned(T * k * H * 2, 16).view(np.uint16).reshape(T * k, H)
+    y[:] = np.tile(y1, reps)[:, None]
+    pos = np.ascontiguousarray(
+        (np.tile(np.array(case["pos"], np.int32), (reps, 1))
+         + (np.arange(reps)[:, None] * (T0 * k)).repeat(T0, 0)).astype(np.int32))
+    w = np.ascontiguousarray(np.tile(np.array(case["w_bits"], np.uint32).view(np.float32),
+                                     (reps, 1)))
+    want = np.repeat(np.tile(np.array(case["out"], np.uint16), reps)[:, None], H, axis=1)
+    assert np.array_equal(unbatched(emu, y, pos, w, T, H, k), want), case["why"]
+    assert np.array_equal(batched(emu, y, pos, w, T, H, k, 1), want), case["why"]

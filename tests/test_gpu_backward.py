@@ -7,8 +7,10 @@ Combine returns the input activations' gradient (ep_dispatch_grad).
 Bars: grad_y bit-exact (the exact product rounded once, also where the f32
 product sits on a bf16 tie -- planted in every other token); grad_w within the
 derived dot-product bound (gpu_util.check_grad_w) and the same bits on a second
-call; grad_x within the combine bound with unit weights.  Full workload sizes
-use the launch configuration the benchmark times.
+call; grad_x bit-exact against the oracle's fp32 sum in pick order (the
+combine chain with unit weights).  Full workload sizes use the launch
+configuration the benchmark times; the skewed incast workload is checked on a
+sample of tokens, the tokens with the most picks of hot experts among them.
 """
 import numpy as np
 import pytest
@@ -18,7 +20,8 @@ import oracle
 from combine_ep_route_topk_amd import workloads as wl
 from exact_bf16 import plant_tie_products
 
-from gpu_util import DEV, bits, check_combine, check_grad_w, poison_bits, say, to_dev_bits
+from gpu_util import (DEV, accuracy_vs_exact, assert_same_bits, bits, check_grad_w, poison_bits,
+                      say, to_dev_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +48,19 @@ def backward_inputs(T, H, E, R, k, seed, logits=None):
     return pos, w, g, y
 
 
-def run_and_check(epm, pos, w, g, y, label):
+def sub_problem(pos, w, g, y, tokens):
+    """The listed tokens as a problem of their own: their picks' rows of y,
+    in pick order, with pos = 0..n*k-1.  Every gradient the oracle forms is
+    per pick (grad_y, grad_w) or per token (grad_x), so the sub-problem's
+    gradients are the full problem's at those tokens."""
+    k = pos.shape[1]
+    rows = pos[tokens].reshape(-1)
+    return (np.arange(len(tokens) * k, dtype=np.int32).reshape(-1, k), w[tokens], g[tokens],
+            y[rows], rows)
+
+
+def run_and_check(epm, pos, w, g, y, label, sample=None):
+    """sample: check only these tokens against the oracle (all when None)."""
     T, k = pos.shape
     H = g.shape[1]
     say(f"combine_grad {label}")
@@ -57,9 +72,16 @@ def run_and_check(epm, pos, w, g, y, label):
     epm.ep_combine_grad(d_g, d_y, d_pos, d_w, grad_y=gy, grad_w=gw)
     torch.cuda.synchronize()
     gw1 = gw.cpu().numpy().copy()
-    r_gy, r_gw = oracle.combine_grad(g, y, pos, w)
-    assert np.array_equal(bits(gy), r_gy), "grad_y differs from the exact product"
-    check_grad_w(gw1, r_gw, g, y, pos)
+    if sample is None:
+        r_pos, r_w, r_g, r_y, rows, toks = pos, w, g, y, slice(None), slice(None)
+    else:
+        r_pos, r_w, r_g, r_y, rows = sub_problem(pos, w, g, y, sample)
+        toks = sample
+    r_gy, r_gw = oracle.combine_grad(r_g, r_y, r_pos, r_w)
+    # with a sample, row i*k+j of the sub-problem's grad_y is pick j of sampled
+    # token i, which the full problem holds at row pos[t][j] (= rows[i*k+j])
+    assert np.array_equal(bits(gy)[rows], r_gy), "grad_y differs from the exact product"
+    check_grad_w(gw1[toks], r_gw, r_g, r_y, r_pos)
     # a second call: the same bits (fixed summation order)
     epm.ep_combine_grad(d_g, d_y, d_pos, d_w, grad_y=gy, grad_w=gw)
     torch.cuda.synchronize()
@@ -70,9 +92,9 @@ def run_and_check(epm, pos, w, g, y, label):
     gx = poison_bits((T, H))
     epm.ep_dispatch_grad(d_y, d_pos, grad_x=gx)
     torch.cuda.synchronize()
-    frac = check_combine(bits(gx), oracle.dispatch_grad(y, pos), y, pos,
-                         np.ones((T, k), np.float32))
-    assert frac > 0.99
+    got = bits(gx)[toks]
+    assert_same_bits(got, oracle.dispatch_grad(r_y, r_pos), f"dispatch_grad {label}")
+    accuracy_vs_exact(got, oracle.dispatch_grad_exact(r_y, r_pos), f"dispatch_grad {label}")
 
 
 @pytest.mark.parametrize("name", ["tiny", "decode", "glm45air", "dsv3"])
@@ -81,6 +103,24 @@ def test_backward_workloads(epm, name):
     pos, w, g, y = backward_inputs(wk.T, wk.H, wk.E, wk.R, wk.k, wk.seed + 7,
                                    logits=wl.make_logits(wk))
     run_and_check(epm, pos, w, g, y, wk.describe())
+
+
+def test_backward_incast_sampled(epm):
+    """The skewed incast workload (10% of the experts take half of the picks)
+    with random expert outputs and signed weights, at full size on the GPU;
+    10,240 tokens checked against the oracle: the 5,120 with the most picks of
+    hot experts and 5,120 drawn at random from the rest."""
+    wk = wl.WORKLOADS["incast"]
+    logits = wl.make_logits(wk)
+    pos, w, g, y = backward_inputs(wk.T, wk.H, wk.E, wk.R, wk.k, wk.seed + 7, logits=logits)
+    w = w - np.float32(0.3)                # signed weights
+    idx, _ = oracle.route_topk(logits, wk.k, 1)
+    hot = np.sum(idx < wl.INCAST_HOT_EXPERTS, axis=1)
+    by_hot = np.argsort(-hot, kind="stable")
+    rest = np.random.default_rng(wk.seed + 9).permutation(by_hot[5120:])[:5120]
+    sample = np.sort(np.concatenate([by_hot[:5120], rest])).astype(np.int64)
+    assert hot[by_hot[:5120]].min() >= 4
+    run_and_check(epm, pos, w, g, y, wk.describe() + " (10,240 sampled tokens)", sample=sample)
 
 
 BACKWARD_EDGE = [
@@ -170,7 +210,7 @@ def test_backward_skips_rows_outside_the_buffer(epm):
     # expected grad_x: the lost picks' rows count as zero
     y0 = y.copy()
     y0[lost] = 0
-    check_combine(bits(gx), oracle.dispatch_grad(y0, pos), y0, pos, np.ones((T, k), np.float32))
+    assert_same_bits(bits(gx), oracle.dispatch_grad(y0, pos), "dispatch_grad with picks outside")
 
 
 def test_backward_validation(epm):

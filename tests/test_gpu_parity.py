@@ -1,11 +1,16 @@
 """GPU parity: every entry point of the C ABI against the CPU oracle, on the five
 seeded workloads at their full sizes and on edge cases.
 
-Bars: bit-exact for indices, counts, offsets, positions and dispatched
-payloads; route weights and combine within the bounds derived in gpu_util.
+Bars: bit-exact for indices, counts, offsets, positions, dispatched payloads
+and combined outputs (the oracle's fp32 chain: the product of pick 0, then a
+fused multiply-add per pick in order, then one RNE); route weights within the
+bound derived in gpu_util.
 Each kernel is fed the oracle's inputs for its stage, so a failure names the
 stage.  Calls go through the Python binding straight into the C ABI.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -13,8 +18,8 @@ import torch
 import oracle
 from combine_ep_route_topk_amd import workloads as wl
 
-from gpu_util import (DEV, Case, bits, check_combine, check_route_weights, poison_bits, say,
-                      to_dev_bits)
+from gpu_util import (DEV, Case, accuracy_vs_exact, assert_same_bits, bits, check_route_weights,
+                      poison_bits, say, to_dev_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -100,15 +105,15 @@ def test_combine_identity_experts(epm, name):
     torch.cuda.synchronize()
     got = bits(out)
     assert np.array_equal(got, c.x), "combine(dispatch(x)) != x"
-    if w.T * w.H <= 4096 * 7168:
-        ref = oracle.combine(c.send, c.lay["pos"], c.wt)
-        assert np.array_equal(got, ref)
+    assert_same_bits(got, oracle.combine(c.send, c.lay["pos"], c.wt), f"combine {name}")
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "glm45air", "dsv3"])
+@pytest.mark.parametrize("name", wl.ORDER)
 def test_combine_random_experts(epm, name):
-    """Distinct random expert outputs and signed weights: exercises the f32
-    accumulation (cancellation included) against the exact oracle."""
+    """Distinct random expert outputs and signed weights on every workload
+    (the skewed incast one included): the fp32 accumulation, cancellation
+    included, bit for bit against the oracle's chain; the distance to the
+    exact sum is reported."""
     w = wl.WORKLOADS[name]
     c = get_case(name)
     y = wl.make_rows(w.S, w.H, seed=w.seed + 77)
@@ -119,10 +124,41 @@ def test_combine_random_experts(epm, name):
                          torch.from_numpy(wt).to(DEV))
     torch.cuda.synchronize()
     got = bits(out)
-    ref = oracle.combine(y, c.lay["pos"], wt)
-    frac = check_combine(got, ref, y, c.lay["pos"], wt)
-    print(f"[gpu-test] {name}: {frac:.6f} of combine outputs bit-identical to the exact oracle")
-    assert frac > 0.99
+    del out
+    assert_same_bits(got, oracle.combine(y, c.lay["pos"], wt), f"combine {name}")
+    accuracy_vs_exact(got, oracle.combine_exact(y, c.lay["pos"], wt), f"combine {name}")
+
+
+def _golden_chain_cases():
+    with open(os.path.join(os.path.dirname(__file__), "golden", "combine_chain.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_chain_cases(), ids=lambda c: c["name"])
+def test_combine_golden_chain_cases(epm, case):
+    """The hand-derived fp32-chain cases (an fma that is not a multiply then an
+    add, rounding inside the chain, pick order, signed zeros, fp32 overflow,
+    subnormal products) on the GPU: each case's values fill every column of
+    every token, at a small shape (one item per wave) and at a large one (the
+    batched kernel), and every output must be the hand-derived pattern."""
+    k = case["k"]
+    for T, H in ((case["T"], 8), (16384 // k * case["T"], 4096)):
+        reps = T // case["T"]
+        y1 = np.array(case["y"], np.uint16)[:, 0]            # [T0*k]
+        pos1 = np.array(case["pos"], np.int32)               # [T0][k]
+        w1 = np.array(case["w_bits"], np.uint32).view(np.float32)
+        # repetition r uses rows r*T0*k .. : the same values at shifted slots
+        n1 = y1.shape[0]
+        y = np.repeat(np.tile(y1, reps)[:, None], H, axis=1)
+        pos = (np.tile(pos1, (reps, 1)) + (np.arange(reps)[:, None] * n1).repeat(case["T"], 0))
+        pos = pos.astype(np.int32)
+        wt = np.tile(w1, (reps, 1))
+        say(f"combine golden case {case['name']} T={T} H={H} k={k}")
+        out = epm.ep_combine(to_dev_bits(y), torch.from_numpy(pos).to(DEV),
+                             torch.from_numpy(wt).to(DEV))
+        torch.cuda.synchronize()
+        want = np.repeat(np.tile(np.array(case["out"], np.uint16), reps)[:, None], H, axis=1)
+        assert_same_bits(bits(out), want, f"golden {case['name']} T={T} H={H}")
 
 
 @pytest.mark.parametrize("name", wl.ORDER)
@@ -181,7 +217,7 @@ def test_edge_shapes(epm, T, H, E, R, k, seed):
         np.testing.assert_array_equal(lay[key].cpu().numpy(), o_lay[key], err_msg=key)
     assert np.array_equal(bits(send), o_send)
     assert np.array_equal(bits(out_rt), x)
-    check_combine(bits(out_y), oracle.combine(y, o_lay["pos"], o_w), y, o_lay["pos"], o_w)
+    assert_same_bits(bits(out_y), oracle.combine(y, o_lay["pos"], o_w), "combine")
 
 
 def test_layout_skewed_and_repeated_ids(epm):
@@ -303,9 +339,8 @@ def test_combine_batched_sizes(epm, T, H, E, R, k, seed):
     out = epm.ep_combine(d_y, d_pos, torch.from_numpy(wt).to(DEV))
     gx = epm.ep_dispatch_grad(d_y, d_pos)
     torch.cuda.synchronize()
-    assert check_combine(bits(out), oracle.combine(y, pos, wt), y, pos, wt) > 0.99
-    assert check_combine(bits(gx), oracle.dispatch_grad(y, pos), y, pos,
-                         np.ones((T, k), np.float32)) > 0.99
+    assert_same_bits(bits(out), oracle.combine(y, pos, wt), "combine")
+    assert_same_bits(bits(gx), oracle.dispatch_grad(y, pos), "dispatch_grad")
 
 
 def test_combine_batched_skips_picks_outside(epm):
@@ -327,7 +362,7 @@ def test_combine_batched_skips_picks_outside(epm):
     torch.cuda.synchronize()
     y0 = y.copy()
     y0[lost] = 0
-    assert check_combine(bits(out), oracle.combine(y0, pos, o_w), y0, pos, o_w) > 0.99
+    assert_same_bits(bits(out), oracle.combine(y0, pos, o_w), "combine with picks outside")
 
 
 def test_dispatch_large_skips_picks_outside(epm):
