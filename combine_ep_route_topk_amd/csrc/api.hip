@@ -169,6 +169,42 @@ ep_status ep_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t k, int3
                     fn);
 }
 
+ep_status ep_dispatch_layout_noalloc(const int32_t* topk_idx, int32_t T, int32_t k, int32_t E,
+                                     int32_t R, int32_t* expert_counts, int32_t* expert_offsets,
+                                     int32_t* rank_counts, int32_t* rank_offsets, int32_t* pos,
+                                     int32_t* slot_src, void* stream)
+{
+    const char* fn = "ep_dispatch_layout_noalloc";
+    TimingScope timing_scope;
+    EP_TRY(check_routing_sizes(fn, T, k, E));
+    if (R < 1 || E % R != 0)
+        return fail(EP_ERR_INVALID_ARG, "%s: R=%d must be >= 1 and divide E=%d", fn, R, E);
+    EP_REQUIRE_PTR(fn, topk_idx, 4);
+    EP_REQUIRE_PTR(fn, expert_counts, 4);
+    EP_REQUIRE_PTR(fn, expert_offsets, 4);
+    EP_REQUIRE_PTR(fn, rank_counts, 4);
+    EP_REQUIRE_PTR(fn, rank_offsets, 4);
+    EP_REQUIRE_PTR(fn, pos, 4);
+    if (slot_src && !aligned(slot_src, 4))
+        return fail(EP_ERR_INVALID_ARG, "%s: slot_src is not 4-byte aligned", fn);
+    const size_t need = ep::layout_plan(T, k, E).bytes;
+    if (need > ep::kLayoutScratchBytes)
+        return fail(EP_ERR_UNSUPPORTED,
+                    "%s: T=%d k=%d E=%d needs %zu bytes of layout scratch; the library's static "
+                    "buffer holds %zu (use ep_dispatch_layout with a workspace)",
+                    fn, T, k, E, need, ep::kLayoutScratchBytes);
+    void* ws = nullptr;
+    const hipError_t e = ep::layout_scratch(&ws);
+    if (e != hipSuccess)
+        return fail(EP_ERR_DEVICE, "%s: the static scratch has no address on this device: %s",
+                    fn, hipGetErrorString(e));
+    return launched(ep::launch_dispatch_layout(topk_idx, T, k, E, R, expert_counts,
+                                               expert_offsets, rank_counts, rank_offsets,
+                                               pos, slot_src, ws,
+                                               static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 ep_status ep_dispatch(const uint16_t* x, int32_t T, int32_t H, int32_t k,
                       const int32_t* pos, uint16_t* send, void* stream)
 {

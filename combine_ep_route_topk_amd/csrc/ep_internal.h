@@ -193,6 +193,12 @@ hipError_t launch_dispatch_layout(const int32_t* topk_idx, int T, int k, int E, 
                                   int32_t* rank_counts, int32_t* rank_offsets,
                                   int32_t* pos, int32_t* slot_src, void* ws,
                                   hipStream_t s);
+// The layout workspace that the library itself holds, one per GPU, for the
+// entry point that allocates nothing: kLayoutScratchBytes bytes, 256-byte
+// aligned, kept until the process ends.  *ptr receives the current device's
+// copy (looked up once per device).
+constexpr size_t kLayoutScratchBytes = size_t(16) << 20;
+hipError_t layout_scratch(void** ptr);
 // The layout with a chosen expected slot total: the device error word reports
 // an id outside [0, E) only when expect >= 0 and fewer than `expect` slots
 // were counted.  expect = -1 lets slots with a negative id be skipped on

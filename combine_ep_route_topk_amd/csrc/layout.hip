@@ -35,6 +35,9 @@
 // which costs each workgroup a 32 KiB read at T=4096, k=8, E=256 and saves a
 // launch and the look-back (measured on MI355X: layout 14.3 -> ~10 us).
 // A layout of a single tile runs all of it in one workgroup and one launch.
+#include <atomic>
+#include <mutex>
+
 #include "ep_device.h"
 #include "ep_internal.h"
 #include "ep_layout_dev.h"
@@ -418,6 +421,37 @@ __global__ __launch_bounds__(kBlock) void layout_single_kernel(
 }
 
 }  // namespace
+
+// The workspace of ep_dispatch_layout_noalloc: a file-scope device array, so
+// no call allocates.  Each GPU the library runs on holds its own copy at its
+// own address; host code never passes this name to a kernel (on the host it
+// is only a stand-in for the symbol), it passes the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kLayoutScratchBytes];
+
+hipError_t layout_scratch(void** ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void*> addr[kMaxDevices];
+    static std::mutex lookup;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> hold(lookup);
+        p = addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 hipError_t launch_dispatch_layout(const int32_t* topk_idx, int T, int k, int E, int R,
                                   int32_t* expert_counts, int32_t* expert_offsets,

@@ -40,6 +40,8 @@ _SIGS = {
     "ep_dispatch_layout_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
     "ep_dispatch_layout": ([_P, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P, _P, _P, _sz, _P],
                            ctypes.c_int),
+    "ep_dispatch_layout_noalloc": ([_P, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P, _P, _P],
+                                   ctypes.c_int),
     "ep_dispatch": ([_P, _i32, _i32, _i32, _P, _P, _P], ctypes.c_int),
     "ep_combine": ([_P, _P, _P, _i32, _i32, _i32, _P, _P], ctypes.c_int),
     "ep_combine_grad": ([_P, _P, _P, _P, _i32, _i32, _i32, _P, _P, _P], ctypes.c_int),
@@ -186,6 +188,25 @@ def ep_dispatch_layout(topk_idx: torch.Tensor, E: int, R: int, out: dict | None 
         _ptr(topk_idx), T, k, E, R, _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
         _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]), _ptr(out["pos"]),
         _ptr(out.get("slot_src")), _ptr(ws), ws.numel(), _P(_stream(stream, dev))))
+    return out
+
+
+def ep_dispatch_layout_noalloc(topk_idx: torch.Tensor, E: int, R: int, out: dict,
+                               stream=None) -> dict:
+    """ep_dispatch_layout on the library's own static scratch (no workspace,
+    nothing allocated by the call): `out` holds the caller's output tensors
+    (layout_outputs' keys; 'workspace' is not used)."""
+    _need(topk_idx, "topk_idx", torch.int32)
+    T, k = topk_idx.shape
+    for name, shape in (("expert_counts", (E,)), ("expert_offsets", (E + 1,)),
+                        ("rank_counts", (R,)), ("rank_offsets", (R + 1,)), ("pos", (T, k))):
+        _need(out[name], name, torch.int32, shape)
+    if out.get("slot_src") is not None:
+        _need(out["slot_src"], "slot_src", torch.int32, (T * k,))
+    _check(_lib.ep_dispatch_layout_noalloc(
+        _ptr(topk_idx), T, k, E, R, _ptr(out["expert_counts"]), _ptr(out["expert_offsets"]),
+        _ptr(out["rank_counts"]), _ptr(out["rank_offsets"]), _ptr(out["pos"]),
+        _ptr(out.get("slot_src")), _P(_stream(stream, topk_idx.device))))
     return out
 
 

@@ -132,6 +132,31 @@ ep_status ep_dispatch_layout(const int32_t* topk_idx, int32_t T, int32_t k,
                              size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * ep_dispatch_layout_noalloc -- ep_dispatch_layout for callers that cannot
+ * allocate device memory: code under graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, outputs and kernels as
+ * ep_dispatch_layout, minus the workspace: the library keeps the workspace
+ * itself, in a static device array of 16 MiB per GPU (held until the process
+ * ends), so the call allocates nothing.
+ *   Size limit: ep_dispatch_layout_workspace_bytes(T, k, E, R) <= 16 MiB
+ *   (about T*k <= 4 million slots); a larger problem is refused with
+ *   EP_ERR_UNSUPPORTED before anything is enqueued.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (concurrent streams, or host threads) race and give undefined
+ *   outputs; calls in stream order are safe.  The array keeps the last call's
+ *   contents; the kernels reset whatever they need to start at zero.
+ *   An id outside [0, E) gets pos = -1 as in ep_dispatch_layout; this
+ *   variant's device error word is not readable by the caller.
+ * Errors: as ep_dispatch_layout, plus EP_ERR_UNSUPPORTED for the size limit
+ * and EP_ERR_DEVICE when the array has no address on the current device.
+ * ------------------------------------------------------------------------- */
+ep_status ep_dispatch_layout_noalloc(const int32_t* topk_idx, int32_t T, int32_t k,
+                                     int32_t E, int32_t R, int32_t* expert_counts,
+                                     int32_t* expert_offsets, int32_t* rank_counts,
+                                     int32_t* rank_offsets, int32_t* pos,
+                                     int32_t* slot_src, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Dispatch.  [UBEP sec. 2.1, sec. 2.3] each token's activation row goes to
  * every expert it picked, written straight into its final place in the
  * expert-contiguous send buffer (no staging copy).

@@ -16,6 +16,7 @@
 
 #define __global__
 #define __device__
+#define __align__(n) __attribute__((aligned(n)))
 #define __host__
 #define __forceinline__ inline
 #define __noinline__ __attribute__((noinline))
@@ -25,7 +26,8 @@
 
 typedef int hipError_t;
 typedef void* hipStream_t;
-enum { hipSuccess = 0, hipErrorInvalidValue = 1, hipErrorNotSupported = 801 };
+enum { hipSuccess = 0, hipErrorInvalidValue = 1, hipErrorInvalidDevice = 101,
+       hipErrorInvalidSymbol = 13, hipErrorNotSupported = 801 };
 struct alignas(16) int4 { int x, y, z, w; };
 inline int4 make_int4(int a, int b, int c, int d) { return int4{a, b, c, d}; }
 struct alignas(16) float4 { float x, y, z, w; };
@@ -176,6 +178,13 @@ inline emu_v4u32 emu_buffer_load_b128(emu_buffer_rsrc r, int off) {
 
 inline hipError_t hipGetLastError() { return hipSuccess; }
 inline hipError_t hipGetDevice(int* d) { *d = 0; return 0; }
+// A __device__ variable is an ordinary host object here, so its address is
+// the symbol's address.
+#define HIP_SYMBOL(x) (&(x))
+inline hipError_t hipGetSymbolAddress(void** p, const void* sym) {
+    *p = const_cast<void*>(sym);
+    return 0;
+}
 inline hipError_t hipOccupancyMaxActiveBlocksPerMultiprocessor(int* n, const void*, int, int) { *n = 2; return 0; }
 enum { hipDeviceAttributeMultiprocessorCount = 1 };
 inline hipError_t hipDeviceGetAttribute(int* v, int, int) { *v = 4; return 0; }
