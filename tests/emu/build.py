@@ -33,28 +33,32 @@ def _inputs():
             [os.path.join(HERE, "emu_runtime.cpp"), os.path.abspath(__file__)])
 
 
-def build(extra=()):
-    """Builds the library unless it is newer than every input (and no extra
-    flags are asked for).  Concurrent callers -- parallel test workers --
-    take turns on a lock file, so none links another's half-written objects."""
+def build(extra=(), variant=None):
+    """Builds the library unless it is newer than every input.  `variant`
+    names a separate build (its own objects and library file) compiled with
+    the `extra` flags -- the emulation's negative controls use this.
+    Concurrent callers -- parallel test workers -- take turns on a lock file,
+    so none links another's half-written objects."""
     cxx = compiler()
     if cxx is None:
         raise RuntimeError("clang++ not found")
-    os.makedirs(OUT, exist_ok=True)
+    out = OUT if variant is None else os.path.join(OUT, variant)
+    lib = LIB if variant is None else os.path.join(OUT, f"libep_emu_{variant}.so")
+    os.makedirs(out, exist_ok=True)
     with open(os.path.join(OUT, ".lock"), "w") as lock:
         fcntl.flock(lock, fcntl.LOCK_EX)
-        if not extra and os.path.exists(LIB) and \
-                os.path.getmtime(LIB) >= max(os.path.getmtime(f) for f in _inputs()):
-            return LIB
-        return _build(cxx, extra)
+        if os.path.exists(lib) and \
+                os.path.getmtime(lib) >= max(os.path.getmtime(f) for f in _inputs()):
+            return lib
+        return _build(cxx, extra, out, lib)
 
 
-def _build(cxx, extra):
+def _build(cxx, extra, out, lib):
     flags = ["-std=c++17", "-O1", "-g", "-fPIC",
              "-I", os.path.join(HERE, "fake"), "-I", os.path.join(ROOT, "include"), *extra]
-    jobs = [(os.path.join(CSRC, f), os.path.join(OUT, f + ".o"), True)
+    jobs = [(os.path.join(CSRC, f), os.path.join(out, f + ".o"), True)
             for f in sorted(os.listdir(CSRC)) if f.endswith(".hip")]
-    jobs.append((os.path.join(HERE, "emu_runtime.cpp"), os.path.join(OUT, "emu_runtime.o"), False))
+    jobs.append((os.path.join(HERE, "emu_runtime.cpp"), os.path.join(out, "emu_runtime.o"), False))
 
     def one(job):
         src, obj, as_cxx = job
@@ -66,9 +70,9 @@ def _build(cxx, extra):
 
     with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         objs = list(ex.map(one, jobs))
-    subprocess.run([cxx, "-shared", "-o", LIB + ".tmp", *objs, "-lpthread", *extra], check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    subprocess.run([cxx, "-shared", "-o", lib + ".tmp", *objs, "-lpthread", *extra], check=True)
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -46,8 +46,19 @@ extern long g_op_limit;
 
 enum OpKind { OP_NONE, OP_BALLOT, OP_SHFL, OP_READLANE, OP_READFIRST, OP_SYNC, OP_EXIT };
 
+// One store that a lane has issued and that has not completed yet (weak
+// memory mode): up to 16 bytes at `addr`; `coherent` for stores with the
+// agent-coherence bit (sc1) and atomic stores, which write through to memory.
+struct Pending {
+    uintptr_t addr;
+    uint8_t bytes[16];
+    int n;
+    bool coherent;
+};
+
 struct Group {
     int nthreads;
+    std::vector<std::vector<Pending>> pending;   // per lane, in issue order
     std::vector<ucontext_t> ctx;
     std::vector<std::vector<char>> stacks;
     ucontext_t sched;
@@ -62,6 +73,23 @@ struct Group {
 
 void yield_op(int kind, uint64_t v, int a);
 uint64_t result();
+
+// ---- weak memory mode (off unless emu_set_weak() turned it on) ----
+// Each simulated XCD (workgroup b runs on XCD b % 8) has a private
+// write-back cache; plain stores complete into it and reach memory only when
+// an agent-scope release writes the cache back, or at the end of the kernel.
+// Coherent (sc1) stores and atomic stores write through to memory; coherent
+// and atomic loads read memory; plain loads may return a stale cached copy
+// until an agent-scope acquire invalidates the cache.  Every store first sits
+// in its lane's queue and completes out of order: at random while the lane
+// runs, at s_waitcnt vmcnt(0) or a release, or -- so that a parked lane's
+// stores still complete, as they do on the hardware -- in the background.
+bool weak_active();
+void mem_store(void* p, const void* src, int n, bool coherent);
+void mem_load(void* dst, const void* p, int n, bool coherent);
+void waitcnt(int bits);
+void fence(int order, const char* scope);
+void complete_all();
 }  // namespace emu
 
 struct EmuIdx { unsigned operator()() const; };
@@ -123,7 +151,7 @@ inline unsigned __float_as_uint(float f) { unsigned u; std::memcpy(&u, &f, 4); r
 #define __builtin_amdgcn_readfirstlane(v) emu_readfirst((v))
 inline void __syncthreads() { emu::yield_op(emu::OP_SYNC, 0, 0); }
 #define __builtin_amdgcn_s_sleep(n) emu::yield_op(emu::OP_NONE, 0, 0)
-#define __builtin_amdgcn_fence(order, scope) std::atomic_thread_fence(std::memory_order_seq_cst)
+#define __builtin_amdgcn_fence(order, scope) emu::fence((order), (scope))
 inline int __popcll(unsigned long long x) { return __builtin_popcountll(x); }
 inline int __ffsll(unsigned long long x) { return __builtin_ffsll((long long)x); }
 inline int __clz(int x) { return x == 0 ? 32 : __builtin_clz((unsigned)x); }
@@ -136,15 +164,38 @@ inline long long wall_clock64() {
 }
 inline float __uint_as_float(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
 #define __HIP_MEMORY_SCOPE_AGENT 3
-template <class T> inline T emu_atomic_load(const T* p) {
-    emu::yield_op(emu::OP_NONE, 0, 0);   // let other fibers / threads progress
-    return __atomic_load_n(p, __ATOMIC_SEQ_CST);
+inline bool emu_order_releases(int o) {
+    return o == __ATOMIC_RELEASE || o == __ATOMIC_ACQ_REL || o == __ATOMIC_SEQ_CST;
 }
-template <class T, class U> inline void emu_atomic_store(T* p, U v) { __atomic_store_n(p, (T)v, __ATOMIC_SEQ_CST); }
-template <class T, class U> inline T emu_atomic_fetch_add(T* p, U v) { return __atomic_fetch_add(p, (T)v, __ATOMIC_SEQ_CST); }
-#define __hip_atomic_load(p, o, s) emu_atomic_load((p))
-#define __hip_atomic_store(p, v, o, s) emu_atomic_store((p), (v))
-#define __hip_atomic_fetch_add(p, v, o, s) emu_atomic_fetch_add((p), (v))
+inline bool emu_order_acquires(int o) {
+    return o == __ATOMIC_ACQUIRE || o == __ATOMIC_ACQ_REL || o == __ATOMIC_SEQ_CST;
+}
+template <class T> inline T emu_atomic_load(const T* p, int o) {
+    emu::yield_op(emu::OP_NONE, 0, 0);   // let other fibers / threads progress
+    if (!emu::weak_active()) return __atomic_load_n(p, __ATOMIC_SEQ_CST);
+    T v;
+    emu::mem_load(&v, p, int(sizeof(T)), true);
+    if (emu_order_acquires(o)) emu::fence(__ATOMIC_ACQUIRE, "agent");
+    return v;
+}
+template <class T, class U> inline void emu_atomic_store(T* p, U v, int o) {
+    if (!emu::weak_active()) { __atomic_store_n(p, (T)v, __ATOMIC_SEQ_CST); return; }
+    if (emu_order_releases(o)) emu::fence(__ATOMIC_RELEASE, "agent");
+    const T t = (T)v;
+    emu::mem_store(p, &t, int(sizeof(T)), true);
+}
+template <class T, class U> inline T emu_atomic_fetch_add(T* p, U v, int o) {
+    if (!emu::weak_active()) return __atomic_fetch_add(p, (T)v, __ATOMIC_SEQ_CST);
+    // performed at memory; the lane's own earlier stores stay queued unless
+    // the order asks for a release
+    if (emu_order_releases(o)) emu::fence(__ATOMIC_RELEASE, "agent");
+    const T r = __atomic_fetch_add(p, (T)v, __ATOMIC_SEQ_CST);
+    if (emu_order_acquires(o)) emu::fence(__ATOMIC_ACQUIRE, "agent");
+    return r;
+}
+#define __hip_atomic_load(p, o, s) emu_atomic_load((p), (o))
+#define __hip_atomic_store(p, v, o, s) emu_atomic_store((p), (v), (o))
+#define __hip_atomic_fetch_add(p, v, o, s) emu_atomic_fetch_add((p), (v), (o))
 template <class T, class U> inline T atomicAdd(T* p, U v) { return __atomic_fetch_add(p, (T)v, __ATOMIC_SEQ_CST); }
 
 // Buffer descriptors and buffer stores: the emulation keeps base and size
@@ -154,27 +205,54 @@ struct emu_buffer_rsrc { char* base; uint32_t n; };
 inline emu_buffer_rsrc emu_make_buffer_rsrc(void* p, int, int n, unsigned) {
     return emu_buffer_rsrc{static_cast<char*>(p), uint32_t(n)};
 }
-template <class V> inline void emu_buffer_store(V v, emu_buffer_rsrc r, int off) {
+// The cache-policy bit of a buffer access that makes it agent-coherent (sc1).
+constexpr int kEmuCpolSc1 = 16;
+// Negative control: stores with the sc1 bit behave as plain stores.
+#ifdef EMU_MUTATE_SC1_STORES_PLAIN
+constexpr bool kEmuSc1StoresCoherent = false;
+#else
+constexpr bool kEmuSc1StoresCoherent = true;
+#endif
+template <class V> inline void emu_buffer_store(V v, emu_buffer_rsrc r, int off, int aux) {
     if (off < 0 || uint64_t(uint32_t(off)) + sizeof(V) > r.n) {
         std::fprintf(stderr, "[emu] buffer store at %d outside a %u-byte range\n", off, r.n);
         std::abort();
     }
-    std::memcpy(r.base + off, &v, sizeof(V));
+    if (emu::weak_active())
+        emu::mem_store(r.base + off, &v, int(sizeof(V)), kEmuSc1StoresCoherent && (aux & kEmuCpolSc1));
+    else
+        std::memcpy(r.base + off, &v, sizeof(V));
 }
 struct emu_v4u32 { uint32_t v[4]; };
-inline emu_v4u32 emu_buffer_load_b128(emu_buffer_rsrc r, int off) {
+inline emu_v4u32 emu_buffer_load_b128(emu_buffer_rsrc r, int off, int aux) {
     if (off < 0 || uint64_t(uint32_t(off)) + 16 > r.n) {
         std::fprintf(stderr, "[emu] buffer load at %d outside a %u-byte range\n", off, r.n);
         std::abort();
     }
     emu_v4u32 v;
-    std::memcpy(&v, r.base + off, 16);
+    if (emu::weak_active())
+        emu::mem_load(&v, r.base + off, 16, (aux & kEmuCpolSc1) != 0);
+    else
+        std::memcpy(&v, r.base + off, 16);
     return v;
 }
 #define __builtin_amdgcn_make_buffer_rsrc(p, s, n, f) emu_make_buffer_rsrc((void*)(p), (s), (n), (f))
-#define __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, aux) emu_buffer_load_b128((r), (off))
-#define __builtin_amdgcn_raw_buffer_store_b128(v, r, off, soff, aux) emu_buffer_store((v), (r), (off))
-#define __builtin_amdgcn_s_waitcnt(x) ((void)0)
+#define __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, aux) emu_buffer_load_b128((r), (off), (aux))
+#define __builtin_amdgcn_raw_buffer_store_b128(v, r, off, soff, aux) emu_buffer_store((v), (r), (off), (aux))
+#define __builtin_amdgcn_s_waitcnt(x) emu::waitcnt((x))
+// Nontemporal accesses are plain (cached) accesses with a hint.
+template <class V> inline void emu_nt_store(V v, V* p) {
+    if (emu::weak_active()) emu::mem_store(p, &v, int(sizeof(V)), false);
+    else std::memcpy(p, &v, sizeof(V));
+}
+template <class V> inline V emu_nt_load(const V* p) {
+    V v;
+    if (emu::weak_active()) emu::mem_load(&v, p, int(sizeof(V)), false);
+    else std::memcpy(&v, p, sizeof(V));
+    return v;
+}
+#define __builtin_nontemporal_store(v, p) emu_nt_store((v), (p))
+#define __builtin_nontemporal_load(p) emu_nt_load((p))
 
 inline hipError_t hipGetLastError() { return hipSuccess; }
 inline hipError_t hipGetDevice(int* d) { *d = 0; return 0; }
