@@ -82,8 +82,10 @@ uint64_t result();
 // and atomic loads read memory; plain loads may return a stale cached copy
 // until an agent-scope acquire invalidates the cache.  Every store first sits
 // in its lane's queue and completes out of order: at random while the lane
-// runs, at s_waitcnt vmcnt(0) or a release, or -- so that a parked lane's
-// stores still complete, as they do on the hardware -- in the background.
+// runs, at s_waitcnt vmcnt(0) or a release, before a load of the same lane
+// to the same bytes (one wave's accesses to one address stay in order), or
+// -- so that a parked lane's stores still complete, as they do on the
+// hardware -- in the background.
 bool weak_active();
 void mem_store(void* p, const void* src, int n, bool coherent);
 void mem_load(void* dst, const void* p, int n, bool coherent);
