@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--no-fused-incast", action="store_true",
+                    help="skip the fused mode on the skewed incast workload")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-pipelined", action="store_true")
     ap.add_argument("--no-coalesce", action="store_true",
@@ -283,6 +285,9 @@ def main():
     if not args.no_fused:
         result["fused"] = bench_fused(ep, torch, w, x, idx, wt, stream, K, args.warmup,
                                       tuple(int(m) for m in args.fused_modes.split(",") if m))
+        if w.name != "incast" and not args.no_fused_incast:
+            result["fused_incast"] = bench_fused_workload(ep, torch, wl.WORKLOADS["incast"], dev,
+                                                          stream, args.warmup)
 
     if not args.no_backward:
         result["backward"] = bench_backward(ep, torch, hip, set_events, w, x, lay, wt, send,
@@ -604,6 +609,25 @@ def time_fused(ep, torch, x, idx, wt, E, R, fz, stream, K, W, sync):
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) * 1e3 / K
+
+
+def bench_fused_workload(ep, torch, w, dev, stream, W, K=10, modes=(0, 1)):
+    """The fused mode on a workload of its own (the skewed incast one, 10% of
+    the experts taking half of the picks): its own inputs, the library's own
+    routing, the same parity gate (combine(dispatch(x)) == x, no device
+    error) before timing."""
+    from combine_ep_route_topk_amd import workloads as wl
+    inp = wl.make_inputs(w)
+    logits = torch.from_numpy(inp["logits"]).to(dev)
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+    idx, wt = ep.ep_route_topk(logits, w.k, stream=stream)
+    res = bench_fused(ep, torch, w, x, idx, wt, stream, K, W, modes)
+    res["workload"] = w.describe()
+    res["pct_of_peak"] = (round(100 * res["gbps"] / HBM_PEAK_GBPS, 2)
+                          if res.get("gbps") else None)
+    del x, logits, idx, wt
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_fused(ep, torch, w, x, idx, wt, stream, K, W, modes=tuple(SYNC_MODES)):
