@@ -182,7 +182,12 @@ uint32_t device_cu_count();
 inline uint32_t dispatch_grid_cap() { return device_cu_count() / 2; }
 // Scatters writing (gathers reading) at most this many bytes are
 // latency-bound: they run one vector per lane on an uncapped grid instead.
-constexpr int64_t kSmallScatterBytes = int64_t(64) << 20;
+// A build may set it lower (the host emulation's tests build with 0, so that
+// every size takes the large-batch kernels).
+#ifndef EP_SMALL_SCATTER_BYTES
+#define EP_SMALL_SCATTER_BYTES (int64_t(64) << 20)
+#endif
+constexpr int64_t kSmallScatterBytes = EP_SMALL_SCATTER_BYTES;
 bool small_scatter(int T, int H, int k);
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int normalize,
