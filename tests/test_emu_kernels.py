@@ -159,10 +159,13 @@ def test_emulated_kernels_match_oracle(emu, T, H, E, R, k, seed):
     assert np.array_equal(m.out, x), "fused combine"
 
 
-def test_emulated_fused_random_experts_equals_combine(emu):
+@pytest.mark.parametrize("T,H", [(200, 520), (64, 3584), (40, 7176), (40, 8192)])
+def test_emulated_fused_random_experts_equals_combine(emu, T, H):
     """Non-uniform weights: the fused reduction is bit-identical to ep_combine
-    over the same rows (they share the arithmetic)."""
-    T, H, E, R, k = 200, 520, 16, 4, 8
+    over the same rows (they share the arithmetic) and to the oracle's fp32
+    chain.  Rows of 1, 7, 14 (plus a partial segment) and 16 whole 64-vector
+    segments: one full batch of 14 segments, a short batch, and both."""
+    E, R, k = 16, 4, 8
     rng = np.random.default_rng(11)
     o_idx, _ = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
     wt = rng.random((T, k), dtype=np.float32) - np.float32(0.3)
@@ -179,6 +182,7 @@ def test_emulated_fused_random_experts_equals_combine(emu):
     send[:] = o_send
     m.check(emu.ep_combine(p(send), p(o_lay["pos"]), p(wt), T, H, k, p(out_ref), None))
     assert np.array_equal(m.out, out_ref)
+    assert np.array_equal(m.out, oracle.combine(o_send, o_lay["pos"], wt))
 
 
 def test_emulated_bounded_waits_and_bad_ids(emu):
