@@ -305,7 +305,10 @@ hipError_t launch_scatter(const uint16_t* grad_out, const int32_t* pos, const fl
 {
     const uint32_t segs = uint32_t((nvec + kWave * U - 1) / (kWave * U));
     const uint32_t items = uint32_t((T + kWavesPerBlock - 1) / kWavesPerBlock) * segs;
-    const uint32_t grid = items < cap ? items : cap;
+    // the fewest rounds of items that cap allows, spread evenly over the
+    // smallest grid that keeps that many rounds: no nearly idle last round
+    const uint32_t rounds = (items + cap - 1) / cap;
+    const uint32_t grid = (items + rounds - 1) / rounds;
     EP_LAUNCH((combine_grad_scatter_kernel<U>), dim3(grid), dim3(kBlock), 0, s, grad_out, pos, w,
               T, nvec, k, grad_y, segs, items);
     return hipGetLastError();
@@ -334,14 +337,18 @@ hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* y,
 #undef EP_DOT
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // Three quarters of the CU count: the per-element multiply and tie check
-    // need more waves than dispatch's plain copy to keep the write path busy
-    // (measured on MI355X at T=4096, H=7168, k=8: 119 us with 128 workgroups,
-    // 90.7 us with 192, 93-95 us with 256-1024).
+    // At most thirteen sixteenths of the CU count, in even rounds: the
+    // per-element multiply and tie check need more waves than dispatch's plain
+    // copy to keep the write path busy, and a nearly idle last round of items
+    // costs as much as a full one (measured on MI355X at T=4096, H=7168, k=8,
+    // the whole combine_grad, 2048 items, fixed grids: 160 workgroups 183 us,
+    // 176 178 us, 192 173.9-178.5 us (11 rounds, 128 busy in the last), 200
+    // 179 us (48 busy), 208 172.3-173.8 us (10 rounds, 176 busy), 216 176 us,
+    // 224 176.7-176.9 us (32 busy)).
     // a small batch: one vector per lane on an uncapped grid, as in dispatch
     if (small_scatter(T, H, k))
         return launch_scatter<1>(grad_out, pos, w, T, nvec, k, grad_y, kMaxGrid, s);
-    const uint32_t cap = dispatch_grid_cap() * 3 / 2;
+    const uint32_t cap = dispatch_grid_cap() * 13 / 8;
     if (nvec % (kWave * 7) == 0) return launch_scatter<7>(grad_out, pos, w, T, nvec, k, grad_y, cap, s);
     if (nvec >= kWave * 8) return launch_scatter<8>(grad_out, pos, w, T, nvec, k, grad_y, cap, s);
     if (nvec >= kWave * 4) return launch_scatter<4>(grad_out, pos, w, T, nvec, k, grad_y, cap, s);

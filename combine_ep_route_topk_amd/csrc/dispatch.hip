@@ -69,9 +69,9 @@ __device__ __noinline__ void copy_tail(const char* __restrict__ src, char* __res
 // one time cover whole rows, so each destination row is written as one
 // contiguous run (measured on MI355X at T=4096, H=7168, k=8: 1-2 us less
 // than token-fastest order).  A 1-D grid of at most half as many workgroups
-// as the GPU has CUs strides over the items: fewer concurrent streams of
-// scattered row writes keep better DRAM locality, and 128 workgroups (512
-// waves) already saturate the write path (measured at the same shape:
+// as the GPU has CUs strides over the items in even rounds: fewer concurrent
+// streams of scattered row writes keep better DRAM locality, and 128
+// workgroups (512 waves) already saturate the write path (measured at the same shape:
 // dispatch alone 92.4 -> 87.7-89.0 us with 96-128 workgroups; the whole
 // route/layout/dispatch/combine step 205.5-207.2 -> 199.4-202.1 us).
 // Rows at or past S (T*k, or a smaller receive buffer's row count) are never
@@ -106,7 +106,10 @@ hipError_t launch_u(const uint16_t* x, int T, int nvec, int k, const int32_t* po
 {
     const uint32_t segs = uint32_t((nvec + kWave * U - 1) / (kWave * U));
     const uint32_t items = uint32_t((T + kWavesPerBlock - 1) / kWavesPerBlock) * segs;
-    const uint32_t grid = items < cap ? items : cap;
+    // the fewest rounds of items that cap allows, spread evenly over the
+    // smallest grid that keeps that many rounds: no nearly idle last round
+    const uint32_t rounds = (items + cap - 1) / cap;
+    const uint32_t grid = (items + rounds - 1) / rounds;
     EP_LAUNCH((dispatch_kernel<U>), dim3(grid), dim3(kBlock), 0, s, x, T, nvec, k, pos,
               send, segs, items, bound);
     return hipGetLastError();

@@ -213,6 +213,39 @@ def test_backward_skips_rows_outside_the_buffer(epm):
     assert_same_bits(bits(gx), oracle.dispatch_grad(y0, pos), "dispatch_grad with picks outside")
 
 
+@pytest.mark.parametrize("T,H,E,R,k,seed", [(4099, 4096, 64, 8, 8, 321),
+                                             (4097, 7168, 64, 8, 6, 322)])
+def test_backward_large_skips_rows_outside_the_buffer(epm, T, H, E, R, k, seed):
+    """The same at sizes that take the capped, evenly rounded scatter grid
+    (more than 64 MiB of grad_y; 8 and 7 vectors per lane), with a last group
+    of tokens that is not full: every kept row bit-exact, the lost rows
+    untouched, grad_w = 0 for the lost picks and within the bound elsewhere."""
+    pos, w, g, y = backward_inputs(T, H, E, R, k, seed)
+    picks = [(0, 0, -1), (T // 2, k - 1, T * k), (T - 1, 1, T * k + 3)]
+    bad = pos.copy()
+    lost = []
+    for t, j, v in picks:
+        lost.append(pos[t, j])
+        bad[t, j] = v
+    say(f"combine_grad (capped grid) with invalid pos T={T} H={H} k={k}")
+    gy = poison_bits((T * k, H))
+    gw = torch.full((T, k), float("nan"), dtype=torch.float32, device=DEV)
+    epm.ep_combine_grad(to_dev_bits(g), to_dev_bits(y), torch.from_numpy(bad).to(DEV),
+                        torch.from_numpy(w).to(DEV), grad_y=gy, grad_w=gw)
+    torch.cuda.synchronize()
+    r_gy, r_gw = oracle.combine_grad(g, y, pos, w)
+    got = bits(gy)
+    keep = np.setdiff1d(np.arange(T * k), lost)
+    assert np.array_equal(got[keep], r_gy[keep])
+    assert np.all(got[lost] == 0xFFFF), "a row outside the buffer's picks was written"
+    gw_np = gw.cpu().numpy()
+    mask = np.ones((T, k), bool)
+    for t, j, _ in picks:
+        mask[t, j] = False
+        assert gw_np[t, j] == 0.0
+    check_grad_w(np.where(mask, gw_np, 0.0), np.where(mask, r_gw, 0.0), g, y, pos)
+
+
 def test_backward_validation(epm):
     T, H, k = 4, 16, 2
     d = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device=DEV)
