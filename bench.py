@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-fused-incast", action="store_true",
                     help="skip the fused mode on the skewed incast workload")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the forward step (and fused call) on the other workloads")
     ap.add_argument("--no-pipelined", action="store_true")
     ap.add_argument("--no-coalesce", action="store_true",
                     help="skip the rank-coalesced send leg (one record per token and rank)")
@@ -289,6 +291,10 @@ def main():
             result["fused_incast"] = bench_fused_workload(ep, torch, wl.WORKLOADS["incast"], dev,
                                                           stream, args.warmup)
 
+    if not args.no_workloads:
+        result["workloads"] = bench_workloads(ep, torch, hip, set_events, dev, stream,
+                                              [n for n in ("decode", "glm45air", "incast")
+                                               if n != w.name], args.warmup)
     if not args.no_backward:
         result["backward"] = bench_backward(ep, torch, hip, set_events, w, x, lay, wt, send,
                                             dev, stream, K, args.warmup, not args.no_isolated)
@@ -491,6 +497,59 @@ def time_steps(torch, hip, step, names, K):
             hip.destroy(e)
     hip.destroy(region_start)
     return per_op, wall
+
+
+def bench_workloads(ep, torch, hip, set_events, dev, stream, names, W, K=20):
+    """The forward step (route -> layout -> dispatch -> combine) on each other
+    workload, timed like the headline (each op's own kernels, back to back),
+    behind the same parity gate; and the fused call (item events) where the
+    fused leg does not already cover the workload."""
+    from combine_ep_route_topk_amd import workloads as wl
+    out = {}
+    for name in names:
+        w = wl.WORKLOADS[name]
+        T, H, E, R, k = w.T, w.H, w.E, w.R, w.k
+        inp = wl.make_inputs(w)
+        logits = torch.from_numpy(inp["logits"]).to(dev)
+        x = torch.from_numpy(inp["x"].view(np.int16)).to(dev).view(torch.bfloat16)
+        del inp
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        wt = torch.empty((T, k), dtype=torch.float32, device=dev)
+        lay = ep.layout_outputs(T, k, E, R, dev, slot_src=True)
+        send = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        ops = [ep.bind_route_topk(logits, k, True, idx, wt, stream),
+               ep.bind_dispatch_layout(idx, E, R, lay, stream),
+               ep.bind_dispatch(x, lay["pos"], send, stream),
+               ep.bind_combine(send, lay["pos"], wt, y, stream)]
+        step = make_step(ops, set_events)
+        step()
+        torch.cuda.synchronize()
+        if not torch.equal(y.view(torch.int16), x.view(torch.int16)) or \
+                ep.ep_get_device_error(lay["workspace"]) != ep.EP_OK:
+            out[name] = {"workload": w.describe(), "status": "parity gate failed"}
+            continue
+        for _ in range(W):
+            step()
+        names4 = ["route", "layout", "dispatch", "combine"]
+        per_op, wall = time_steps(torch, hip, step, names4, K)
+        mean_us = {n: float(np.mean(v)) for n, v in per_op.items()}
+        ab = wl.algorithmic_bytes(w)
+        dc_us = mean_us["dispatch"] + mean_us["combine"]
+        gbps = (ab["dispatch"] + ab["combine"]) / (dc_us * 1e-6) / 1e9
+        res = {"workload": w.describe(),
+               "per_op_us": {n: round(v, 2) for n, v in mean_us.items()},
+               "dispatch_combine_us": round(dc_us, 2), "gbps": round(gbps, 1),
+               "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+               "step_us": round(wall / K * 1e6, 2), "parity": True}
+        if name != "incast":
+            f = bench_fused(ep, torch, w, x, idx, wt, stream, K, W, modes=(0,))
+            res["fused_us"] = f["us_per_call"]
+            res["fused_status"] = f["sync_modes"].get("item_events", {}).get("status")
+        out[name] = res
+        del logits, x, idx, wt, lay, send, y, ops, step
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_backward(ep, torch, hip, set_events, w, x, lay, wt, send, dev, stream, K, W,
