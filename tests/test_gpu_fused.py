@@ -66,6 +66,39 @@ def test_fused_matches_oracle(epm, name):
     assert torch.equal(out.view(torch.int16), fz["out"].view(torch.int16))
 
 
+@pytest.mark.parametrize("name", wl.ORDER)
+def test_fused_signed_weights_match_oracle(epm, name):
+    """Weights that are not the routing's (signed, not normalised): the fused
+    reduction -- a token's row segments reduced in batches before they are
+    stored -- gives the oracle's fp32 chain bit for bit, and the three-launch
+    combine over the same rows; at H=4096 a row is one short batch."""
+    w = wl.WORKLOADS[name]
+    c = Case(w)
+    rng = np.random.default_rng(w.seed + 77)
+    ws = (rng.random(c.wt.shape, dtype=np.float32) * np.float32(1.5) - np.float32(0.5))
+    say(f"fused, signed weights, {w.describe()}")
+    x = to_dev_bits(c.x)
+    idx = torch.from_numpy(c.idx).to(DEV)
+    d_ws = torch.from_numpy(ws).to(DEV)
+    fz = epm.ep_fused_dispatch_combine(x, idx, d_ws, w.E, w.R, want_epoch=True)
+    torch.cuda.synchronize()
+    assert epm.ep_get_device_error(fz["workspace"]) == epm.EP_OK
+    o_lay = oracle.dispatch_layout(c.idx, w.E, w.R)
+    o_send = oracle.dispatch(c.x, o_lay["pos"])
+    out = bits(fz["out"])
+    if w.T <= 4096:
+        assert_same_bits(out, oracle.combine(o_send, o_lay["pos"], ws), "fused, signed weights")
+    else:
+        toks = np.unique(np.concatenate([np.arange(0, w.T, 7), [w.T - 1]]))
+        assert_same_bits(out[toks], oracle.combine_tokens(o_send, o_lay["pos"], ws, toks),
+                         "fused, signed weights (sampled tokens)")
+    lay = epm.ep_dispatch_layout(idx, w.E, w.R)
+    send = epm.ep_dispatch(x, lay["pos"])
+    ref = epm.ep_combine(send, lay["pos"], d_ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int16), fz["out"].view(torch.int16))
+
+
 def test_fused_epochs_and_reuse(epm):
     """Repeated calls on one workspace: the epoch advances by one per call, and
     a call on new inputs over rows holding the previous call's trailers reads
