@@ -71,9 +71,9 @@ __device__ __noinline__ void copy_tail(const char* __restrict__ src, char* __res
 // than token-fastest order).  A 1-D grid of at most half as many workgroups
 // as the GPU has CUs strides over the items in even rounds: fewer concurrent
 // streams of scattered row writes keep better DRAM locality, and 128
-// workgroups (512 waves) already saturate the write path (measured at the same shape:
-// dispatch alone 92.4 -> 87.7-89.0 us with 96-128 workgroups; the whole
-// route/layout/dispatch/combine step 205.5-207.2 -> 199.4-202.1 us).
+// workgroups (512 waves) already saturate the write path (measured at the
+// same shape: dispatch alone 92.4 -> 87.7-89.0 us with 96-128 workgroups; the
+// whole route/layout/dispatch/combine step 205.5-207.2 -> 199.4-202.1 us).
 // Rows at or past S (T*k, or a smaller receive buffer's row count) are never
 // written.
 template <int U>

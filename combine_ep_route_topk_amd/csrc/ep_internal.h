@@ -177,8 +177,8 @@ inline size_t fused_row_stride(int H) {
 // ----------------------------------------------------------------- launchers
 // The CU count of the current device (cached per device).
 uint32_t device_cu_count();
-// Grid cap of the kernels that scatter whole rows (dispatch, the backward
-// combine's gradient scatter): half the CU count of the current device.
+// Grid cap of dispatch's row scatter: half the CU count of the current
+// device (the backward combine's gradient scatter takes 13/8 of it).
 inline uint32_t dispatch_grid_cap() { return device_cu_count() / 2; }
 // Scatters writing (gathers reading) at most this many bytes are
 // latency-bound: they run one vector per lane on an uncapped grid instead.
