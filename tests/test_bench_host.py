@@ -41,16 +41,32 @@ def test_traffic_reads_null_when_the_sources_changed(kernel, tmp_path, monkeypat
     os.makedirs(tmp_path / "profiles")
     shutil.copytree(os.path.join(ROOT, "combine_ep_route_topk_amd", "csrc"),
                     tmp_path / "combine_ep_route_topk_amd" / "csrc")
-    shutil.copy(src, tmp_path / "profiles")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    rec = json.loads([ln for ln in open(src) if ln.startswith("json:")][-1][5:])
-    got = bench.traffic_for(kernel, "dsv3")
-    # the committed summary matches the committed sources
-    assert got == rec["hbm_bytes_per_launch"]
-    # a change to any of the kernel's sources voids it
-    first = bench.KERNEL_SOURCES[kernel][0]
-    with open(tmp_path / "combine_ep_route_topk_amd" / "csrc" / first, "a") as f:
-        f.write("\n// changed\n")
-    assert bench.traffic_for(kernel, "dsv3") is None
-    # and a workload without a summary has none
+    lines = open(src).read().splitlines()
+    rec = json.loads([ln for ln in lines if ln.startswith("json:")][-1][5:])
+    # a summary taken on these very sources is read ...
+    rec["source_sha256_16"] = bench.src_digest(bench.KERNEL_SOURCES[kernel])
+    body = [ln for ln in lines if not ln.startswith("json:")] + ["json:" + json.dumps(rec)]
+    (tmp_path / "profiles" / f"traffic_{kernel}_dsv3.txt").write_text("\n".join(body) + "\n")
+    assert bench.traffic_for(kernel, "dsv3") == rec["hbm_bytes_per_launch"]
+    # ... and a change to any of the kernel's sources voids it
+    for n in bench.KERNEL_SOURCES[kernel]:
+        path = tmp_path / "combine_ep_route_topk_amd" / "csrc" / n
+        keep = path.read_bytes()
+        path.write_bytes(keep + b"\n// changed\n")
+        assert bench.traffic_for(kernel, "dsv3") is None, n
+        path.write_bytes(keep)
+    assert bench.traffic_for(kernel, "dsv3") == rec["hbm_bytes_per_launch"]
+    # a workload without a summary has none
     assert bench.traffic_for(kernel, "decode") is None
+
+
+def test_committed_traffic_matches_its_digest_or_reads_null():
+    """The committed summaries are read only where their digest is current."""
+    for kernel, names in bench.KERNEL_SOURCES.items():
+        src = os.path.join(ROOT, "profiles", f"traffic_{kernel}_dsv3.txt")
+        if not os.path.exists(src):
+            continue
+        rec = json.loads([ln for ln in open(src) if ln.startswith("json:")][-1][5:])
+        current = rec["source_sha256_16"] == bench.src_digest(names)
+        assert bench.traffic_for(kernel, "dsv3") == (rec["hbm_bytes_per_launch"] if current else None)
