@@ -307,7 +307,7 @@ ep_status ep_window_copy(const void* src, void* dst, int64_t row_bytes, int64_t 
  * Each send row is the bf16 payload followed by a 16-byte trailer
  * { u64 epoch, u32 slot_src, u32 0 }, then one u64 flag per 1 KiB chunk of
  * the payload (used by EP_FUSED_SYNC_CHUNK_FLAG only), padded to
- * ep_fused_row_stride_bytes(H) = roundup(2H + 16 + 8*ceil(2H/1024), 128).
+ * ep_fused_row_stride_bytes(H) = roundup(2H + 16 + 8*ceil(2H/1024), 1024).
  *   send_rows  u8 [T*k][stride]  out: payload = x[token of the slot]; trailer
  *                                as above with this call's epoch.
  *   out        bf16 [T][H]       out: combine of the payload rows, identical

@@ -64,7 +64,7 @@ int main(void)
           EP_ERR_INVALID_ARG);
     CHECK(f_dispatch(NULL, 4, 16, 2, NULL, NULL, NULL) == EP_ERR_INVALID_ARG);
     CHECK(f_combine(NULL, NULL, NULL, 4, 16, 2, NULL, NULL) == EP_ERR_INVALID_ARG);
-    CHECK(f_stride(7168) == 14464);
+    CHECK(f_stride(7168) == 15360);
     CHECK(f_fused_ws(4096, 8, 256, 32) > f_layout_ws(4096, 8, 256, 32));
     CHECK(f_fused_init(NULL, 0, NULL) == EP_ERR_INVALID_ARG);
     CHECK(f_fused(NULL, NULL, NULL, 4, 16, 2, 8, 2, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
@@ -87,7 +87,7 @@ int main(void)
         CHECK(ep_fused_last_epoch(NULL, &epoch, NULL) == EP_ERR_INVALID_ARG);
     }
     CHECK(ep_dispatch_layout_workspace_bytes(4096, 8, 256, 32) > 0);
-    CHECK(ep_fused_row_stride_bytes(7168) % 128 == 0);
+    CHECK(ep_fused_row_stride_bytes(7168) % 1024 == 0);
 
     /* the host scheduler: 3 peers, windows of 5, 0 and 9 rows, units of 4 rows */
     {

@@ -54,10 +54,10 @@ def test_workspace_and_stride_queries(ep):
     assert big >= 4 * 16384 * 8          # holds one rank word per slot
     assert lib.ep_dispatch_layout_workspace_bytes(0, 2, 8, 2) == 0
     assert lib.ep_fused_workspace_bytes(16384, 8, 256, 64) > big
-    # payload + 16-byte trailer, rounded up to 128-byte lines
+    # payload + 16-byte trailer + chunk flags, rounded up to 1 KiB
     for H in (8, 256, 4096, 7168, 7176):
         chunks = -(-2 * H // 1024)
-        assert lib.ep_fused_row_stride_bytes(H) == -(-(2 * H + 16 + 8 * chunks) // 128) * 128
+        assert lib.ep_fused_row_stride_bytes(H) == -(-(2 * H + 16 + 8 * chunks) // 1024) * 1024
     assert lib.ep_fused_row_stride_bytes(7) == 0
 
 
