@@ -186,6 +186,39 @@ def test_fused_bounded_waits_drain_and_recover(epm):
     assert np.array_equal(bits(fz["out"]), c.x)
 
 
+def test_fused_bad_id_beside_the_batched_path(epm):
+    """k = 8 and 14 KiB rows: every token but one takes the batched reduction;
+    the token with an id outside [0, E) gets pos = -1 for that pick and the
+    segment-at-a-time path, where the missing row counts as zeros.  The call
+    reports the device error, equals the three-launch path bit for bit, and
+    the bad token's output is the oracle's fp32 chain over its rows with that
+    one row zero."""
+    T, H, E, R, k = 96, 7168, 64, 8, 8
+    rng = np.random.default_rng(23)
+    idx, wt = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
+    wt = (wt - np.float32(0.05)).astype(np.float32)        # not normalised
+    bad_t, bad_j = 37, 3
+    idx[bad_t, bad_j] = E + 5
+    x = wl.make_rows(T, H, 24)
+    say("fused, k=8, one bad id")
+    d_x, d_idx, d_w = to_dev_bits(x), torch.from_numpy(idx).to(DEV), torch.from_numpy(wt).to(DEV)
+    fz = epm.ep_fused_dispatch_combine(d_x, d_idx, d_w, E, R)
+    torch.cuda.synchronize()
+    assert epm.ep_get_device_error(fz["workspace"]) == epm.EP_ERR_DEVICE
+    pos = fz["pos"].cpu().numpy()
+    assert pos[bad_t, bad_j] == -1
+    lay = epm.ep_dispatch_layout(d_idx, E, R)
+    send = epm.ep_dispatch(d_x, lay["pos"])
+    ref = epm.ep_combine(send, lay["pos"], d_w)
+    torch.cuda.synchronize()
+    assert np.array_equal(lay["pos"].cpu().numpy(), pos)
+    out = bits(fz["out"])
+    assert np.array_equal(out, bits(ref)), "fused differs from the three-launch path"
+    rows = np.stack([x[bad_t] if j != bad_j else np.zeros(H, np.uint16) for j in range(k)])
+    want = oracle.combine(rows, np.arange(k, dtype=np.int32).reshape(1, k), wt[bad_t:bad_t + 1])
+    assert_same_bits(out[bad_t:bad_t + 1], want, "the token with a bad id")
+
+
 def test_fused_flags_bad_expert_ids(epm):
     T, H, k, E, R = 300, 64, 2, 8, 2
     rng = np.random.default_rng(21)
