@@ -120,6 +120,28 @@ def test_sync_modes_back_to_back_without_host_sync(epm, sync):
     assert np.array_equal(bits(fz["out"]), c.x)
 
 
+@pytest.mark.parametrize("name,calls", [("dsv3", 200), ("incast", 60)])
+def test_every_mode_long_back_to_back(epm, name, calls):
+    """Long runs without host synchronisation, every readiness mode in turn on
+    one workspace (epochs keep growing across modes): every 20th call the
+    device error word is clear and the output is the round trip, then the
+    output is zeroed so the next check sees only later calls' work."""
+    w = wl.WORKLOADS[name]
+    inp = wl.make_inputs(w)
+    x = to_dev_bits(inp["x"])
+    idx, wt = epm.ep_route_topk(torch.from_numpy(inp["logits"]).to(DEV), w.k)
+    fz = epm.fused_outputs(w.T, w.H, w.k, w.E, w.R, DEV)
+    for sync in (0, *MODES):
+        say(f"fused sync={MODES.get(sync, 'item events')} {name} x{calls}")
+        for c in range(calls):
+            epm.ep_fused_dispatch_combine(x, idx, wt, w.E, w.R, out=fz, sync=sync)
+            if (c + 1) % 20 == 0:
+                torch.cuda.synchronize()
+                assert epm.ep_get_device_error(fz["workspace"]) == epm.EP_OK, (sync, c)
+                assert torch.equal(fz["out"].view(torch.int16), x.view(torch.int16)), (sync, c)
+                fz["out"].zero_()
+
+
 def test_sentinel_collision_is_reported(epm):
     """UBEP sec. 3.4: data equal to the sentinel cannot be told from no data.
     A token whose leading 16 bytes hold the reserved 32-bit word makes the
