@@ -158,8 +158,16 @@ void mem_load(void* dst, const void* p, int n, bool coherent) {
 
 void waitcnt(int bits) {
 #ifndef EMU_MUTATE_NO_STORE_WAIT
-    // s_waitcnt vmcnt(0): vmcnt is bits [3:0] and [15:14]
-    if (weak_active() && (bits & 0xF) == 0 && ((bits >> 14) & 3) == 0) complete_all();
+    // s_waitcnt vmcnt(0): vmcnt is bits [3:0] and [15:14].  The counter is
+    // the wave's, not the lane's: the hardware issues every store of the
+    // wave, for all its active lanes, before it reaches the wait, and the
+    // wait covers them all.  Each lane completes its own queue, then the
+    // lanes of the wave meet (a wave op), so no lane goes past the wait
+    // while another lane of its wave still has a store outstanding.
+    if (weak_active() && (bits & 0xF) == 0 && ((bits >> 14) & 3) == 0) {
+        complete_all();
+        yield_op(OP_WAITCNT, 0, 0);
+    }
 #else
     (void)bits;
 #endif
@@ -295,7 +303,7 @@ static void run_group(const std::function<void()>& body, int nthreads) {
             for (int t = lo; t < hi; ++t) {
                 int o = g.op[t];
                 if (o == OP_EXIT) continue;
-                if (o == OP_BALLOT || o == OP_SHFL) {
+                if (o == OP_BALLOT || o == OP_SHFL || o == OP_WAITCNT) {
                     if (kind == -2) kind = o;
                     else if (kind != o) fail(&g, "lanes of one wave at different wave ops");
                     waiting = true;
@@ -318,7 +326,7 @@ static void run_group(const std::function<void()>& body, int nthreads) {
                 for (int t = lo; t < hi; ++t)
                     if (g.op[t] != OP_EXIT && g.val[t]) m |= uint64_t(1) << (t - lo);
                 for (int t = lo; t < hi; ++t) g.res[t] = m;
-            } else {
+            } else if (kind == OP_SHFL) {
                 for (int t = lo; t < hi; ++t) {
                     if (g.op[t] == OP_EXIT) continue;
                     int src = lo + g.arg[t];

@@ -44,7 +44,7 @@ extern thread_local U3 g_block;
 extern U3 g_grid;
 extern long g_op_limit;
 
-enum OpKind { OP_NONE, OP_BALLOT, OP_SHFL, OP_READLANE, OP_READFIRST, OP_SYNC, OP_EXIT };
+enum OpKind { OP_NONE, OP_BALLOT, OP_SHFL, OP_READLANE, OP_READFIRST, OP_SYNC, OP_EXIT, OP_WAITCNT };
 
 // One store that a lane has issued and that has not completed yet (weak
 // memory mode): up to 16 bytes at `addr`; `coherent` for stores with the
