@@ -413,8 +413,51 @@ extern "C" int emu_errors() { return emu::g_errors.load(); }
 //   mode 3: as mode 1, but the reader loads the datum once before polling
 //           and not again after an acquire -- stale (its cached copy)
 //   mode 4: as mode 3 with an acquire after the flag -- never stale
+// Mode 5 of the litmus: every lane of one wave stores its own word of the
+// data (coherent stores), the wave waits for its stores, then lane 0 alone
+// stores the flag.  The wait is the wave's, so the reader must never see a
+// word of another lane stale.
+static int litmus_wave_wait(int trials)
+{
+    int stale = 0;
+    alignas(16) static uint32_t words[64];
+    alignas(16) static uint64_t flag[2];
+    for (int trial = 0; trial < trials; ++trial) {
+        std::memset(words, 0, sizeof words);
+        std::memset(flag, 0, sizeof flag);
+        std::atomic<int> seen_stale{0};
+        emu::launch(dim3(2), dim3(64), [&]() {
+            const unsigned lane = threadIdx.x;
+            if (blockIdx.x == 0) {
+                const uint32_t v = uint32_t(trial) * 64u + lane + 1u;
+                emu::mem_store(&words[lane], &v, 4, true);
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+                if (lane == 0) __hip_atomic_store(&flag[0], uint64_t(1), __ATOMIC_RELAXED, 3);
+            } else {
+                if (lane != 0) return;
+                long spins = 0;
+                while (__hip_atomic_load(&flag[0], __ATOMIC_RELAXED, 3) != 1) {
+                    if (++spins > 50000000L) { std::fprintf(stderr, "[emu] litmus hung\n"); std::abort(); }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                for (unsigned i = 0; i < 64; ++i) {
+                    uint32_t r;
+                    emu::mem_load(&r, &words[i], 4, false);
+                    if (r != uint32_t(trial) * 64u + i + 1u) {
+                        seen_stale.fetch_add(1);
+                        break;
+                    }
+                }
+            }
+        });
+        stale += seen_stale.load();
+    }
+    return stale;
+}
+
 extern "C" int emu_litmus_message_passing(int mode, int trials)
 {
+    if (mode == 5) return litmus_wave_wait(trials);
     int stale = 0;
     alignas(16) static uint32_t datum[4];
     alignas(16) static uint64_t flag[2];

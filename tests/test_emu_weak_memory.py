@@ -17,7 +17,9 @@ exactly that:
 
 Pins of the model itself (message-passing litmus tests): it shows a stale
 read for plain data behind a coherent flag and for a missing acquire, and
-never for the ordered patterns.
+never for the ordered patterns -- among them one lane's flag behind the
+wave's wait for every lane's stores (s_waitcnt counts the wave's stores, not
+the lane's).
 
 The real kernels, every readiness mode of the fused kernel included, give the
 oracle's answer under the model.  Two negative controls, each a build that
@@ -59,7 +61,7 @@ def lib(emu_build):
 
 
 @pytest.mark.parametrize("mode,stale", [(0, "always"), (1, "never"), (2, "never"),
-                                        (3, "sometimes"), (4, "never")])
+                                        (3, "sometimes"), (4, "never"), (5, "never")])
 def test_model_message_passing_litmus(lib, mode, stale):
     lib.emu_set_weak(1, ctypes.c_ulonglong(99))
     try:
