@@ -95,6 +95,7 @@ KERNEL_SOURCES = {
     "combine": ["combine.hip", "ep_combine_dev.h", "ep_device.h", "ep_internal.h"],
     "combine_grad": ["backward.hip", "ep_combine_dev.h", "ep_device.h", "ep_internal.h"],
     "dispatch_grad": ["combine.hip", "ep_combine_dev.h", "ep_device.h", "ep_internal.h"],
+    "fused": ["fused.hip", "ep_combine_dev.h", "ep_device.h", "ep_internal.h", "ep_layout_dev.h"],
 }
 
 
@@ -715,7 +716,8 @@ def bench_fused(ep, torch, w, x, idx, wt, stream, K, W, modes=tuple(SYNC_MODES))
         res[name] = {"us_per_call": round(us, 2), "gbps": round(byts / (us * 1e-6) / 1e9, 1)}
     d = res.get("item_events", {})
     return {"us_per_call": d.get("us_per_call"), "gbps": d.get("gbps"),
-            "algorithmic_bytes": byts, "sync_modes": res,
+            "algorithmic_bytes": byts, "traffic": traffic_for("fused", w.name),
+            "sync_modes": res,
             "what": "layout + dispatch + combine (identity experts) in one launch"}
 
 
