@@ -42,7 +42,7 @@ constexpr int kScanItems = 2048;     // (expert, tile) counters per scan block
 // instead of a separate device-wide scan.
 constexpr int kRedundantScanMax = 32768;
 // Counters per scan item of the persistent fused mode: one item covers the
-// 8192 counters of the dsv3-sized layout, so its look-back chain is empty.
+// 8192 counters of a T=4096, k=8, E=256 layout, so its look-back chain is empty.
 constexpr int kFusedScanItems = 8192;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;

@@ -127,7 +127,8 @@ __device__ __forceinline__ void hist_tile(const int32_t* __restrict__ topk_idx, 
 }
 
 // Block-wide scan of the ITEMS counters of scan block `blk`: loads
-// v[q] = cnt[i0 + q] (0 past nCnt) as 16-byte vectors, returns this thread's
+// v[q] = cnt[i0 + q] (0 past nCnt), as 16-byte vectors when nCnt % 4 == 0,
+// and returns this thread's
 // exclusive offset inside the block and the block total.  `sh_wave_total`
 // is LDS scratch.
 template <int ITEMS>
@@ -151,18 +152,27 @@ __device__ __forceinline__ BlockScan<ITEMS> block_scan(const int32_t* __restrict
     const int lane = lane_id();
     r.i0 = blk * ITEMS + tid * kScanPerThread;
     int tsum = 0;
+    // Every load is unconditional, from a clamped in-bounds address (counter
+    // 0) whose value is then dropped: a guarded load becomes a branch with a
+    // full memory wait inside, and the thread's loads would go out one round
+    // trip apart instead of together.
+    if (nCnt % 4 == 0) {                   // a 4-group is wholly inside or outside
 #pragma unroll
-    for (int m = 0; m < kScanPerThread / 4; ++m) {
-        const int i = r.i0 + 4 * m;
-        if (i + 3 < nCnt) {
-            const int4 x = *reinterpret_cast<const int4*>(cnt + i);
-            r.v[4 * m] = x.x;
-            r.v[4 * m + 1] = x.y;
-            r.v[4 * m + 2] = x.z;
-            r.v[4 * m + 3] = x.w;
-        } else {
+        for (int m = 0; m < kScanPerThread / 4; ++m) {
+            const int i = r.i0 + 4 * m;
+            const bool in = i < nCnt;
+            const int4 x = *reinterpret_cast<const int4*>(cnt + (in ? i : 0));
+            r.v[4 * m] = in ? x.x : 0;
+            r.v[4 * m + 1] = in ? x.y : 0;
+            r.v[4 * m + 2] = in ? x.z : 0;
+            r.v[4 * m + 3] = in ? x.w : 0;
+        }
+    } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) r.v[4 * m + c] = i + c < nCnt ? cnt[i + c] : 0;
+        for (int q = 0; q < kScanPerThread; ++q) {
+            const int i = r.i0 + q;
+            const int x = cnt[i < nCnt ? i : 0];
+            r.v[q] = i < nCnt ? x : 0;
         }
     }
 #pragma unroll

@@ -16,7 +16,9 @@
 // by workgroups that are already running -- so the launch cannot deadlock
 // whatever the number of co-resident workgroups:
 //   [hist]    one per tile: tile histogram + stable ranks (shared with the
-//             three-launch layout), then hist_done += 1 (release).
+//             three-launch layout), then hist_done += 1 (release).  A layout
+//             of one tile is a single item instead, which also scans the
+//             counts and publishes the bases (no scan items).
 //   [scan]    one per kFusedScanItems counters: waits for hist_done == nTiles
 //             (an event counter with a static threshold), block scan, then
 //             decoupled look-back over 64-bit status words that carry the
@@ -40,11 +42,11 @@
 // single-copy atomic but a 14 KiB row is not, hence payload -> release ->
 // trailer, and trailer -> acquire -> payload on the reading side.  An
 // agent-scope release FENCE writes back the whole L2 of the XCD (measured at
-// dsv3: 2048 of them cost ~160 us of a 400 us call), so the scatter side
-// releases the way an agent-scope atomic store does instead: the payload is
-// stored agent-coherent (sc1), each wave waits for its stores to complete,
-// then the flags are stored.  The combine side keeps one acquire fence (an
-// L2 invalidate, cheap) per item.
+// T=4096, H=7168, k=8: 2048 of them cost ~160 us of a 400 us call), so the
+// scatter side releases the way an agent-scope atomic store does instead: the
+// payload is stored agent-coherent (sc1), each wave waits for its stores to
+// complete, then the flags are stored.  The combine side keeps one acquire
+// fence (an L2 invalidate, cheap) per item.
 //
 // Scatter items are small (2 tokens) and outnumber the resident workgroups
 // at the shapes that matter, so the first ticket of almost every workgroup is
@@ -162,6 +164,67 @@ __device__ void do_hist(const FusedArgs& a, int tile, int32_t (*hist)[kMaxE]) {
     if (threadIdx.x == 0) fetch_add(&a.hdr->hist_done.v, 1u);
 }
 
+// ---------------------------------------------------------------- one-tile layout item
+// A layout of a single tile (T*k <= kTileSlots, e.g. a decode batch) is one
+// item: the histogram leaves the per-expert totals in LDS, the workgroup
+// scans them itself and publishes the bases as soon as its ranks are stored.
+// No scan item waits on hist_done, invalidates its cache and reads the
+// counts back -- a chain that cost more than the histogram at this size.
+__device__ void do_layout1(const FusedArgs& a, uint32_t ep32, int32_t (*hist)[kMaxE],
+                           int* sh_tot, int* sh_wave_total)
+{
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = lane_id();
+    int key[kChunksPerWave];
+    int rank[kChunksPerWave];
+    tile_ranks(a.idx, a.S, a.E, 1, 0, nullptr, sh_tot, hist, key, rank);
+    const int64_t wave_first = int64_t(wave) * kChunksPerWave * kWave;
+#pragma unroll
+    for (int c = 0; c < kChunksPerWave; ++c) {
+        const int64_t s = wave_first + c * kWave + lane;
+        if (key[c] >= 0)
+            st_relaxed(reinterpret_cast<uint32_t*>(&a.local_rank[s]),
+                       uint32_t(hist[wave][key[c]] + rank[c]));
+    }
+    // exclusive scan of the totals, kMaxE / kBlock experts per thread
+    constexpr int kPer = kMaxE / kBlock;
+    int tot[kPer];
+    int tsum = 0;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int e = tid * kPer + q;
+        tot[q] = e < a.E ? sh_tot[e] : 0;
+        tsum += tot[q];
+    }
+    const int incl = wave_inclusive_sum(tsum);
+    if (lane == kWave - 1) sh_wave_total[wave] = incl;
+    // the ranks are agent-coherent stores: once every wave has seen its own
+    // complete, a reader that sees a base also sees them
+    wait_own_stores();
+    __syncthreads();
+    int run = incl - tsum;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w)
+        if (w < wave) run += sh_wave_total[w];
+    const uint64_t tag = uint64_t(ep32) << 32;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int e = tid * kPer + q;
+        if (e < a.E) {
+            st_relaxed(reinterpret_cast<uint32_t*>(&a.expert_offsets[e]), uint32_t(run));
+            st_relaxed64(&a.fbase[e], tag | uint32_t(run));
+            if (e == a.E - 1)
+                st_relaxed(reinterpret_cast<uint32_t*>(&a.expert_offsets[a.E]),
+                           uint32_t(run + tot[q]));
+        }
+        run += tot[q];
+    }
+    // expert_offsets complete before this workgroup's next ticket claim (the
+    // workgroup that makes the last claim of all reads them after an acquire)
+    wait_own_stores();
+}
+
 // ---------------------------------------------------------------- scan item
 __device__ void do_scan(const FusedArgs& a, int blk, uint32_t ep32, int* sh_wave_total,
                         int* sh_word)
@@ -221,17 +284,25 @@ __device__ void do_scan(const FusedArgs& a, int blk, uint32_t ep32, int* sh_wave
     // and completed before hist_done counted their tile, so publishing needs
     // no write-back first.
     int run = sh_word[1] + bs.thread_excl;
+    // counter i is (expert i / nTiles, tile i % nTiles): one division per
+    // thread, then the tile steps along (an integer division per counter
+    // cost more VALU time than the stores at small layouts)
+    int e = bs.i0 / a.nTiles;
+    int tile = bs.i0 - e * a.nTiles;
 #pragma unroll
     for (int q = 0; q < BlockScan<kFusedScanItems>::kPer; ++q) {
         const int i = bs.i0 + q;
         if (i < a.nCnt) {
-            if (i % a.nTiles == 0)
-                st_relaxed(reinterpret_cast<uint32_t*>(&a.expert_offsets[i / a.nTiles]),
-                           uint32_t(run));
+            if (tile == 0)
+                st_relaxed(reinterpret_cast<uint32_t*>(&a.expert_offsets[e]), uint32_t(run));
             st_relaxed64(&a.fbase[i], tag | uint32_t(run));
             run += bs.v[q];
             if (i == a.nCnt - 1)
                 st_relaxed(reinterpret_cast<uint32_t*>(&a.expert_offsets[a.E]), uint32_t(run));
+        }
+        if (++tile == a.nTiles) {
+            tile = 0;
+            ++e;
         }
     }
     // expert_offsets (agent-coherent) complete before this workgroup's next
@@ -816,6 +887,7 @@ __device__ void do_combine(const FusedArgs& a, int item, uint64_t epoch, int* sh
 template <int KC>
 __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs a) {
     __shared__ int32_t hist[kWavesPerBlock][kMaxE];
+    __shared__ int sh_tot[kMaxE];
     __shared__ int sh_pos[kMaxItemPicks];
     __shared__ int sh_wave_total[kWavesPerBlock];
     __shared__ int sh_word[2];
@@ -840,7 +912,10 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs a) {
         __syncthreads();
         ticket = __builtin_amdgcn_readfirstlane(sh_ticket);
         if (ticket >= total) break;
-        if (ticket < first_scan) do_hist(a, ticket, hist);
+        if (ticket < first_scan) {
+            if (a.nScan == 0) do_layout1(a, uint32_t(epoch), hist, sh_tot, sh_wave_total);
+            else do_hist(a, ticket, hist);
+        }
         else if (ticket < first_scatter) do_scan(a, ticket - first_scan, uint32_t(epoch), sh_wave_total, sh_word);
         else if (ticket < first_combine) do_scatter(a, ticket - first_scatter, epoch, sh_pos, sh_word);
         else do_combine<KC>(a, ticket - first_combine, epoch, sh_pos, sh_word);
@@ -962,7 +1037,8 @@ hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float*
     a.S = f.lay.S;
     a.nTiles = f.lay.nTiles;
     a.nCnt = f.lay.nCnt;
-    a.nScan = (f.lay.nCnt + kFusedScanItems - 1) / kFusedScanItems;   // <= f.lay.nScan
+    // one tile: its item scans the counts itself (no scan items)
+    a.nScan = f.lay.nTiles == 1 ? 0 : (f.lay.nCnt + kFusedScanItems - 1) / kFusedScanItems;
     a.nScat = (T + kScatTok - 1) / kScatTok;
     a.nComb = (T + kCombTok - 1) / kCombTok;
     a.stride = int64_t(fused_row_stride(H));

@@ -123,14 +123,22 @@ __global__ __launch_bounds__(kBlock) void layout_scan_kernel(
     __syncthreads();
 
     int run = sh_exclusive + bs.thread_excl;
+    // counter i is (expert i / nTiles, tile i % nTiles): one division per
+    // thread, then the tile steps along
+    int e = bs.i0 / nTiles;
+    int tile = bs.i0 - e * nTiles;
 #pragma unroll
     for (int q = 0; q < BlockScan<kScanItems>::kPer; ++q) {
         const int i = bs.i0 + q;
         if (i < nCnt) {
             base[i] = run;
-            if (i % nTiles == 0) expert_offsets[i / nTiles] = run;
+            if (tile == 0) expert_offsets[e] = run;
             run += bs.v[q];
             if (i == nCnt - 1) expert_offsets[E] = run;
+        }
+        if (++tile == nTiles) {
+            tile = 0;
+            ++e;
         }
     }
 }
