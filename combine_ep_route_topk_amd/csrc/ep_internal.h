@@ -44,6 +44,12 @@ constexpr int kRedundantScanMax = 32768;
 // Counters per scan item of the persistent fused mode: one item covers the
 // 8192 counters of a T=4096, k=8, E=256 layout, so its look-back chain is empty.
 constexpr int kFusedScanItems = 8192;
+// Most parts a small batch's rows are split into in the fused mode's
+// item-event readiness (so that its few tokens still spread over the GPU).
+#ifndef EP_FUSED_MAX_PARTS
+#define EP_FUSED_MAX_PARTS 4
+#endif
+constexpr int kFusedMaxParts = EP_FUSED_MAX_PARTS;
 constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 // Cap on the 1-D grid of the row kernels, which stride over their items.
@@ -121,7 +127,8 @@ struct FusedPlan {
     LayoutPlan lay;
     size_t off_status64;  // u64 [nScan]  (epoch32 << 32 | flag << 30 | value)
     size_t off_fbase;     // u64 [nCnt]   (epoch32 << 32 | base) published bases
-    size_t off_sdone;     // u64 [ceil(T/2)] epoch of the call once a scatter item is done
+    size_t off_sdone;     // u64 [ceil(T/2) * kFusedMaxParts] epoch of the call once a
+                          //     scatter item (or one part of it) is done
     size_t bytes;
 };
 
@@ -131,7 +138,8 @@ inline FusedPlan fused_plan(int T, int k, int E) {
     size_t off = f.lay.bytes;
     f.off_status64 = off; off += align256(sizeof(uint64_t) * f.lay.nScan);
     f.off_fbase = off;    off += align256(sizeof(uint64_t) * f.lay.nCnt);
-    f.off_sdone = off;    off += align256(sizeof(uint64_t) * ((size_t(T) + 1) / 2));
+    f.off_sdone = off;
+    off += align256(sizeof(uint64_t) * ((size_t(T) + 1) / 2) * kFusedMaxParts);
     f.bytes = off;
     return f;
 }

@@ -38,6 +38,9 @@
 //             barrier each wave reduces one token's k rows with the same fp32
 //             arithmetic as ep_combine, up to kCombBatch row segments before
 //             it stores any of them.
+//   A batch with fewer scatter items than workgroups splits the rows of each
+//   scatter and combine item into parts (item-event mode; an event word per
+//   part), so that its few tokens still spread over the GPU.
 // A row's trailer is its flag: on gfx950 a 64-bit aligned store is
 // single-copy atomic but a 14 KiB row is not, hence payload -> release ->
 // trailer, and trailer -> acquire -> payload on the reading side.  An
@@ -89,6 +92,7 @@ struct FusedArgs {
     int T, k, E, R, nvec;
     int64_t S;
     int nTiles, nCnt, nScan, nScat, nComb;
+    int parts;                            // row parts per scatter / combine item (item events)
     int64_t stride;                       // bytes per send row (payload + trailer + pad)
     int64_t trailer_off;                  // = 2H
     int32_t* expert_counts;
@@ -449,7 +453,7 @@ __device__ __noinline__ void scatter_tail(const char* __restrict__ src, char* __
     }
 }
 
-__device__ void do_scatter(const FusedArgs& a, int item, uint64_t epoch, int* sh_pos,
+__device__ void do_scatter(const FusedArgs& a, int item, int part, uint64_t epoch, int* sh_pos,
                            int* sh_word)
 {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -463,10 +467,35 @@ __device__ void do_scatter(const FusedArgs& a, int item, uint64_t epoch, int* sh
     __syncthreads();
     if (!__builtin_amdgcn_readfirstlane(sh_word[0])) return;
 
+    if (a.parts > 1) {
+        // one part of each row: 64-vector chunks [c0, c0 + nc) of both
+        // tokens, a chunk per wave at a time (one load, k stores per lane)
+        const int nchunk = (a.nvec + kWave - 1) / kWave;
+        const int c0 = part * nchunk / a.parts;
+        const int nc = (part + 1) * nchunk / a.parts - c0;
+        char* rows = reinterpret_cast<char*>(a.send_rows);
+        for (int q = wave; q < kScatTok * nc; q += kWavesPerBlock) {
+            const int i = q / nc;
+            const int t = t0 + i;
+            if (t >= a.T) break;
+            const int vi = (c0 + q % nc) * kWave + lane;
+            const int* prow = sh_pos + i * a.k;
+            if (vi < a.nvec) {
+                const u32x4 v =
+                    load16(reinterpret_cast<const char*>(a.x) + (int64_t(t) * a.nvec + vi) * 16);
+                for (int j = 0; j < a.k; ++j) {
+                    const int p = prow[j];         // lanes may have left: no wave op here
+                    if (p >= 0)
+                        store16_coherent(buffer_rsrc(rows + int64_t(p) * a.stride, a.stride),
+                                         vi * 16, v);
+                }
+            }
+        }
+    }
     // payload: waves 2i and 2i+1 copy token t0 + i, alternating row segments
     const int i = wave >> 1;
     const int t = t0 + i;
-    if (t < a.T) {
+    if (a.parts == 1 && t < a.T) {
         const char* src = reinterpret_cast<const char*>(a.x) + int64_t(t) * a.nvec * 16;
         const int* prow = sh_pos + i * a.k;
         for (int seg = wave & 1; seg * kSegVec < a.nvec; seg += 2) {
@@ -559,23 +588,27 @@ __device__ void do_scatter(const FusedArgs& a, int item, uint64_t epoch, int* sh
         return;
     }
     // item events / row flags: pos, trailer tails (agent-coherent), then the
-    // epochs
+    // epochs.  With row parts every part stores pos (the same values), and
+    // part 0 the trailers.
     for (int q = lane; q < npick; q += kWave) {
         const int64_t s = s0 + q;
         if (s >= a.S) break;
         const int p = sh_pos[q];
         st_relaxed(reinterpret_cast<uint32_t*>(&a.pos[s]), uint32_t(p));
-        if (p >= 0) st_relaxed64(trailer(a, p) + 1, uint64_t(uint32_t(s)));
+        if (part == 0 && p >= 0) st_relaxed64(trailer(a, p) + 1, uint64_t(uint32_t(s)));
     }
     wait_own_stores();                     // pos and trailer tails before the flags
-    for (int q = lane; q < npick; q += kWave) {
-        const int64_t s = s0 + q;
-        if (s >= a.S) break;
-        const int p = sh_pos[q];
-        if (p >= 0) st_relaxed64(trailer(a, p), epoch);
+    if (part == 0) {
+        for (int q = lane; q < npick; q += kWave) {
+            const int64_t s = s0 + q;
+            if (s >= a.S) break;
+            const int p = sh_pos[q];
+            if (p >= 0) st_relaxed64(trailer(a, p), epoch);
+        }
     }
-    // the item's event word: its pos entries are final
-    if (a.sync == kSyncItemEvents && lane == 0) st_relaxed64(&a.sdone[item], tag);
+    // the item's (part's) event word: its pos entries and its part of the
+    // rows are final
+    if (a.sync == kSyncItemEvents && lane == 0) st_relaxed64(&a.sdone[item * a.parts + part], tag);
 }
 
 // ---------------------------------------------------------------- combine item
@@ -779,7 +812,7 @@ __device__ bool rows_ready(const FusedArgs& a, int t0, const int (&p)[kPickRound
 }
 
 template <int KC>
-__device__ void do_combine(const FusedArgs& a, int item, uint64_t epoch, int* sh_pos,
+__device__ void do_combine(const FusedArgs& a, int item, int part, uint64_t epoch, int* sh_pos,
                            int* sh_word)
 {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -804,7 +837,8 @@ __device__ void do_combine(const FusedArgs& a, int item, uint64_t epoch, int* sh
         Waiter wt0;
         while (true) {
             const uint64_t tag = uint64_t(uint32_t(epoch)) << 32;
-            const bool mine = lane < nsc ? ld_relaxed64(&a.sdone[sfirst + lane]) == tag : true;
+            const bool mine =
+                lane < nsc ? ld_relaxed64(&a.sdone[(sfirst + lane) * a.parts + part]) == tag : true;
             if (ballot(!mine) == 0) break;
             if (!wt0.tick(a.hdr, a.spin_limit)) {
                 ok = false;
@@ -814,15 +848,17 @@ __device__ void do_combine(const FusedArgs& a, int item, uint64_t epoch, int* sh
         int p[kPickRounds];
         if (ok) {
             fence_acquire();               // the pos entries of those items
-            // 2. positions of the item's picks, from pos
+            // 2. positions of the item's picks, from pos (every load from a
+            //    clamped in-bounds slot, so the rounds' loads go out together)
             const int npick = kCombTok * a.k;
             const int64_t s0 = int64_t(t0) * a.k;
 #pragma unroll
             for (int r = 0; r < kPickRounds; ++r) {
                 const int q = r * kWave + lane;
                 const int64_t s = s0 + q;
-                int pr = (q < npick && s < a.S) ? a.pos[s] : -1;
-                if (uint64_t(uint32_t(pr)) >= uint64_t(a.S)) pr = -1;   // never address outside the rows
+                const bool in = q < npick && s < a.S;
+                int pr = a.pos[in ? s : 0];
+                if (!in || uint64_t(uint32_t(pr)) >= uint64_t(a.S)) pr = -1;   // never address outside the rows
                 p[r] = pr;
                 if (q < npick) sh_pos[q] = pr;
             }
@@ -860,8 +896,9 @@ __device__ void do_combine(const FusedArgs& a, int item, uint64_t epoch, int* sh
     for (int j = 0; j < (KC > 0 ? KC : 1); ++j)
         pj[j] = KC > 0 ? __builtin_amdgcn_readfirstlane(prow[j]) : 0;
     if constexpr (KC > 0 && kWpt == 1) {
-        // rows known complete (not the per-chunk mode) and every pick inside
-        bool inside = a.sync != kSyncChunkFlag;
+        // rows known complete (not the per-chunk mode), whole rows and every
+        // pick inside
+        bool inside = a.sync != kSyncChunkFlag && a.parts == 1;
 #pragma unroll
         for (int j = 0; j < KC; ++j) inside = inside && uint32_t(pj[j]) < uint32_t(a.S);
         if (inside) {
@@ -869,7 +906,11 @@ __device__ void do_combine(const FusedArgs& a, int item, uint64_t epoch, int* sh
             return;
         }
     }
-    for (int v0 = (wave % kWpt) * kWave + lane; v0 - lane < a.nvec; v0 += kWpt * kWave) {
+    // the item's part of the row: 64-vector chunks [c0, c1)
+    const int nchunk = (a.nvec + kWave - 1) / kWave;
+    const int c0 = part * nchunk / a.parts;
+    const int c1 = (part + 1) * nchunk / a.parts;
+    for (int v0 = (c0 + wave % kWpt) * kWave + lane; v0 - lane < c1 * kWave; v0 += kWpt * kWave) {
         if (a.sync == kSyncChunkFlag && !chunk_ready(a, prow, k, (v0 - lane) / kWave, epoch))
             return;
         const bool coh = a.sync == kSyncChunkFlag;
@@ -896,8 +937,8 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs a) {
     const uint64_t epoch = a.hdr->epoch;          // constant during the call
     const int first_scan = a.nTiles;
     const int first_scatter = first_scan + a.nScan;
-    const int first_combine = first_scatter + a.nScat;
-    const int total = first_combine + a.nComb;
+    const int first_combine = first_scatter + a.nScat * a.parts;
+    const int total = first_combine + a.nComb * a.parts;
 
     // The barrier opens each round, BEFORE thread 0 claims the ticket: a
     // divergent thread-0 block must never follow another one (the end of a
@@ -917,8 +958,13 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs a) {
             else do_hist(a, ticket, hist);
         }
         else if (ticket < first_scatter) do_scan(a, ticket - first_scan, uint32_t(epoch), sh_wave_total, sh_word);
-        else if (ticket < first_combine) do_scatter(a, ticket - first_scatter, epoch, sh_pos, sh_word);
-        else do_combine<KC>(a, ticket - first_combine, epoch, sh_pos, sh_word);
+        else if (ticket < first_combine) {
+            const int u = ticket - first_scatter;
+            do_scatter(a, u / a.parts, u % a.parts, epoch, sh_pos, sh_word);
+        } else {
+            const int u = ticket - first_combine;
+            do_combine<KC>(a, u / a.parts, u % a.parts, epoch, sh_pos, sh_word);
+        }
     }
 
     // Every workgroup makes exactly one claim past the last item, after all
@@ -1069,8 +1115,21 @@ hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float*
 
     const void* kern = k == 8 ? reinterpret_cast<const void*>(&fused_kernel<8>)
                               : reinterpret_cast<const void*>(&fused_kernel<0>);
-    const int items = a.nTiles + a.nScan + a.nScat + a.nComb;
     int g = grid > 0 ? grid : resident_grid(kern);
+    // Row parts: a batch with fewer scatter items than workgroups splits each
+    // item's rows into parts (64-vector chunks), so its few tokens still
+    // spread over the GPU -- at T = 128 two-token items would keep 64
+    // workgroups busy, and one workgroup moves only ~30-40 GB/s of scattered
+    // rows.  Item-event readiness only: each part has its own event word.
+    a.parts = 1;
+    if (sync == kSyncItemEvents && a.nScat < g) {
+        const int nchunk = (a.nvec + kWave - 1) / kWave;
+        int P = (g + a.nScat - 1) / a.nScat;
+        if (P > kFusedMaxParts) P = kFusedMaxParts;
+        if (P > nchunk) P = nchunk;
+        a.parts = P;
+    }
+    const int items = a.nTiles + a.nScan + (a.nScat + a.nComb) * a.parts;
     if (g > items) g = items;
     if (k == 8)
         EP_LAUNCH((fused_kernel<8>), dim3(g), dim3(kBlock), 0, s, a);

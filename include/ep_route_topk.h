@@ -363,7 +363,9 @@ ep_status ep_fused_last_epoch(const void* workspace, uint64_t* epoch, void* stre
  *               drains.
  *   sync = EP_FUSED_SYNC_ITEM_EVENTS (0): ep_fused_dispatch_combine's mode.
  *          Combine waits for the event words of the scatter items of its
- *          tokens, reads pos, then checks each row's trailer.
+ *          tokens, reads pos, then checks each row's trailer.  A batch with
+ *          fewer scatter items than resident workgroups splits every item's
+ *          rows into parts, each with its own event word.
  *   sync = EP_FUSED_SYNC_ROW_FLAG (1): combine derives its positions from
  *          the published bases and polls each row's 16-byte trailer
  *          {epoch, slot_src} (Token-Flag Fusion at row granularity).

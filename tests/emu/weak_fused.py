@@ -27,10 +27,11 @@ sys.path.insert(0, ROOT)
 import oracle  # noqa: E402
 from combine_ep_route_topk_amd import workloads as wl  # noqa: E402
 
-# T, H, E, R, k, seed (the last: k = 8 rows of 7 whole 64-vector segments, which the combine side
-# reduces as one batch behind the acquire)
+# T, H, E, R, k, seed (the fourth: k = 8 rows of 7 whole 64-vector segments, which the combine side
+# reduces as one batch behind the acquire; the last: 3 scatter items for the emulation's 8
+# workgroups, so in item-event mode each row is split into 3 parts with an event word each)
 SHAPES = [(128, 256, 8, 2, 2, 1001), (600, 64, 256, 32, 8, 5), (130, 7176, 64, 8, 6, 4),
-          (48, 3584, 16, 4, 8, 7)]
+          (48, 3584, 16, 4, 8, 7), (6, 3584, 16, 4, 8, 8)]
 MODES = (0, 1, 2, 3, 4)
 SPIN_LIMIT = 4096
 

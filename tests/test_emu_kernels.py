@@ -120,6 +120,10 @@ SHAPES = [
     (3000, 24, 33, 3, 5, 7),        # fifteen tiles, odd E
     (2560, 16, 1024, 8, 8, 8),      # 20480 counters: bases in the positions launch; fused: three scan items
     (4608, 8, 1024, 8, 8, 9),       # 36864 counters: separate scan launch with look-back; fused: five
+    # fewer scatter items than the emulation's 8 workgroups: the fused mode
+    # splits the rows into parts (3 parts of 7 chunks; 4 parts of 15, ragged)
+    (6, 3584, 16, 4, 8, 10),
+    (3, 7176, 64, 8, 6, 11),
 ]
 
 
@@ -159,12 +163,15 @@ def test_emulated_kernels_match_oracle(emu, T, H, E, R, k, seed):
     assert np.array_equal(m.out, x), "fused combine"
 
 
-@pytest.mark.parametrize("T,H", [(200, 520), (64, 3584), (40, 7176), (40, 8192)])
+@pytest.mark.parametrize("T,H", [(200, 520), (64, 3584), (40, 7176), (40, 8192),
+                                 (6, 3584), (3, 7176), (13, 8192)])
 def test_emulated_fused_random_experts_equals_combine(emu, T, H):
     """Non-uniform weights: the fused reduction is bit-identical to ep_combine
     over the same rows (they share the arithmetic) and to the oracle's fp32
     chain.  Rows of 1, 7, 14 (plus a partial segment) and 16 whole 64-vector
-    segments: one full batch of 14 segments, a short batch, and both."""
+    segments: one full batch of 14 segments, a short batch, and both.  The
+    last three batches have fewer scatter items than the emulation's 8
+    workgroups, so their rows are split into 3, 4 and 2 parts."""
     E, R, k = 16, 4, 8
     rng = np.random.default_rng(11)
     o_idx, _ = oracle.route_topk(rng.standard_normal((T, E), dtype=np.float32), k, 1)
