@@ -243,8 +243,13 @@ __device__ __forceinline__ void scatter_whole(const char* __restrict__ g_row,
         const float w = wrow[j];
         const __amdgpu_buffer_rsrc_t row = buffer_rsrc(gyb + int64_t(p) * row_bytes, row_bytes);
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            store16_coherent(row, int(lane_off) + u * kWave * 16, scaled(g[u], w));
+        for (int u = 0; u < U; ++u) {
+            // a small batch (U == 1) keeps its rows in the caches for the
+            // dispatch_grad that reads them next
+            const int off = int(lane_off) + u * kWave * 16;
+            if constexpr (U == 1) store16_coherent_keep(row, off, scaled(g[u], w));
+            else store16_coherent(row, off, scaled(g[u], w));
+        }
     }
 }
 
@@ -253,7 +258,7 @@ __device__ __noinline__ void scatter_tail(const char* __restrict__ g_row,
                                           char* __restrict__ gyb, int64_t row_bytes,
                                           const int32_t* __restrict__ prow,
                                           const float* __restrict__ wrow, int k, uint32_t S,
-                                          int v0, int U, int nvec)
+                                          int v0, int U, int nvec, bool keep)
 {
     for (int u = 0; u < U; ++u) {
         const int vi = v0 + u * kWave;
@@ -266,7 +271,11 @@ __device__ __noinline__ void scatter_tail(const char* __restrict__ g_row,
             const int32_t p = prow[j];
             if (uint32_t(p) >= S) continue;
             const u32x4 o = scaled(g, wrow[j]);      // every lane: scaled() votes
-            if (lane_ok) store16_nt(gyb + int64_t(p) * row_bytes + int64_t(vi) * 16, o);
+            char* d = gyb + int64_t(p) * row_bytes + int64_t(vi) * 16;
+            if (lane_ok) {
+                if (keep) store16(d, o);
+                else store16_nt(d, o);
+            }
         }
     }
 }
@@ -295,7 +304,7 @@ __global__ __launch_bounds__(kBlock) void combine_grad_scatter_kernel(
         if ((seg + 1) * kWave * U <= nvec)
             scatter_whole<U>(g_row, gyb, row_bytes, prow, wrow, k, S, v0);
         else
-            scatter_tail(g_row, gyb, row_bytes, prow, wrow, k, S, v0, U, nvec);
+            scatter_tail(g_row, gyb, row_bytes, prow, wrow, k, S, v0, U, nvec, U == 1);
     }
 }
 

@@ -42,16 +42,21 @@ __device__ __forceinline__ void copy_whole(const char* __restrict__ src,
         if (uint32_t(p) >= S) continue;
         const __amdgpu_buffer_rsrc_t row = buffer_rsrc(send + int64_t(p) * row_bytes, row_bytes);
 #pragma unroll
-        for (int u = 0; u < U; ++u) store16_coherent(row, int(lane_off) + u * kWave * 16, v[u]);
+        for (int u = 0; u < U; ++u) {
+            // a small batch (U == 1) keeps its rows in the caches for the
+            // combine that reads them next
+            if constexpr (U == 1) store16_coherent_keep(row, int(lane_off) + u * kWave * 16, v[u]);
+            else store16_coherent(row, int(lane_off) + u * kWave * 16, v[u]);
+        }
     }
 }
 
-// The last, partial segment of a row: one vector at a time (plain streaming
-// stores: a descriptor built from this function's non-uniform arguments
-// would cost a loop over the lanes).
+// The last, partial segment of a row: one vector at a time (plain stores,
+// streaming unless `keep`: a descriptor built from this function's
+// non-uniform arguments would cost a loop over the lanes).
 __device__ __noinline__ void copy_tail(const char* __restrict__ src, char* __restrict__ send,
                                        int64_t row_bytes, const int32_t* __restrict__ prow,
-                                       int k, uint32_t S, int v0, int U, int nvec)
+                                       int k, uint32_t S, int v0, int U, int nvec, bool keep)
 {
     for (int u = 0; u < U; ++u) {
         const int vi = v0 + u * kWave;
@@ -59,7 +64,10 @@ __device__ __noinline__ void copy_tail(const char* __restrict__ src, char* __res
         const u32x4 v = load16(src + int64_t(vi) * 16);
         for (int j = 0; j < k; ++j) {
             const int32_t p = prow[j];
-            if (uint32_t(p) < S) store16_nt(send + int64_t(p) * row_bytes + int64_t(vi) * 16, v);
+            if (uint32_t(p) >= S) continue;
+            char* d = send + int64_t(p) * row_bytes + int64_t(vi) * 16;
+            if (keep) store16(d, v);
+            else store16_nt(d, v);
         }
     }
 }
@@ -96,7 +104,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(
         if ((seg + 1) * kWave * U <= nvec)
             copy_whole<U>(src, dst, row_bytes, prow, k, S, v0);
         else
-            copy_tail(src, dst, row_bytes, prow, k, S, v0, U, nvec);
+            copy_tail(src, dst, row_bytes, prow, k, S, v0, U, nvec, U == 1);
     }
 }
 

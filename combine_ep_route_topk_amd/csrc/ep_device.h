@@ -61,6 +61,13 @@ constexpr int kCpolNtSc1 = 2 | 16;
 __device__ __forceinline__ void store16_coherent(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolNtSc1);
 }
+// The same store without the streaming hint: still written through at agent
+// scope, but the line may stay in the caches for a reader that comes soon
+// (a small batch whose rows the next kernel reads while they still fit).
+constexpr int kCpolSc1 = 16;
+__device__ __forceinline__ void store16_coherent_keep(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCpolSc1);
+}
 // 16-byte load with the same bits: served at agent scope (it sees every
 // store from any XCD that has completed) and not kept in this XCD's L2, so
 // no L2 invalidate (acquire fence) is needed before it.  The descriptor's
