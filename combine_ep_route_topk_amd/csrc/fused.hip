@@ -483,11 +483,13 @@ __device__ void do_scatter(const FusedArgs& a, int item, int part, uint64_t epoc
             if (vi < a.nvec) {
                 const u32x4 v =
                     load16(reinterpret_cast<const char*>(a.x) + (int64_t(t) * a.nvec + vi) * 16);
+                // a small batch: the rows stay in the caches for the combine
+                // items that read them soon after
                 for (int j = 0; j < a.k; ++j) {
                     const int p = prow[j];         // lanes may have left: no wave op here
                     if (p >= 0)
-                        store16_coherent(buffer_rsrc(rows + int64_t(p) * a.stride, a.stride),
-                                         vi * 16, v);
+                        store16_coherent_keep(buffer_rsrc(rows + int64_t(p) * a.stride, a.stride),
+                                              vi * 16, v);
                 }
             }
         }
