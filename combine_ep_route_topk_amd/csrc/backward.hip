@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kBlock) void combine_grad_dot_kernel(
 // One (token, segment) item whose vectors all lie inside the row: U loads
 // per lane, then per pick U scaled vectors stored through a descriptor over
 // the destination row (streaming, agent-coherent).
-template <int U>
+template <int U, bool KEEP>
 __device__ __forceinline__ void scatter_whole(const char* __restrict__ g_row,
                                               char* __restrict__ gyb, int64_t row_bytes,
                                               const int32_t* __restrict__ prow,
@@ -244,10 +244,9 @@ __device__ __forceinline__ void scatter_whole(const char* __restrict__ g_row,
         const __amdgpu_buffer_rsrc_t row = buffer_rsrc(gyb + int64_t(p) * row_bytes, row_bytes);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            // a small batch (U == 1) keeps its rows in the caches for the
-            // dispatch_grad that reads them next
+            // KEEP: rows that dispatch_grad reads next while still cached
             const int off = int(lane_off) + u * kWave * 16;
-            if constexpr (U == 1) store16_coherent_keep(row, off, scaled(g[u], w));
+            if constexpr (KEEP) store16_coherent_keep(row, off, scaled(g[u], w));
             else store16_coherent(row, off, scaled(g[u], w));
         }
     }
@@ -282,7 +281,7 @@ __device__ __noinline__ void scatter_tail(const char* __restrict__ g_row,
 
 // Items are (group of 4 tokens, row segment of kWave*U vectors), one wave per
 // token, numbered segment-fastest, as in dispatch.
-template <int U>
+template <int U, bool KEEP>
 __global__ __launch_bounds__(kBlock) void combine_grad_scatter_kernel(
     const uint16_t* __restrict__ grad_out, const int32_t* __restrict__ pos,
     const float* __restrict__ w, int T, int nvec, int k, uint16_t* __restrict__ grad_y,
@@ -302,15 +301,16 @@ __global__ __launch_bounds__(kBlock) void combine_grad_scatter_kernel(
         const float* wrow = w + int64_t(t) * k;
         const int v0 = seg * kWave * U + lane_id();
         if ((seg + 1) * kWave * U <= nvec)
-            scatter_whole<U>(g_row, gyb, row_bytes, prow, wrow, k, S, v0);
+            scatter_whole<U, KEEP>(g_row, gyb, row_bytes, prow, wrow, k, S, v0);
         else
-            scatter_tail(g_row, gyb, row_bytes, prow, wrow, k, S, v0, U, nvec, U == 1);
+            scatter_tail(g_row, gyb, row_bytes, prow, wrow, k, S, v0, U, nvec, KEEP);
     }
 }
 
 template <int U>
 hipError_t launch_scatter(const uint16_t* grad_out, const int32_t* pos, const float* w, int T,
-                          int nvec, int k, uint16_t* grad_y, uint32_t cap, hipStream_t s)
+                          int nvec, int k, uint16_t* grad_y, uint32_t cap, bool keep,
+                          hipStream_t s)
 {
     const uint32_t segs = uint32_t((nvec + kWave * U - 1) / (kWave * U));
     const uint32_t items = uint32_t((T + kWavesPerBlock - 1) / kWavesPerBlock) * segs;
@@ -318,8 +318,12 @@ hipError_t launch_scatter(const uint16_t* grad_out, const int32_t* pos, const fl
     // smallest grid that keeps that many rounds: no nearly idle last round
     const uint32_t rounds = (items + cap - 1) / cap;
     const uint32_t grid = (items + rounds - 1) / rounds;
-    EP_LAUNCH((combine_grad_scatter_kernel<U>), dim3(grid), dim3(kBlock), 0, s, grad_out, pos, w,
-              T, nvec, k, grad_y, segs, items);
+    if (keep)
+        EP_LAUNCH((combine_grad_scatter_kernel<U, true>), dim3(grid), dim3(kBlock), 0, s, grad_out,
+                  pos, w, T, nvec, k, grad_y, segs, items);
+    else
+        EP_LAUNCH((combine_grad_scatter_kernel<U, false>), dim3(grid), dim3(kBlock), 0, s, grad_out,
+                  pos, w, T, nvec, k, grad_y, segs, items);
     return hipGetLastError();
 }
 
@@ -355,13 +359,17 @@ hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* y,
     // 179 us (48 busy), 208 172.3-173.8 us (10 rounds, 176 busy), 216 176 us,
     // 224 176.7-176.9 us (32 busy)).
     // a small batch: one vector per lane on an uncapped grid, as in dispatch
+    const bool keep = keep_rows(T, H, k);
     if (small_scatter(T, H, k))
-        return launch_scatter<1>(grad_out, pos, w, T, nvec, k, grad_y, kMaxGrid, s);
+        return launch_scatter<1>(grad_out, pos, w, T, nvec, k, grad_y, kMaxGrid, keep, s);
     const uint32_t cap = dispatch_grid_cap() * 13 / 8;
-    if (nvec % (kWave * 7) == 0) return launch_scatter<7>(grad_out, pos, w, T, nvec, k, grad_y, cap, s);
-    if (nvec >= kWave * 8) return launch_scatter<8>(grad_out, pos, w, T, nvec, k, grad_y, cap, s);
-    if (nvec >= kWave * 4) return launch_scatter<4>(grad_out, pos, w, T, nvec, k, grad_y, cap, s);
-    return launch_scatter<1>(grad_out, pos, w, T, nvec, k, grad_y, cap, s);
+    if (nvec % (kWave * 7) == 0)
+        return launch_scatter<7>(grad_out, pos, w, T, nvec, k, grad_y, cap, keep, s);
+    if (nvec >= kWave * 8)
+        return launch_scatter<8>(grad_out, pos, w, T, nvec, k, grad_y, cap, keep, s);
+    if (nvec >= kWave * 4)
+        return launch_scatter<4>(grad_out, pos, w, T, nvec, k, grad_y, cap, keep, s);
+    return launch_scatter<1>(grad_out, pos, w, T, nvec, k, grad_y, cap, keep, s);
 }
 
 }  // namespace ep

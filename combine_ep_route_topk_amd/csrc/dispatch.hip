@@ -26,8 +26,9 @@ namespace {
 constexpr int kWavesPerBlock = kBlock / kWave;
 
 // One (token, segment) item whose vectors all lie inside the row: U loads
-// per lane, then U stores per pick, no per-vector checks.
-template <int U>
+// per lane, then U stores per pick, no per-vector checks.  KEEP: the stores
+// drop the streaming hint (rows the next kernel reads while still cached).
+template <int U, bool KEEP>
 __device__ __forceinline__ void copy_whole(const char* __restrict__ src,
                                            char* __restrict__ send, int64_t row_bytes,
                                            const int32_t* __restrict__ prow, int k,
@@ -43,9 +44,7 @@ __device__ __forceinline__ void copy_whole(const char* __restrict__ src,
         const __amdgpu_buffer_rsrc_t row = buffer_rsrc(send + int64_t(p) * row_bytes, row_bytes);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            // a small batch (U == 1) keeps its rows in the caches for the
-            // combine that reads them next
-            if constexpr (U == 1) store16_coherent_keep(row, int(lane_off) + u * kWave * 16, v[u]);
+            if constexpr (KEEP) store16_coherent_keep(row, int(lane_off) + u * kWave * 16, v[u]);
             else store16_coherent(row, int(lane_off) + u * kWave * 16, v[u]);
         }
     }
@@ -84,7 +83,7 @@ __device__ __noinline__ void copy_tail(const char* __restrict__ src, char* __res
 // whole route/layout/dispatch/combine step 205.5-207.2 -> 199.4-202.1 us).
 // Rows at or past S (T*k, or a smaller receive buffer's row count) are never
 // written.
-template <int U>
+template <int U, bool KEEP>
 __global__ __launch_bounds__(kBlock) void dispatch_kernel(
     const uint16_t* __restrict__ x, int T, int nvec, int k,
     const int32_t* __restrict__ pos, uint16_t* __restrict__ send,
@@ -102,15 +101,15 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(
         const int32_t* prow = pos + int64_t(t) * k;
         const int v0 = seg * kWave * U + lane_id();
         if ((seg + 1) * kWave * U <= nvec)
-            copy_whole<U>(src, dst, row_bytes, prow, k, S, v0);
+            copy_whole<U, KEEP>(src, dst, row_bytes, prow, k, S, v0);
         else
-            copy_tail(src, dst, row_bytes, prow, k, S, v0, U, nvec, U == 1);
+            copy_tail(src, dst, row_bytes, prow, k, S, v0, U, nvec, KEEP);
     }
 }
 
-template <int U>
-hipError_t launch_u(const uint16_t* x, int T, int nvec, int k, const int32_t* pos,
-                    uint16_t* send, uint32_t cap, uint32_t bound, hipStream_t s)
+template <int U, bool KEEP>
+hipError_t launch_uk(const uint16_t* x, int T, int nvec, int k, const int32_t* pos,
+                     uint16_t* send, uint32_t cap, uint32_t bound, hipStream_t s)
 {
     const uint32_t segs = uint32_t((nvec + kWave * U - 1) / (kWave * U));
     const uint32_t items = uint32_t((T + kWavesPerBlock - 1) / kWavesPerBlock) * segs;
@@ -118,9 +117,17 @@ hipError_t launch_u(const uint16_t* x, int T, int nvec, int k, const int32_t* po
     // smallest grid that keeps that many rounds: no nearly idle last round
     const uint32_t rounds = (items + cap - 1) / cap;
     const uint32_t grid = (items + rounds - 1) / rounds;
-    EP_LAUNCH((dispatch_kernel<U>), dim3(grid), dim3(kBlock), 0, s, x, T, nvec, k, pos,
+    EP_LAUNCH((dispatch_kernel<U, KEEP>), dim3(grid), dim3(kBlock), 0, s, x, T, nvec, k, pos,
               send, segs, items, bound);
     return hipGetLastError();
+}
+
+template <int U>
+hipError_t launch_u(const uint16_t* x, int T, int nvec, int k, const int32_t* pos,
+                    uint16_t* send, uint32_t cap, uint32_t bound, bool keep, hipStream_t s)
+{
+    return keep ? launch_uk<U, true>(x, T, nvec, k, pos, send, cap, bound, s)
+                : launch_uk<U, false>(x, T, nvec, k, pos, send, cap, bound, s);
 }
 
 }  // namespace
@@ -149,6 +156,11 @@ bool small_scatter(int T, int H, int k)
     return int64_t(T) * k * H * 2 <= kSmallScatterBytes;
 }
 
+bool keep_rows(int T, int H, int k)
+{
+    return int64_t(T) * k * H * 2 <= kKeepRowsBytes;
+}
+
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int k, const int32_t* pos,
                            uint16_t* send, hipStream_t s)
 {
@@ -162,13 +174,14 @@ hipError_t launch_dispatch_bounded(const uint16_t* x, int T, int H, int k, const
     // A small batch is bound by latency, not by the write path: one vector per
     // lane and an uncapped grid put the most requests in flight (measured on
     // MI355X at T=128, H=7168, k=8: 8.2 -> 5.0 us).
+    const bool keep = keep_rows(T, H, k);
     if (small_scatter(T, H, k))
-        return launch_u<1>(x, T, nvec, k, pos, send, kMaxGrid, bound, s);
+        return launch_u<1>(x, T, nvec, k, pos, send, kMaxGrid, bound, keep, s);
     const uint32_t cap = dispatch_grid_cap();
-    if (nvec % (kWave * 7) == 0) return launch_u<7>(x, T, nvec, k, pos, send, cap, bound, s);
-    if (nvec >= kWave * 8) return launch_u<8>(x, T, nvec, k, pos, send, cap, bound, s);
-    if (nvec >= kWave * 4) return launch_u<4>(x, T, nvec, k, pos, send, cap, bound, s);
-    return launch_u<1>(x, T, nvec, k, pos, send, cap, bound, s);
+    if (nvec % (kWave * 7) == 0) return launch_u<7>(x, T, nvec, k, pos, send, cap, bound, keep, s);
+    if (nvec >= kWave * 8) return launch_u<8>(x, T, nvec, k, pos, send, cap, bound, keep, s);
+    if (nvec >= kWave * 4) return launch_u<4>(x, T, nvec, k, pos, send, cap, bound, keep, s);
+    return launch_u<1>(x, T, nvec, k, pos, send, cap, bound, keep, s);
 }
 
 }  // namespace ep
