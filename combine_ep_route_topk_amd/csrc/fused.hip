@@ -93,6 +93,7 @@ struct FusedArgs {
     int64_t S;
     int nTiles, nCnt, nScan, nScat, nComb;
     int parts;                            // row parts per scatter / combine item (item events)
+    int keep;                             // row stores without the streaming hint (small batches)
     int64_t stride;                       // bytes per send row (payload + trailer + pad)
     int64_t trailer_off;                  // = 2H
     int32_t* expert_counts;
@@ -427,10 +428,17 @@ __device__ __forceinline__ void scatter_whole(const char* __restrict__ src, cons
         const int p = __builtin_amdgcn_readfirstlane(prow[j]);
         if (p < 0) continue;
         const __amdgpu_buffer_rsrc_t row = buffer_rsrc(rows + int64_t(p) * a.stride, a.stride);
+        if (a.keep) {
 #pragma unroll
-        for (int u = 0; u < kScatU; ++u)
-            if (lane_off + u * kWave * 16 != skip_off)
-                store16_coherent(row, int(lane_off) + u * kWave * 16, v[u]);
+            for (int u = 0; u < kScatU; ++u)
+                if (lane_off + u * kWave * 16 != skip_off)
+                    store16_coherent_keep(row, int(lane_off) + u * kWave * 16, v[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < kScatU; ++u)
+                if (lane_off + u * kWave * 16 != skip_off)
+                    store16_coherent(row, int(lane_off) + u * kWave * 16, v[u]);
+        }
     }
 }
 
@@ -1123,6 +1131,8 @@ hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float*
     // spread over the GPU -- at T = 128 two-token items would keep 64
     // workgroups busy, and one workgroup moves only ~30-40 GB/s of scattered
     // rows.  Item-event readiness only: each part has its own event word.
+    // rows the combine items read soon after stay in the caches when they fit
+    a.keep = keep_rows(T, H, k) ? 1 : 0;
     a.parts = 1;
     if (sync == kSyncItemEvents && a.nScat < g) {
         const int nchunk = (a.nvec + kWave - 1) / kWave;
