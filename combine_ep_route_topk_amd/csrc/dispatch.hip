@@ -26,13 +26,13 @@ namespace {
 constexpr int kWavesPerBlock = kBlock / kWave;
 
 // One (token, segment) item whose vectors all lie inside the row: U loads
-// per lane, then U stores per pick, no per-vector checks.  KEEP: the stores
+// per lane, then U stores per pick, no per-vector checks.  keep: the stores
 // drop the streaming hint (rows the next kernel reads while still cached).
-template <int U, bool KEEP>
+template <int U>
 __device__ __forceinline__ void copy_whole(const char* __restrict__ src,
                                            char* __restrict__ send, int64_t row_bytes,
                                            const int32_t* __restrict__ prow, int k,
-                                           uint32_t S, int v0)
+                                           uint32_t S, int v0, bool keep)
 {
     const uint32_t lane_off = uint32_t(v0) * 16u;
     u32x4 v[U];
@@ -42,10 +42,13 @@ __device__ __forceinline__ void copy_whole(const char* __restrict__ src,
         const int32_t p = prow[j];
         if (uint32_t(p) >= S) continue;
         const __amdgpu_buffer_rsrc_t row = buffer_rsrc(send + int64_t(p) * row_bytes, row_bytes);
+        if (keep) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if constexpr (KEEP) store16_coherent_keep(row, int(lane_off) + u * kWave * 16, v[u]);
-            else store16_coherent(row, int(lane_off) + u * kWave * 16, v[u]);
+            for (int u = 0; u < U; ++u)
+                store16_coherent_keep(row, int(lane_off) + u * kWave * 16, v[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) store16_coherent(row, int(lane_off) + u * kWave * 16, v[u]);
         }
     }
 }
@@ -83,11 +86,12 @@ __device__ __noinline__ void copy_tail(const char* __restrict__ src, char* __res
 // whole route/layout/dispatch/combine step 205.5-207.2 -> 199.4-202.1 us).
 // Rows at or past S (T*k, or a smaller receive buffer's row count) are never
 // written.
-template <int U, bool KEEP>
+// Tokens from t_keep on store their rows cached (keep_from).
+template <int U>
 __global__ __launch_bounds__(kBlock) void dispatch_kernel(
     const uint16_t* __restrict__ x, int T, int nvec, int k,
     const int32_t* __restrict__ pos, uint16_t* __restrict__ send,
-    uint32_t segs, uint32_t items, uint32_t S)
+    uint32_t segs, uint32_t items, uint32_t S, int t_keep)
 {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t row_bytes = int64_t(nvec) * 16;
@@ -101,15 +105,15 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(
         const int32_t* prow = pos + int64_t(t) * k;
         const int v0 = seg * kWave * U + lane_id();
         if ((seg + 1) * kWave * U <= nvec)
-            copy_whole<U, KEEP>(src, dst, row_bytes, prow, k, S, v0);
+            copy_whole<U>(src, dst, row_bytes, prow, k, S, v0, t >= t_keep);
         else
-            copy_tail(src, dst, row_bytes, prow, k, S, v0, U, nvec, KEEP);
+            copy_tail(src, dst, row_bytes, prow, k, S, v0, U, nvec, t >= t_keep);
     }
 }
 
-template <int U, bool KEEP>
-hipError_t launch_uk(const uint16_t* x, int T, int nvec, int k, const int32_t* pos,
-                     uint16_t* send, uint32_t cap, uint32_t bound, hipStream_t s)
+template <int U>
+hipError_t launch_u(const uint16_t* x, int T, int nvec, int k, const int32_t* pos,
+                    uint16_t* send, uint32_t cap, uint32_t bound, int t_keep, hipStream_t s)
 {
     const uint32_t segs = uint32_t((nvec + kWave * U - 1) / (kWave * U));
     const uint32_t items = uint32_t((T + kWavesPerBlock - 1) / kWavesPerBlock) * segs;
@@ -117,17 +121,9 @@ hipError_t launch_uk(const uint16_t* x, int T, int nvec, int k, const int32_t* p
     // smallest grid that keeps that many rounds: no nearly idle last round
     const uint32_t rounds = (items + cap - 1) / cap;
     const uint32_t grid = (items + rounds - 1) / rounds;
-    EP_LAUNCH((dispatch_kernel<U, KEEP>), dim3(grid), dim3(kBlock), 0, s, x, T, nvec, k, pos,
-              send, segs, items, bound);
+    EP_LAUNCH((dispatch_kernel<U>), dim3(grid), dim3(kBlock), 0, s, x, T, nvec, k, pos,
+              send, segs, items, bound, t_keep);
     return hipGetLastError();
-}
-
-template <int U>
-hipError_t launch_u(const uint16_t* x, int T, int nvec, int k, const int32_t* pos,
-                    uint16_t* send, uint32_t cap, uint32_t bound, bool keep, hipStream_t s)
-{
-    return keep ? launch_uk<U, true>(x, T, nvec, k, pos, send, cap, bound, s)
-                : launch_uk<U, false>(x, T, nvec, k, pos, send, cap, bound, s);
 }
 
 }  // namespace
@@ -161,6 +157,14 @@ bool keep_rows(int T, int H, int k)
     return int64_t(T) * k * H * 2 <= kKeepRowsBytes;
 }
 
+int keep_from(int T, int H, int k)
+{
+    const int64_t per_token = int64_t(k) * H * 2;
+    if (int64_t(T) * per_token > kKeepMaxBytes) return T;
+    const int64_t tail = kKeepTailBytes / per_token;
+    return tail >= T ? 0 : int(T - tail);
+}
+
 hipError_t launch_dispatch(const uint16_t* x, int T, int H, int k, const int32_t* pos,
                            uint16_t* send, hipStream_t s)
 {
@@ -174,7 +178,7 @@ hipError_t launch_dispatch_bounded(const uint16_t* x, int T, int H, int k, const
     // A small batch is bound by latency, not by the write path: one vector per
     // lane and an uncapped grid put the most requests in flight (measured on
     // MI355X at T=128, H=7168, k=8: 8.2 -> 5.0 us).
-    const bool keep = keep_rows(T, H, k);
+    const int keep = keep_from(T, H, k);
     if (small_scatter(T, H, k))
         return launch_u<1>(x, T, nvec, k, pos, send, kMaxGrid, bound, keep, s);
     const uint32_t cap = dispatch_grid_cap();

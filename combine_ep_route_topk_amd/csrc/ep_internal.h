@@ -201,11 +201,28 @@ inline uint32_t dispatch_grid_cap() { return device_cu_count() / 2; }
 #endif
 constexpr int64_t kSmallScatterBytes = EP_SMALL_SCATTER_BYTES;
 bool small_scatter(int T, int H, int k);
-// Scatters that write at most this much store their rows without the
-// streaming hint, so the kernel that reads them next finds them in the
-// caches (measured on MI355X, dispatch then combine: 256 MiB of rows at
-// T=4096, H=4096, k=8 98.3 -> 94.1 us; 448 MiB at H=7168 172.5 -> 210 us,
-// where the rows overflow the 256 MB Infinity Cache and evict x).
+// Cached rows.  Dispatch (and the fused scatter) stores the rows of its last
+// tokens -- up to kKeepTailBytes of them -- without the streaming hint, so
+// combine, which reads the rows in token order, finds that tail in the
+// caches, and streams the rest; batches of more than kKeepMaxBytes of rows
+// stream all.  Measured on MI355X, dispatch then combine, A/B on one box:
+// T=4096, H=7168, k=8 (448 MiB of rows) 175.9-176.2 -> 168.7-168.8 us with a
+// 128 MiB tail (96 MiB 169.1-169.7, 160 MiB 170.7-171.1; every row cached
+// 210 us, since they overflow the 256 MB Infinity Cache and evict x);
+// T=4096, H=4096 (256 MiB) 95.8-97.0 with every row cached -> 91.8-92.1 us
+// with the tail; T=16384, H=7168 (1.75 GiB) 667.3-667.7 -> 742.4-743.5 us
+// with the tail.
+constexpr int64_t kKeepTailBytes = int64_t(128) << 20;
+constexpr int64_t kKeepMaxBytes = int64_t(512) << 20;
+// The first token whose rows a scatter of T tokens x k rows x H bf16 keeps
+// cached (T: none).
+int keep_from(int T, int H, int k);
+// The backward's gradient scatter keeps all of its rows cached for
+// dispatch_grad, or none: up to kKeepRowsBytes (measured at T=4096, H=4096,
+// k=8, 256 MiB: combine_grad 100.4-102.1 -> 99.2-99.4 us, dispatch_grad
+// 51.3-51.6 -> 49.7-50.1 us).  A cached tail chosen per token at run time
+// made its scatter kernel slower at every size (T=4096, H=7168: combine_grad
+// 173.0-173.2 -> 183.2-183.5 us, with no row cached at T=16384 as well).
 constexpr int64_t kKeepRowsBytes = int64_t(256) << 20;
 bool keep_rows(int T, int H, int k);
 

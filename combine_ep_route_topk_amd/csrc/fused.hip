@@ -93,7 +93,7 @@ struct FusedArgs {
     int64_t S;
     int nTiles, nCnt, nScan, nScat, nComb;
     int parts;                            // row parts per scatter / combine item (item events)
-    int keep;                             // row stores without the streaming hint (small batches)
+    int t_keep;                           // tokens from here on store their rows cached
     int64_t stride;                       // bytes per send row (payload + trailer + pad)
     int64_t trailer_off;                  // = 2H
     int32_t* expert_counts;
@@ -418,7 +418,7 @@ __device__ bool chunk_ready(const FusedArgs& a, const int* prow, int k, int c, u
 // per lane, then kScatU streaming stores per valid pick.
 __device__ __forceinline__ void scatter_whole(const char* __restrict__ src, const FusedArgs& a,
                                               const int* prow, uint32_t lane_off,
-                                              uint32_t skip_off)
+                                              uint32_t skip_off, bool keep)
 {
     u32x4 v[kScatU];
 #pragma unroll
@@ -428,7 +428,7 @@ __device__ __forceinline__ void scatter_whole(const char* __restrict__ src, cons
         const int p = __builtin_amdgcn_readfirstlane(prow[j]);
         if (p < 0) continue;
         const __amdgpu_buffer_rsrc_t row = buffer_rsrc(rows + int64_t(p) * a.stride, a.stride);
-        if (a.keep) {
+        if (keep) {
 #pragma unroll
             for (int u = 0; u < kScatU; ++u)
                 if (lane_off + u * kWave * 16 != skip_off)
@@ -447,7 +447,7 @@ __device__ __forceinline__ void scatter_whole(const char* __restrict__ src, cons
 // the whole struct into scratch memory.
 __device__ __noinline__ void scatter_tail(const char* __restrict__ src, char* __restrict__ rows,
                                           int64_t stride, const int* prow, int k, int nvec,
-                                          int v0, bool skip_first)
+                                          int v0, bool skip_first, bool keep)
 {
     for (int u = 0; u < kScatU; ++u) {
         const int vi = v0 + u * kWave;
@@ -456,7 +456,10 @@ __device__ __noinline__ void scatter_tail(const char* __restrict__ src, char* __
         const u32x4 v = load16(src + int64_t(vi) * 16);
         for (int j = 0; j < k; ++j) {
             const int p = prow[j];         // lanes may have left: no wave op here
-            if (p >= 0) store16_coherent(buffer_rsrc(rows + int64_t(p) * stride, stride), vi * 16, v);
+            if (p < 0) continue;
+            const __amdgpu_buffer_rsrc_t r = buffer_rsrc(rows + int64_t(p) * stride, stride);
+            if (keep) store16_coherent_keep(r, vi * 16, v);
+            else store16_coherent(r, vi * 16, v);
         }
     }
 }
@@ -491,13 +494,13 @@ __device__ void do_scatter(const FusedArgs& a, int item, int part, uint64_t epoc
             if (vi < a.nvec) {
                 const u32x4 v =
                     load16(reinterpret_cast<const char*>(a.x) + (int64_t(t) * a.nvec + vi) * 16);
-                // a small batch: the rows stay in the caches for the combine
-                // items that read them soon after
                 for (int j = 0; j < a.k; ++j) {
                     const int p = prow[j];         // lanes may have left: no wave op here
-                    if (p >= 0)
-                        store16_coherent_keep(buffer_rsrc(rows + int64_t(p) * a.stride, a.stride),
-                                              vi * 16, v);
+                    if (p < 0) continue;
+                    const __amdgpu_buffer_rsrc_t r =
+                        buffer_rsrc(rows + int64_t(p) * a.stride, a.stride);
+                    if (t >= a.t_keep) store16_coherent_keep(r, vi * 16, v);
+                    else store16_coherent(r, vi * 16, v);
                 }
             }
         }
@@ -513,10 +516,10 @@ __device__ void do_scatter(const FusedArgs& a, int item, int part, uint64_t epoc
             // sentinel mode: the leading 16 bytes are written last, below
             const bool sp = a.sync == kSyncSentinel;
             if ((seg + 1) * kSegVec <= a.nvec)
-                scatter_whole(src, a, prow, uint32_t(v0) * 16u, sp ? 0u : ~0u);
+                scatter_whole(src, a, prow, uint32_t(v0) * 16u, sp ? 0u : ~0u, t >= a.t_keep);
             else
                 scatter_tail(src, reinterpret_cast<char*>(a.send_rows), a.stride, prow, a.k,
-                             a.nvec, v0, sp);
+                             a.nvec, v0, sp, t >= a.t_keep);
             if (a.sync == kSyncChunkFlag) {
                 // sub-row flags: this wave's chunks of the k rows, as soon as
                 // its own stores of them have completed
@@ -1131,8 +1134,8 @@ hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float*
     // spread over the GPU -- at T = 128 two-token items would keep 64
     // workgroups busy, and one workgroup moves only ~30-40 GB/s of scattered
     // rows.  Item-event readiness only: each part has its own event word.
-    // rows the combine items read soon after stay in the caches when they fit
-    a.keep = keep_rows(T, H, k) ? 1 : 0;
+    // the rows of the last tokens stay in the caches for the combine items
+    a.t_keep = keep_from(T, H, k);
     a.parts = 1;
     if (sync == kSyncItemEvents && a.nScat < g) {
         const int nchunk = (a.nvec + kWave - 1) / kWave;
