@@ -178,14 +178,14 @@ hipError_t launch_dispatch_bounded(const uint16_t* x, int T, int H, int k, const
     // A small batch is bound by latency, not by the write path: one vector per
     // lane and an uncapped grid put the most requests in flight (measured on
     // MI355X at T=128, H=7168, k=8: 8.2 -> 5.0 us).
-    const int keep = keep_from(T, H, k);
+    const int tk = keep_from(T, H, k);       // first token whose rows stay cached
     if (small_scatter(T, H, k))
-        return launch_u<1>(x, T, nvec, k, pos, send, kMaxGrid, bound, keep, s);
+        return launch_u<1>(x, T, nvec, k, pos, send, kMaxGrid, bound, tk, s);
     const uint32_t cap = dispatch_grid_cap();
-    if (nvec % (kWave * 7) == 0) return launch_u<7>(x, T, nvec, k, pos, send, cap, bound, keep, s);
-    if (nvec >= kWave * 8) return launch_u<8>(x, T, nvec, k, pos, send, cap, bound, keep, s);
-    if (nvec >= kWave * 4) return launch_u<4>(x, T, nvec, k, pos, send, cap, bound, keep, s);
-    return launch_u<1>(x, T, nvec, k, pos, send, cap, bound, keep, s);
+    if (nvec % (kWave * 7) == 0) return launch_u<7>(x, T, nvec, k, pos, send, cap, bound, tk, s);
+    if (nvec >= kWave * 8) return launch_u<8>(x, T, nvec, k, pos, send, cap, bound, tk, s);
+    if (nvec >= kWave * 4) return launch_u<4>(x, T, nvec, k, pos, send, cap, bound, tk, s);
+    return launch_u<1>(x, T, nvec, k, pos, send, cap, bound, tk, s);
 }
 
 }  // namespace ep
