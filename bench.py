@@ -231,7 +231,10 @@ def main():
                    "experts": E, "virtual_ranks": R, "top_k": k,
                    "step": "route -> layout -> dispatch -> combine"},
         "value_is": "(dispatch + combine algorithmic bytes) / (dispatch time + combine time), "
-                    "per-op times from the ops' own kernels inside back-to-back steps",
+                    "per-op times from the ops' own kernels inside back-to-back steps: x stays "
+                    "in the Infinity Cache between steps, and dispatch leaves the rows of its "
+                    "last tokens (up to 128 MiB) there for combine; isolated_dispatch_combine "
+                    "reads every input from HBM",
         "tokens_per_s": round(T / (dc_us * 1e-6), 1),
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "dispatch_combine_us": round(dc_us, 2),
