@@ -76,7 +76,6 @@ constexpr int kScatTok = 2;                    // tokens per scatter item (2 wav
 constexpr int kCombTok = kWavesPerBlock;       // tokens per combine item (1 wave each)
 static_assert(kWavesPerBlock % kCombTok == 0, "whole waves per combine token");
 constexpr int kScatU = 7;                      // 16-byte vectors per lane per row segment
-constexpr int kSegVec = kWave * kScatU;        // vectors per scatter row segment
 constexpr int kMaxItemPicks = kCombTok * kMaxK;
 constexpr int kPickRounds = kMaxItemPicks / kWave;   // lanes cover the picks in <= 4 rounds
 static_assert(kScatTok * 2 == kWavesPerBlock, "two waves per scatter token");
@@ -414,15 +413,16 @@ __device__ bool chunk_ready(const FusedArgs& a, const int* prow, int k, int c, u
 }
 
 // ---------------------------------------------------------------- scatter item
-// One row segment of kSegVec vectors that lies inside the row: kScatU loads
-// per lane, then kScatU streaming stores per valid pick.
+// U whole 64-vector chunks of a row, from the lane's byte offset lane_off:
+// U loads per lane, then U streaming stores per valid pick.
+template <int U>
 __device__ __forceinline__ void scatter_whole(const char* __restrict__ src, const FusedArgs& a,
                                               const int* prow, uint32_t lane_off,
                                               uint32_t skip_off, bool keep)
 {
-    u32x4 v[kScatU];
+    u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < kScatU; ++u) v[u] = load16(src + lane_off + u * kWave * 16);
+    for (int u = 0; u < U; ++u) v[u] = load16(src + lane_off + u * kWave * 16);
     char* rows = reinterpret_cast<char*>(a.send_rows);
     for (int j = 0; j < a.k; ++j) {
         const int p = __builtin_amdgcn_readfirstlane(prow[j]);
@@ -430,12 +430,12 @@ __device__ __forceinline__ void scatter_whole(const char* __restrict__ src, cons
         const __amdgpu_buffer_rsrc_t row = buffer_rsrc(rows + int64_t(p) * a.stride, a.stride);
         if (keep) {
 #pragma unroll
-            for (int u = 0; u < kScatU; ++u)
+            for (int u = 0; u < U; ++u)
                 if (lane_off + u * kWave * 16 != skip_off)
                     store16_coherent_keep(row, int(lane_off) + u * kWave * 16, v[u]);
         } else {
 #pragma unroll
-            for (int u = 0; u < kScatU; ++u)
+            for (int u = 0; u < U; ++u)
                 if (lane_off + u * kWave * 16 != skip_off)
                     store16_coherent(row, int(lane_off) + u * kWave * 16, v[u]);
         }
@@ -505,33 +505,42 @@ __device__ void do_scatter(const FusedArgs& a, int item, int part, uint64_t epoc
             }
         }
     }
-    // payload: waves 2i and 2i+1 copy token t0 + i, alternating row segments
+    // payload: waves 2i and 2i+1 copy token t0 + i, each one half of the
+    // row's 64-vector chunks, in runs of kScatU chunks, then of 4, then 1
+    // (runs of kScatU alternating between the two waves left one wave with
+    // 7/8 of an 8 KiB row)
     const int i = wave >> 1;
     const int t = t0 + i;
     if (a.parts == 1 && t < a.T) {
         const char* src = reinterpret_cast<const char*>(a.x) + int64_t(t) * a.nvec * 16;
         const int* prow = sh_pos + i * a.k;
-        for (int seg = wave & 1; seg * kSegVec < a.nvec; seg += 2) {
-            const int v0 = seg * kSegVec + lane;
-            // sentinel mode: the leading 16 bytes are written last, below
-            const bool sp = a.sync == kSyncSentinel;
-            if ((seg + 1) * kSegVec <= a.nvec)
-                scatter_whole(src, a, prow, uint32_t(v0) * 16u, sp ? 0u : ~0u, t >= a.t_keep);
-            else
+        const int nchunk = (a.nvec + kWave - 1) / kWave;
+        const int nwhole = a.nvec / kWave;
+        const int ce = ((wave & 1) + 1) * nchunk / 2;
+        const int we = ce < nwhole ? ce : nwhole;         // this wave's whole chunks end here
+        // sentinel mode: the leading 16 bytes are written last, below
+        const uint32_t skip = a.sync == kSyncSentinel ? 0u : ~0u;
+        const bool keep = t >= a.t_keep;
+        for (int c0 = (wave & 1) * nchunk / 2; c0 < ce;) {
+            const int run = we - c0 >= kScatU ? kScatU : we - c0 >= 4 ? 4 : we - c0 >= 1 ? 1 : 0;
+            const uint32_t off = uint32_t(c0 * kWave + lane) * 16u;
+            if (run == kScatU) scatter_whole<kScatU>(src, a, prow, off, skip, keep);
+            else if (run == 4) scatter_whole<4>(src, a, prow, off, skip, keep);
+            else if (run == 1) scatter_whole<1>(src, a, prow, off, skip, keep);
+            else                                          // the row's partial last chunk
                 scatter_tail(src, reinterpret_cast<char*>(a.send_rows), a.stride, prow, a.k,
-                             a.nvec, v0, sp, t >= a.t_keep);
+                             a.nvec, c0 * kWave + lane, skip == 0u, keep);
+            const int nc = run > 0 ? run : 1;
             if (a.sync == kSyncChunkFlag) {
                 // sub-row flags: this wave's chunks of the k rows, as soon as
                 // its own stores of them have completed
                 wait_own_stores();
-                const int nchunk = (a.nvec + kWave - 1) / kWave;
-                const int c0 = seg * kScatU;
-                const int nc = nchunk - c0 < kScatU ? nchunk - c0 : kScatU;
                 for (int q = lane; q < a.k * nc; q += kWave) {
                     const int p = prow[q / nc];
                     if (p >= 0) st_relaxed64(chunk_flag(a, p, c0 + q % nc), epoch);
                 }
             }
+            c0 += nc;
         }
     }
     // Release without an L2 write-back: every payload store is agent-coherent
