@@ -163,14 +163,16 @@ def test_emulated_kernels_match_oracle(emu, T, H, E, R, k, seed):
     assert np.array_equal(m.out, x), "fused combine"
 
 
-@pytest.mark.parametrize("T,H", [(200, 520), (64, 3584), (40, 7176), (40, 8192),
+@pytest.mark.parametrize("T,H", [(200, 520), (64, 3584), (40, 7176), (40, 8192), (24, 4096),
                                  (6, 3584), (3, 7176), (13, 8192)])
 def test_emulated_fused_random_experts_equals_combine(emu, T, H):
     """Non-uniform weights: the fused reduction is bit-identical to ep_combine
     over the same rows (they share the arithmetic) and to the oracle's fp32
     chain.  Rows of 1, 7, 14 (plus a partial segment) and 16 whole 64-vector
     segments: one full batch of 14 segments, a short batch, and both.  The
-    last three batches have fewer scatter items than the emulation's 8
+    scatter side splits a row's chunks between a token's two waves in runs of
+    7, 4 and 1 (H=4096: one run of 4 each; 3584: 1+1+1 and 4).  The last
+    three batches have fewer scatter items than the emulation's 8
     workgroups, so their rows are split into 3, 4 and 2 parts."""
     E, R, k = 16, 4, 8
     rng = np.random.default_rng(11)
