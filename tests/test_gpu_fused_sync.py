@@ -120,12 +120,16 @@ def test_sync_modes_back_to_back_without_host_sync(epm, sync):
     assert np.array_equal(bits(fz["out"]), c.x)
 
 
-@pytest.mark.parametrize("name,calls", [("dsv3", 200), ("incast", 60)])
+@pytest.mark.parametrize("name,calls", [("dsv3", 200), ("incast", 60), ("decode", 400),
+                                        ("glm45air", 200)])
 def test_every_mode_long_back_to_back(epm, name, calls):
     """Long runs without host synchronisation, every readiness mode in turn on
     one workspace (epochs keep growing across modes): every 20th call the
     device error word is clear and the output is the round trip, then the
-    output is zeroed so the next check sees only later calls' work."""
+    output is zeroed so the next check sees only later calls' work.  The
+    decode-like batch splits its rows into parts in item-event mode (and not
+    in the others), the GLM-like one splits each 8 KiB row into two 4-chunk
+    runs; both keep their rows cached."""
     w = wl.WORKLOADS[name]
     inp = wl.make_inputs(w)
     x = to_dev_bits(inp["x"])
