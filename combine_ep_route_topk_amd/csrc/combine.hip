@@ -317,14 +317,25 @@ bool batchable(int T, int H, uint32_t grid)
     return items + span < (uint64_t(1) << 32);
 }
 
-// Gathers reading more than kSmallScatterBytes run batched on one workgroup
-// per CU where the rows allow it; smaller ones are latency-bound and take the
-// one-item-per-wave kernel on an uncapped grid.
+// Gathers reading more than kSmallScatterBytes run batched where the rows
+// allow it, on two workgroups per CU when every wave then takes a single
+// batch, else on one; smaller ones are latency-bound and take the
+// one-item-per-wave kernel on an uncapped grid.  Measured on MI355X, A/B on
+// one box: T=4096, H=7168, k=8 (57,344 items: one round of 28-item batches
+// on 512 workgroups, two on 256) combine 82.1-82.4 -> 79.0-79.2 us and
+// 85.2 -> 82.9-83.2 us on two boxes; T=16384 (four rounds against eight)
+// 328.6-329.2 -> 362.4-364.2 us, so a batch that needs more than one round
+// stays on one workgroup per CU.  The unit-weight gather (dispatch_grad)
+// moved 86.9-87.0 -> 87.6-89.2 us at T=4096, H=7168 and 49.4-49.6 ->
+// 46.9-47.2 us at H=4096.
 template <bool UW>
 hipError_t launch_gather(const uint16_t* y, const int32_t* pos, const float* w, int T, int H,
                          int k, uint16_t* out, hipStream_t s)
 {
-    const uint32_t grid = device_cu_count();
+    const uint32_t cus = device_cu_count();
+    const uint64_t items = uint64_t(T) * uint64_t(H / 8 / kWave);
+    const bool one_round = items <= uint64_t(kBatch) * 2 * cus * kWavesPerBlock;
+    const uint32_t grid = one_round ? 2 * cus : cus;
     if (!small_scatter(T, H, k) && batchable(T, H, grid))
         return launch_batched<UW>(y, pos, w, T, H / 8, k, out, grid, s);
     // One vector per lane and pick: more, smaller items keep more waves
