@@ -313,7 +313,7 @@ def bench_pipelined(ep, torch, w, logits, x, dev, K, W):
     """Steps whose preprocessing is pipelined (UBEP sec. 5.2: the
     preprocessing steps are pipelined with the transfers): route and layout of
     batch i+1 run on a second stream while batch i's dispatch runs -- dispatch
-    fills only half the CUs -- and its combine.  Every step still runs all four
+    fills only five eighths of the CUs -- and its combine.  Every step still runs all four
     ops on its own batch; routing and layout outputs are double-buffered, and
     stream events order each buffer's reuse.  Returns the wall time per step
     and the parity of every step's output."""

@@ -362,7 +362,7 @@ hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* y,
     const bool keep = keep_rows(T, H, k);
     if (small_scatter(T, H, k))
         return launch_scatter<1>(grad_out, pos, w, T, nvec, k, grad_y, kMaxGrid, keep, s);
-    const uint32_t cap = dispatch_grid_cap() * 13 / 8;
+    const uint32_t cap = scatter_grid_cap();
     if (nvec % (kWave * 7) == 0)
         return launch_scatter<7>(grad_out, pos, w, T, nvec, k, grad_y, cap, keep, s);
     if (nvec >= kWave * 8)

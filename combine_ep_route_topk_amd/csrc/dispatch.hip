@@ -78,12 +78,14 @@ __device__ __noinline__ void copy_tail(const char* __restrict__ src, char* __res
 // one wave per token, numbered segment-fastest: the workgroups resident at
 // one time cover whole rows, so each destination row is written as one
 // contiguous run (measured on MI355X at T=4096, H=7168, k=8: 1-2 us less
-// than token-fastest order).  A 1-D grid of at most half as many workgroups
-// as the GPU has CUs strides over the items in even rounds: fewer concurrent
-// streams of scattered row writes keep better DRAM locality, and 128
-// workgroups (512 waves) already saturate the write path (measured at the
-// same shape: dispatch alone 92.4 -> 87.7-89.0 us with 96-128 workgroups; the
-// whole route/layout/dispatch/combine step 205.5-207.2 -> 199.4-202.1 us).
+// than token-fastest order).  A 1-D grid of at most dispatch_grid_cap()
+// workgroups (160 on MI355X) strides over the items in even rounds: fewer
+// concurrent streams of scattered row writes keep better DRAM locality, and
+// 96-128 workgroups already saturate the write path (measured at the same
+// shape, streaming stores: dispatch alone 92.4 -> 87.7-89.0 us with 96-128
+// workgroups against every item's; the whole route/layout/dispatch/combine
+// step 205.5-207.2 -> 199.4-202.1 us); a few more hide x's read latency when
+// x comes from HBM.
 // Rows at or past S (T*k, or a smaller receive buffer's row count) are never
 // written.
 // Tokens from t_keep on store their rows cached (keep_from).
