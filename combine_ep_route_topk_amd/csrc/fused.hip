@@ -25,9 +25,9 @@
 //             call's epoch next to flag and value, then publishes every
 //             base as a 64-bit word (epoch << 32 | base): the base value is
 //             its own readiness flag.
-//   [scatter] kScatTok tokens: wave 0 polls the base words of the item's
-//             picks and puts the positions in LDS; two waves per token copy
-//             one half row each into the token's k send rows with
+//   [scatter] ST tokens (2 or 4): wave 0 polls the base words of the item's
+//             picks and puts the positions in LDS; the waves of a token
+//             (4 / ST) copy one share of its row each into its k send rows with
 //             agent-coherent streaming stores; every wave waits for its
 //             stores to complete, and after a barrier wave 0 writes pos and
 //             {slot_src, 0} into the rows' trailers, then the 64-bit epoch.
@@ -44,14 +44,15 @@
 // A row's trailer is its flag: on gfx950 a 64-bit aligned store is
 // single-copy atomic but a 14 KiB row is not, hence payload -> release ->
 // trailer, and trailer -> acquire -> payload on the reading side.  An
-// agent-scope release FENCE writes back the whole L2 of the XCD (measured at
-// T=4096, H=7168, k=8: 2048 of them cost ~160 us of a 400 us call), so the
-// scatter side releases the way an agent-scope atomic store does instead: the
+// agent-scope release FENCE writes back the whole L2 of the XCD (a first
+// version that fenced once per scatter item took 404 us a call at T=4096,
+// H=7168, k=8), so the scatter side releases the way an agent-scope atomic
+// store does instead: the
 // payload is stored agent-coherent (sc1), each wave waits for its stores to
 // complete, then the flags are stored.  The combine side keeps one acquire
 // fence (an L2 invalidate, cheap) per item.
 //
-// Scatter items are small (2 tokens) and outnumber the resident workgroups
+// Scatter items are small (2 or 4 tokens) and outnumber the resident workgroups
 // at the shapes that matter, so the first ticket of almost every workgroup is
 // layout or scatter work: no workgroup sits on a combine item waiting for
 // rows that nobody is writing yet.
@@ -72,14 +73,22 @@
 namespace ep {
 namespace {
 
-constexpr int kScatTok = 2;                    // tokens per scatter item (2 waves each)
+// Tokens per scatter item (ST, a template parameter of the kernel): 2, two
+// waves per token, each half of the row; or 4, one wave per token and row.
+// launch_fused picks 4 for rows of at most 8 KiB and for a small batch split
+// into row parts, 2 otherwise.  Measured on MI355X, fused call, 4 tokens
+// everywhere against 2: T=4096, H=4096 112.1-113.5 -> 109.8-110.0 us (item
+// events); T=128, H=7168 26.5-26.7 -> 24.9 us (item events) but 27.0-27.2 ->
+// 30.0-30.4 us (row flags); T=4096, H=7168 183.2-184.1 -> 186.2-188.0 us and
+// T=16384, H=7168 720.8-722.8 -> 736.0-736.4 us.  With the rule, against 2
+// everywhere: T=4096, H=4096 110.8-111.7 -> 108.2-110.7 us (item events),
+// checksum 114.1 -> 108.8-109.3, sentinel 116.3-116.7 -> 111.0-111.4; T=128
+// 26.1-26.2 -> 24.4-24.5 us (item events); the other shapes unchanged.
 constexpr int kCombTok = kWavesPerBlock;       // tokens per combine item (1 wave each)
 static_assert(kWavesPerBlock % kCombTok == 0, "whole waves per combine token");
 constexpr int kScatU = 7;                      // 16-byte vectors per lane per row segment
 constexpr int kMaxItemPicks = kCombTok * kMaxK;
 constexpr int kPickRounds = kMaxItemPicks / kWave;   // lanes cover the picks in <= 4 rounds
-static_assert(kScatTok * 2 == kWavesPerBlock, "two waves per scatter token");
-static_assert(kCombTok % kScatTok == 0, "a combine item covers whole scatter items");
 constexpr uint64_t kStFlagAggregate = uint64_t(1) << 30;
 constexpr uint64_t kStFlagInclusive = uint64_t(2) << 30;
 constexpr uint64_t kStValueMask = (uint64_t(1) << 30) - 1;
@@ -464,15 +473,20 @@ __device__ __noinline__ void scatter_tail(const char* __restrict__ src, char* __
     }
 }
 
+template <int ST>
 __device__ void do_scatter(const FusedArgs& a, int item, int part, uint64_t epoch, int* sh_pos,
                            int* sh_word)
 {
+    constexpr int kSWpt = kWavesPerBlock / ST;      // waves per scatter token
+    static_assert(ST * kSWpt == kWavesPerBlock, "whole waves per scatter token");
+    static_assert(kCombTok % ST == 0 && kCombTok / ST <= 2,
+                  "a combine item covers one or two whole scatter items");
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int lane = lane_id();
-    const int t0 = item * kScatTok;
+    const int t0 = item * ST;
     if (wave == 0) {
         int p[kPickRounds];
-        const bool ok = item_positions(a, t0, kScatTok, uint32_t(epoch), sh_pos, p);
+        const bool ok = item_positions(a, t0, ST, uint32_t(epoch), sh_pos, p);
         if (lane == 0) sh_word[0] = ok;
     }
     __syncthreads();
@@ -485,7 +499,7 @@ __device__ void do_scatter(const FusedArgs& a, int item, int part, uint64_t epoc
         const int c0 = part * nchunk / a.parts;
         const int nc = (part + 1) * nchunk / a.parts - c0;
         char* rows = reinterpret_cast<char*>(a.send_rows);
-        for (int q = wave; q < kScatTok * nc; q += kWavesPerBlock) {
+        for (int q = wave; q < ST * nc; q += kWavesPerBlock) {
             const int i = q / nc;
             const int t = t0 + i;
             if (t >= a.T) break;
@@ -505,23 +519,24 @@ __device__ void do_scatter(const FusedArgs& a, int item, int part, uint64_t epoc
             }
         }
     }
-    // payload: waves 2i and 2i+1 copy token t0 + i, each one half of the
+    // payload: the kSWpt waves of token t0 + i copy one share each of the
     // row's 64-vector chunks, in runs of kScatU chunks, then of 4, then 1
-    // (runs of kScatU alternating between the two waves left one wave with
-    // 7/8 of an 8 KiB row)
-    const int i = wave >> 1;
+    // (runs of kScatU alternating between two waves left one wave with 7/8
+    // of an 8 KiB row)
+    const int i = wave / kSWpt;
+    const int wi = wave % kSWpt;
     const int t = t0 + i;
     if (a.parts == 1 && t < a.T) {
         const char* src = reinterpret_cast<const char*>(a.x) + int64_t(t) * a.nvec * 16;
         const int* prow = sh_pos + i * a.k;
         const int nchunk = (a.nvec + kWave - 1) / kWave;
         const int nwhole = a.nvec / kWave;
-        const int ce = ((wave & 1) + 1) * nchunk / 2;
+        const int ce = (wi + 1) * nchunk / kSWpt;
         const int we = ce < nwhole ? ce : nwhole;         // this wave's whole chunks end here
         // sentinel mode: the leading 16 bytes are written last, below
         const uint32_t skip = a.sync == kSyncSentinel ? 0u : ~0u;
         const bool keep = t >= a.t_keep;
-        for (int c0 = (wave & 1) * nchunk / 2; c0 < ce;) {
+        for (int c0 = wi * nchunk / kSWpt; c0 < ce;) {
             const int run = we - c0 >= kScatU ? kScatU : we - c0 >= 4 ? 4 : we - c0 >= 1 ? 1 : 0;
             const uint32_t off = uint32_t(c0 * kWave + lane) * 16u;
             if (run == kScatU) scatter_whole<kScatU>(src, a, prow, off, skip, keep);
@@ -554,7 +569,7 @@ __device__ void do_scatter(const FusedArgs& a, int item, int part, uint64_t epoc
     __syncthreads();
 
     if (wave != 0) return;
-    const int npick = kScatTok * a.k;
+    const int npick = ST * a.k;
     const int64_t s0 = int64_t(t0) * a.k;
     const uint64_t tag = uint64_t(uint32_t(epoch)) << 32;
     if (a.sync == kSyncSentinel) {
@@ -768,6 +783,7 @@ __device__ __forceinline__ void combine_token_batched(const FusedArgs& a, const 
 // Waits, in one wave, until the rows p[] of a combine item are complete by
 // the Data-as-Flag check of a.sync (row flag, checksum or sentinel).  The
 // positions came from the published bases, not from the scatter items.
+template <int ST>
 __device__ bool rows_ready(const FusedArgs& a, int t0, const int (&p)[kPickRounds],
                            uint64_t epoch)
 {
@@ -801,8 +817,8 @@ __device__ bool rows_ready(const FusedArgs& a, int t0, const int (&p)[kPickRound
     // kSyncChecksum: the scatter items' words, then the rows' markers summed
     // per item must match them
     const uint32_t ep32 = uint32_t(epoch);
-    const int sfirst = t0 / kScatTok;
-    const int nsc = a.nScat - sfirst < kCombTok / kScatTok ? a.nScat - sfirst : kCombTok / kScatTok;
+    const int sfirst = t0 / ST;
+    const int nsc = a.nScat - sfirst < kCombTok / ST ? a.nScat - sfirst : kCombTok / ST;
     uint64_t word = 0;
     while (true) {
         if (lane < nsc) word = ld_relaxed64(&a.sdone[sfirst + lane]);
@@ -811,10 +827,10 @@ __device__ bool rows_ready(const FusedArgs& a, int t0, const int (&p)[kPickRound
         if (!wt.tick(a.hdr, a.spin_limit)) return false;
     }
     fence_acquire();
-    static_assert(kCombTok / kScatTok == 2, "two scatter items per combine item");
+    static_assert(kCombTok / ST <= 2, "at most two scatter items per combine item");
     const uint32_t want0 = uint32_t(__shfl(word, 0, kWave));
     const uint32_t want1 = uint32_t(__shfl(word, 1, kWave));
-    const int per_item = kScatTok * a.k;
+    const int per_item = ST * a.k;
     while (true) {
         uint32_t sum0 = 0, sum1 = 0;
 #pragma unroll
@@ -833,7 +849,7 @@ __device__ bool rows_ready(const FusedArgs& a, int t0, const int (&p)[kPickRound
     }
 }
 
-template <int KC>
+template <int KC, int ST>
 __device__ void do_combine(const FusedArgs& a, int item, int part, uint64_t epoch, int* sh_pos,
                            int* sh_word)
 {
@@ -844,7 +860,7 @@ __device__ void do_combine(const FusedArgs& a, int item, int part, uint64_t epoc
         int p[kPickRounds];
         bool ok = item_positions(a, t0, kCombTok, uint32_t(epoch), sh_pos, p);
         // sub-row flags: each wave waits per chunk below
-        if (ok && a.sync != kSyncChunkFlag) ok = rows_ready(a, t0, p, epoch);
+        if (ok && a.sync != kSyncChunkFlag) ok = rows_ready<ST>(a, t0, p, epoch);
         if (ok) fence_acquire();           // the rows' payloads
         if (lane == 0) sh_word[0] = ok;
     } else if (wave == 0) {
@@ -854,8 +870,8 @@ __device__ void do_combine(const FusedArgs& a, int item, int part, uint64_t epoc
         //    the published bases and ranks -- fewer dependent load rounds,
         //    which cost several microseconds each while HBM is saturated)
         bool ok = true;
-        const int sfirst = t0 / kScatTok;
-        const int nsc = a.nScat - sfirst < kCombTok / kScatTok ? a.nScat - sfirst : kCombTok / kScatTok;
+        const int sfirst = t0 / ST;
+        const int nsc = a.nScat - sfirst < kCombTok / ST ? a.nScat - sfirst : kCombTok / ST;
         Waiter wt0;
         while (true) {
             const uint64_t tag = uint64_t(uint32_t(epoch)) << 32;
@@ -947,7 +963,7 @@ __device__ void do_combine(const FusedArgs& a, int item, int part, uint64_t epoc
 }
 
 // ---------------------------------------------------------------- the launch
-template <int KC>
+template <int KC, int ST>
 __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs a) {
     __shared__ int32_t hist[kWavesPerBlock][kMaxE];
     __shared__ int sh_tot[kMaxE];
@@ -982,10 +998,10 @@ __global__ __launch_bounds__(kBlock) void fused_kernel(FusedArgs a) {
         else if (ticket < first_scatter) do_scan(a, ticket - first_scan, uint32_t(epoch), sh_wave_total, sh_word);
         else if (ticket < first_combine) {
             const int u = ticket - first_scatter;
-            do_scatter(a, u / a.parts, u % a.parts, epoch, sh_pos, sh_word);
+            do_scatter<ST>(a, u / a.parts, u % a.parts, epoch, sh_pos, sh_word);
         } else {
             const int u = ticket - first_combine;
-            do_combine<KC>(a, u / a.parts, u % a.parts, epoch, sh_pos, sh_word);
+            do_combine<KC, ST>(a, u / a.parts, u % a.parts, epoch, sh_pos, sh_word);
         }
     }
 
@@ -1055,12 +1071,12 @@ __global__ __launch_bounds__(kBlock) void sentinel_reset_kernel(uint8_t* rows, i
 // 512 workgroups; the other sync modes alike).
 constexpr int kFusedPerCu = 2;
 
-int resident_grid(const void* kernel) {
-    static std::atomic<int> cached[64][2];
+// `which` numbers the instantiation (0-3) for the cache.
+int resident_grid(const void* kernel, int which) {
+    static std::atomic<int> cached[64][4];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
     const int slot = dev < 64 ? dev : 63;
-    const int which = kernel == reinterpret_cast<const void*>(&fused_kernel<8>) ? 0 : 1;
     const int have = cached[slot][which].load(std::memory_order_relaxed);
     if (have > 0) return have;
     int per_cu = 0, cus = 0;
@@ -1107,7 +1123,6 @@ hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float*
     a.nCnt = f.lay.nCnt;
     // one tile: its item scans the counts itself (no scan items)
     a.nScan = f.lay.nTiles == 1 ? 0 : (f.lay.nCnt + kFusedScanItems - 1) / kFusedScanItems;
-    a.nScat = (T + kScatTok - 1) / kScatTok;
     a.nComb = (T + kCombTok - 1) / kCombTok;
     a.stride = int64_t(fused_row_stride(H));
     a.trailer_off = int64_t(2) * H;
@@ -1135,9 +1150,23 @@ hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float*
         if (e != hipSuccess) return e;
     }
 
-    const void* kern = k == 8 ? reinterpret_cast<const void*>(&fused_kernel<8>)
-                              : reinterpret_cast<const void*>(&fused_kernel<0>);
-    int g = grid > 0 ? grid : resident_grid(kern);
+    // the instantiation for the pick count and the scatter item size
+    auto kernel_for = [k](int st) -> const void* {
+        if (k == 8)
+            return st == 4 ? reinterpret_cast<const void*>(&fused_kernel<8, 4>)
+                           : reinterpret_cast<const void*>(&fused_kernel<8, 2>);
+        return st == 4 ? reinterpret_cast<const void*>(&fused_kernel<0, 4>)
+                       : reinterpret_cast<const void*>(&fused_kernel<0, 2>);
+    };
+    auto which = [k](int st) { return (k == 8 ? 0 : 2) + (st == 4 ? 1 : 0); };
+    int g = grid > 0 ? grid : resident_grid(kernel_for(2), which(2));
+    // Scatter items of 4 tokens for rows of at most 8 KiB, and for a batch
+    // whose 2-token items would be fewer than the workgroups (it is split into
+    // row parts below, item-event mode only); 2 tokens otherwise.
+    const bool few = sync == kSyncItemEvents && (T + 1) / 2 < g;
+    const int st = (a.nvec <= 512 || few) ? 4 : 2;
+    if (grid <= 0 && st != 2) g = resident_grid(kernel_for(st), which(st));
+    a.nScat = (T + st - 1) / st;
     // Row parts: a batch with fewer scatter items than workgroups splits each
     // item's rows into parts (64-vector chunks), so its few tokens still
     // spread over the GPU -- at T = 128 two-token items would keep 64
@@ -1155,10 +1184,14 @@ hipError_t launch_fused(const uint16_t* x, const int32_t* topk_idx, const float*
     }
     const int items = a.nTiles + a.nScan + (a.nScat + a.nComb) * a.parts;
     if (g > items) g = items;
-    if (k == 8)
-        EP_LAUNCH((fused_kernel<8>), dim3(g), dim3(kBlock), 0, s, a);
+    if (k == 8 && st == 4)
+        EP_LAUNCH((fused_kernel<8, 4>), dim3(g), dim3(kBlock), 0, s, a);
+    else if (k == 8)
+        EP_LAUNCH((fused_kernel<8, 2>), dim3(g), dim3(kBlock), 0, s, a);
+    else if (st == 4)
+        EP_LAUNCH((fused_kernel<0, 4>), dim3(g), dim3(kBlock), 0, s, a);
     else
-        EP_LAUNCH((fused_kernel<0>), dim3(g), dim3(kBlock), 0, s, a);
+        EP_LAUNCH((fused_kernel<0, 2>), dim3(g), dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 

@@ -170,8 +170,9 @@ def test_emulated_fused_random_experts_equals_combine(emu, T, H):
     over the same rows (they share the arithmetic) and to the oracle's fp32
     chain.  Rows of 1, 7, 14 (plus a partial segment) and 16 whole 64-vector
     segments: one full batch of 14 segments, a short batch, and both.  The
-    scatter side splits a row's chunks between a token's two waves in runs of
-    7, 4 and 1 (H=4096: one run of 4 each; 3584: 1+1+1 and 4).  The last
+    scatter side copies a row in runs of 7, 4 and 1 chunks: one wave per row in
+    4-token items (rows of at most 8 KiB, and batches of few items; H=4096: 7+1,
+    3584: 7), else two waves per row, each half of its chunks (H=8192: 7+1).  The last
     three batches have fewer scatter items than the emulation's 8
     workgroups, so their rows are split into 3, 4 and 2 parts."""
     E, R, k = 16, 4, 8
